@@ -1,0 +1,157 @@
+"""CPU oracle for D = alpha*op(A)*op(B) + beta*C (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The GPU library never calls it and shares no code
+with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, FP64 accumulation; see its
+header).  This module builds that file with gcc, marshals numpy arrays into it,
+and computes the parity metric
+
+    err_ij = |D_ij - d_ij| / (sum_k |op(A)_ik||op(B)_kj| + |beta*C_ij|)
+
+with tolerance 1e-5 for fp32 inputs and 1e-2 for bf16 inputs.  A zero
+denominator demands exact equality; a non-finite D fails.  The bf16 bound
+follows the relative-error threshold of 1e-2 that "High-Performance FP16
+General Matrix Multiplication on NVIDIA Ada Lovelace via CUTLASS and WMMA"
+(Methodology) used to validate its custom kernel; "GEMM on NVIDIA GPUs: from a
+naive kernel to a tiled pipeline" (section 5, precision; section 6,
+measurement) asks for a reference and tolerance matched to the dtypes rather
+than bitwise equality.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+TOLERANCE = {"f32": 1e-5, "bf16": 1e-2}
+
+_lib = None
+
+
+def compile_oracle(src: str, out: str, openmp: bool = True) -> None:
+    """Compile an oracle C source into a shared library with gcc."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+           "-shared", "-fPIC", src, "-o", out, "-lm"]
+    if openmp:
+        cmd.insert(1, "-fopenmp")
+    subprocess.run(cmd, check=True)
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        compile_oracle(_SRC, tmp)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    lib = ctypes.CDLL(path)
+    f = lib.oracle_gemm_points
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"operands must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def gemm_points(transA: str, transB: str, M: int, N: int, K: int, alpha: float,
+                A: np.ndarray, lda: int, B: np.ndarray, ldb: int,
+                beta: float, C: Optional[np.ndarray], ldc: int,
+                rows: Sequence[int], cols: Sequence[int],
+                nthreads: int = 0, lib=None):
+    """Reference values and error denominators at the points (rows[p], cols[p]).
+
+    A and B are flat or 2-D numpy arrays in the row-major storage described in
+    oracle.c (float32, or uint16 bf16 bit patterns, both the same dtype); C is
+    float32 or None (only allowed when beta == 0).
+    """
+    lib = lib or _get()
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    code = _dtype_code(A)
+    if _dtype_code(B) != code:
+        raise TypeError("A and B must have the same dtype")
+    if C is not None:
+        C = np.ascontiguousarray(C, dtype=np.float32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols must have the same length")
+    n = rows.size
+    val = np.empty(n, dtype=np.float64)
+    den = np.empty(n, dtype=np.float64)
+    rc = lib.oracle_gemm_points(code, int(transA == "T"), int(transB == "T"),
+                                M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                                float(beta), _ptr(C), ldc, n, _ptr(rows), _ptr(cols),
+                                _ptr(val), _ptr(den), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return val, den
+
+
+def gemm_full(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+              nthreads: int = 0, lib=None):
+    """Reference values and denominators for the whole M x N output."""
+    ii, jj = np.meshgrid(np.arange(M, dtype=np.int64), np.arange(N, dtype=np.int64),
+                         indexing="ij")
+    val, den = gemm_points(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                           ii.ravel(), jj.ravel(), nthreads=nthreads, lib=lib)
+    return val.reshape(M, N), den.reshape(M, N)
+
+
+def relative_errors(D: np.ndarray, val: np.ndarray, den: np.ndarray) -> np.ndarray:
+    """Per-element |D - d| / den; 0 where den == 0 and D == d; inf on mismatch/non-finite."""
+    D = np.asarray(D, dtype=np.float64)
+    diff = np.abs(D - val)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(den > 0, diff / np.where(den > 0, den, 1.0),
+                       np.where(diff == 0, 0.0, np.inf))
+    err = np.where(np.isfinite(D), err, np.inf)
+    return err
+
+
+def max_relative_error(D, val, den) -> float:
+    e = relative_errors(D, val, den)
+    return float(e.max()) if e.size else 0.0
+
+
+def max_threads() -> int:
+    return int(_get().oracle_max_threads())
