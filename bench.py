@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 dense GEMM on its headline workloads.
+
+One step = one FP32 GEMM D = A*B at M=N=K=4096 followed by one BF16-input /
+FP32-accumulate GEMM at M=N=K=8192 (row-major, no transpose, alpha=1,
+beta=0), both through the library's C ABI with automatic kernel selection.
+Inputs are seeded synthetic matrices (uniform[-1,1] fp32; normal(0,1) rounded
+to bf16), generated on the host and resident in HBM before timing.  Two
+buffer sets per workload are used in turn so that consecutive launches do not
+find their inputs in cache.
+
+Prints one JSON line: whole-job TFLOP/s (2*M*N*K summed over the step /
+step time), per-workload rates and fractions of the MI355X dense peaks, a
+roofline entry for the kernel that dominates the step, and the CPU oracle's
+rate on a bounded sample of the same workloads (a reported baseline only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = ("GEMM TFLOPS (2MNK/s) FP32 4096³ & BF16→FP32 8192³; "
+          "% of MI355X dense peak")
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+HBM_GBS = 8000.0
+STEP_WORKLOADS = ("fp32_4096", "bf16_8192")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def compulsory_bytes(w: workloads.Workload) -> int:
+    """Read A and B once, read C once if beta != 0, write D once.
+
+    The one-pass traffic of "Understanding Roofline and Tiling through Matrix
+    Multiplication", section 8.5 (12 N^2 bytes for square fp32), generalized to
+    M x N x K, bf16 operands and the beta*C read ("GEMM on NVIDIA GPUs",
+    section 2, ideal traffic).
+    """
+    ea = 4 if w.dtype == "f32" else 2
+    c = 4 * w.M * w.N if w.beta != 0.0 else 0
+    return ea * (w.M * w.K + w.K * w.N) + c + 4 * w.M * w.N
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_11_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(variant_name: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_src_digest") != kernel_source_digest():
+        return None
+    ent = rec.get("kernels", {}).get(f"{workload}:{variant_name}")
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+class Part:
+    """One workload: buffer sets on the GPU and a launcher."""
+
+    def __init__(self, g, h, name: str, nsets: int):
+        self.g, self.h, self.name = g, h, name
+        self.w = workloads.WORKLOADS[name]
+        self.sets = []
+        for s in range(nsets):
+            w = self.w
+            if s == 0:
+                A, B, C = workloads.make_inputs(w)
+            else:  # other sets: same recipe, shifted seeds
+                ws = workloads.Workload(**{**w.__dict__, "index": w.index + 100 * s})
+                A, B, C = workloads.make_inputs(ws)
+            D = torch.empty(w.M, w.N, dtype=torch.float32, device="cuda")
+            self.sets.append((A.cuda(), B.cuda(), None if C is None else C.cuda(), D))
+        self.host_inputs = workloads.make_inputs(self.w)
+        self.i = 0
+        self.events = []
+
+    def launch(self, stream_handle, record=False):
+        A, B, C, D = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        w = self.w
+        if record:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        self.g.run_tensors(self.h, A, B, D, C=C, transA=w.transA, transB=w.transB,
+                           alpha=w.alpha, beta=w.beta, stream=stream_handle)
+        if record:
+            e1.record()
+            self.events.append((e0, e1))
+
+    def kernel_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.events]))
+
+
+def oracle_sample_rate(part: Part, cores: int, budget_s: float):
+    """Time the CPU oracle on a sample of outputs of the part's workload."""
+    import oracle
+    w = part.w
+    A, B, C = part.host_inputs
+    A_np, B_np = workloads.as_numpy_operand(A), workloads.as_numpy_operand(B)
+    C_np = None if C is None else C.numpy()
+    rng = np.random.default_rng(w.seeds["sample"])
+
+    def run(n):
+        ii = rng.integers(0, w.M, size=n)
+        jj = rng.integers(0, w.N, size=n)
+        t0 = time.perf_counter()
+        oracle.gemm_points(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A_np, A.shape[1], B_np,
+                           B.shape[1], w.beta, C_np, w.N, ii, jj, nthreads=cores)
+        return time.perf_counter() - t0
+
+    t = run(max(cores * 4, 64))          # calibrate
+    rate = max(cores * 4, 64) / max(t, 1e-6)
+    n = int(min(max(rate * budget_s, 256), 4_000_000))
+    t = run(n)
+    return {"outputs": n, "seconds": t, "tflops": 2.0 * w.K * n / t / 1e12}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=2, help="buffer sets per workload")
+    ap.add_argument("--cpu-budget", type=float, default=6.0,
+                    help="seconds of oracle work per workload for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    import dense_gemm_11_amd as g
+    torch.cuda.set_device(0)
+    h = g.gemm_create()
+    parts = [Part(g, h, n, args.sets) for n in STEP_WORKLOADS]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        for p in parts:
+            p.launch(sh)
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        for p in parts:
+            p.launch(sh, record=True)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    step_flops = sum(p.w.flops for p in parts)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    report_parts = {}
+    for p in parts:
+        kms = p.kernel_ms()
+        tf = p.w.flops / (kms * 1e-3) / 1e12
+        vid = g.gemm_last_variant(h) if False else None
+        report_parts[p.name] = {"kernel_ms": round(kms, 4), "tflops": round(tf, 2),
+                                "frac_of_peak": round(tf / PEAK_TFLOPS[p.w.dtype], 4),
+                                "peak_tflops": PEAK_TFLOPS[p.w.dtype]}
+    # which kernel each part used
+    for p in parts:
+        A, B, C, D = p.sets[0]
+        w = p.w
+        g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB, alpha=w.alpha,
+                      beta=w.beta)
+        report_parts[p.name]["variant"] = g.gemm_variant_name(g.gemm_last_variant(h))
+    torch.cuda.synchronize()
+
+    dom = max(parts, key=lambda p: report_parts[p.name]["kernel_ms"])
+    drep = report_parts[dom.name]
+    achieved = dom.w.flops / (drep["kernel_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_TFLOPS[dom.w.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[dom.w.dtype], 4),
+                "traffic": measured_traffic(drep["variant"], dom.name),
+                "kernel": drep["variant"], "workload": dom.name,
+                "compulsory_bytes": compulsory_bytes(dom.w)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cores = len(os.sched_getaffinity(0))
+        samples = {p.name: oracle_sample_rate(p, cores, args.cpu_budget) for p in parts}
+        secs = sum(s["seconds"] for s in samples.values())
+        fl = sum(2.0 * p.w.K * samples[p.name]["outputs"] for p in parts)
+        cpu = {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": "; ".join(f"{k}: {v['outputs']} random outputs, full K, "
+                                    f"{v['seconds']:.1f} s" for k, v in samples.items()),
+               "per_workload_tflops": {k: v["tflops"] for k, v in samples.items()}}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32 + bf16-in/fp32-acc", "data": "synthetic",
+        "config": {"workload": "fp32 GEMM 4096^3 + bf16->fp32 GEMM 8192^3 (NN, alpha=1, beta=0)",
+                   "parallelism": "single GPU", "buffer_sets": args.sets},
+        "parts": report_parts, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    g.gemm_destroy(h)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

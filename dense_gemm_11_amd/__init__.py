@@ -1,0 +1,201 @@
+"""Python binding of the gfx950 dense GEMM library (libdense_gemm.so).
+
+The functions mirror the C ABI in include/dense_gemm.h one to one and only
+marshal arguments; every step of the GEMM runs in the library's HIP kernels.
+``run_tensors`` is a convenience that reads shapes, leading dimensions, device
+pointers and the current stream from torch tensors (torch supplies device
+memory and streams only).
+
+Importing this package loads the library; if it has not been built the import
+fails loudly (there is no fallback implementation).
+
+One HIP runtime per process: PyTorch's ROCm wheels ship their own copy of
+libamdhip64 (same soname as the system one).  Device pointers and streams
+only mean something to the runtime that created them, so torch is imported
+before the library is loaded; the dynamic linker then binds the library to
+the runtime torch already loaded instead of loading a second one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdense_gemm.so")
+
+GEMM_OP_N = 0
+GEMM_OP_T = 1
+GEMM_DTYPE_F32 = 0
+GEMM_DTYPE_BF16_F32 = 1
+GEMM_OK = 0
+GEMM_ERR_INVALID_VALUE = 1
+GEMM_ERR_NOT_SUPPORTED = 2
+GEMM_ERR_HIP = 3
+GEMM_ERR_ALLOC = 4
+
+# Every function declared in include/dense_gemm.h.
+EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
+           "gemm_variant_count", "gemm_variant_name", "gemm_variant_dtype",
+           "gemm_variant_tile", "gemm_set_variant", "gemm_last_variant",
+           "gemm_select_variant")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str = "gemm_run"):
+        self.status = status
+        super().__init__(f"{what} failed: {gemm_status_string(status)}")
+
+
+def hip_runtimes_loaded():
+    """Distinct libamdhip64 files mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return []
+    return sorted({os.path.realpath(p) for p in paths})
+
+
+def _load():
+    try:  # bind to torch's HIP runtime when torch is present (see module docstring)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m dense_gemm_11_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = hip_runtimes_loaded()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process (" + ", ".join(runtimes)
+                          + "); import torch before anything that loads libamdhip64")
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.gemm_create.argtypes = [ctypes.POINTER(vp)]
+    lib.gemm_create.restype = i32
+    lib.gemm_destroy.argtypes = [vp]
+    lib.gemm_destroy.restype = i32
+    lib.gemm_run.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
+                             vp, i64, i32, vp]
+    lib.gemm_run.restype = i32
+    lib.gemm_status_string.argtypes = [i32]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_variant_count.argtypes = []
+    lib.gemm_variant_count.restype = i32
+    lib.gemm_variant_name.argtypes = [i32]
+    lib.gemm_variant_name.restype = ctypes.c_char_p
+    lib.gemm_variant_dtype.argtypes = [i32]
+    lib.gemm_variant_dtype.restype = i32
+    lib.gemm_variant_tile.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                      ctypes.POINTER(i32)]
+    lib.gemm_variant_tile.restype = i32
+    lib.gemm_set_variant.argtypes = [vp, i32]
+    lib.gemm_set_variant.restype = i32
+    lib.gemm_last_variant.argtypes = [vp]
+    lib.gemm_last_variant.restype = i32
+    lib.gemm_select_variant.argtypes = [i32, i32, i32, i64, i64, i64]
+    lib.gemm_select_variant.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def gemm_create() -> int:
+    h = ctypes.c_void_p()
+    s = lib.gemm_create(ctypes.byref(h))
+    if s != GEMM_OK:
+        raise GemmError(s, "gemm_create")
+    return h.value
+
+
+def gemm_destroy(h) -> int:
+    return lib.gemm_destroy(h)
+
+
+def gemm_run(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd,
+             dtype, stream) -> int:
+    """Raw call: pointers and the stream are integers (0/None for NULL)."""
+    return lib.gemm_run(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                        D, ldd, dtype, stream)
+
+
+def gemm_status_string(s: int) -> str:
+    return lib.gemm_status_string(s).decode()
+
+
+def gemm_variant_count() -> int:
+    return lib.gemm_variant_count()
+
+
+def gemm_variant_name(i: int):
+    n = lib.gemm_variant_name(i)
+    return None if n is None else n.decode()
+
+
+def gemm_variant_dtype(i: int) -> int:
+    return lib.gemm_variant_dtype(i)
+
+
+def gemm_variant_tile(i: int):
+    bm, bn, bk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    s = lib.gemm_variant_tile(i, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(bk))
+    if s != GEMM_OK:
+        raise GemmError(s, "gemm_variant_tile")
+    return bm.value, bn.value, bk.value
+
+
+def gemm_set_variant(h, i: int) -> int:
+    return lib.gemm_set_variant(h, i)
+
+
+def gemm_last_variant(h) -> int:
+    return lib.gemm_last_variant(h)
+
+
+def gemm_select_variant(dtype, transA, transB, M, N, K) -> int:
+    return lib.gemm_select_variant(dtype, transA, transB, M, N, K)
+
+
+def variants():
+    """[(id, name, dtype, (bm, bn, bk))] for every kernel variant."""
+    return [(i, gemm_variant_name(i), gemm_variant_dtype(i), gemm_variant_tile(i))
+            for i in range(gemm_variant_count())]
+
+
+def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
+                stream=None, check=True) -> int:
+    """gemm_run on torch tensors (row-major 2-D views with unit column stride).
+
+    A: op(A) is M x K (A stored M x K for "N", K x M for "T"); B likewise;
+    C, D: M x N float32.  A and B are float32 (fp32 GEMM) or bfloat16.
+    """
+    import torch
+
+    def ld(t):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("expected a 2-D tensor with unit column stride")
+        return t.stride(0)
+
+    if A.dtype == torch.float32 and B.dtype == torch.float32:
+        dtype = GEMM_DTYPE_F32
+    elif A.dtype == torch.bfloat16 and B.dtype == torch.bfloat16:
+        dtype = GEMM_DTYPE_BF16_F32
+    else:
+        raise TypeError("A and B must both be float32 or both bfloat16")
+    if D.dtype != torch.float32 or (C is not None and C.dtype != torch.float32):
+        raise TypeError("C and D must be float32")
+    M, K = (A.shape[0], A.shape[1]) if transA == "N" else (A.shape[1], A.shape[0])
+    Kb, N = (B.shape[0], B.shape[1]) if transB == "N" else (B.shape[1], B.shape[0])
+    if Kb != K or tuple(D.shape) != (M, N) or (C is not None and tuple(C.shape) != (M, N)):
+        raise ValueError("inconsistent GEMM shapes")
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device).cuda_stream
+    s = gemm_run(h, GEMM_OP_N if transA == "N" else GEMM_OP_T,
+                 GEMM_OP_N if transB == "N" else GEMM_OP_T, M, N, K, float(alpha),
+                 A.data_ptr(), ld(A), B.data_ptr(), ld(B), float(beta),
+                 None if C is None else C.data_ptr(), ld(C) if C is not None else N,
+                 D.data_ptr(), ld(D), dtype, stream)
+    if check and s != GEMM_OK:
+        raise GemmError(s)
+    return s

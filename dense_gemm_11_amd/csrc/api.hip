@@ -1,0 +1,234 @@
+// C ABI of the dense GEMM library: argument validation, degenerate cases,
+// per-shape kernel selection and the launch.  Declared in include/dense_gemm.h.
+#include <algorithm>
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "dense_gemm.h"
+#include "common.hpp"
+#include "variants.hpp"
+
+struct gemm_handle_s {
+    int forced_variant;  // -1: automatic selection
+    int last_variant;
+};
+
+namespace dg {
+
+// D = beta * C (or 0 when beta == 0): the whole result when K == 0 or alpha == 0.
+__global__ __launch_bounds__(256) void scale_c_kernel(GemmArgs p)
+{
+    const int64_t total = (int64_t)p.M * p.N;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * 256) {
+        const int64_t row = e / p.N, col = e % p.N;
+        p.D[row * p.ldd + col] = (p.beta != 0.0f) ? p.beta * p.C[row * p.ldc + col] : 0.0f;
+    }
+}
+
+
+namespace {
+
+const std::vector<Variant>& table()
+{
+    static const std::vector<Variant> t = [] {
+        std::vector<Variant> v;
+        for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table}) {
+            int n = 0;
+            const Variant* t = get(&n);
+            v.insert(v.end(), t, t + n);
+        }
+        return v;
+    }();
+    return t;
+}
+
+int find_variant(const char* name)
+{
+    const auto& t = table();
+    for (size_t i = 0; i < t.size(); ++i)
+        if (std::strcmp(t[i].name, name) == 0) return (int)i;
+    return -1;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Per-shape selection.  Large tiles give the most reuse per LDS byte
+// (the tile's input intensity grows with BM*BN/(BM+BN), "GEMM on NVIDIA
+// GPUs", section 3) but fewer workgroups; small problems take the smaller
+// tile so that enough of the 256 compute units get work (section 5 on
+// tails and small shapes).
+int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/)
+{
+    static const int bf16_big = find_variant("bf16_mfma16x16x32_256x256x64_w2x2");
+    static const int bf16_mid = find_variant("bf16_mfma16x16x32_128x128x64_w2x2");
+    static const int f32_big = find_variant("f32_mfma32x32x2_256x256x32_w2x2");
+    static const int f32_mid = find_variant("f32_mfma32x32x2_128x128x32_w2x2");
+    const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
+    if (dtype == GEMM_DTYPE_BF16_F32) return big_tiles >= 192 ? bf16_big : bf16_mid;
+    return big_tiles >= 192 ? f32_big : f32_mid;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+}  // namespace
+}  // namespace dg
+
+extern "C" {
+
+gemm_status_t gemm_create(gemm_handle_t* out)
+{
+    if (!out) return GEMM_ERR_INVALID_VALUE;
+    gemm_handle_t h = new (std::nothrow) gemm_handle_s{-1, -1};
+    if (!h) return GEMM_ERR_ALLOC;
+    *out = h;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_destroy(gemm_handle_t h)
+{
+    delete h;
+    return GEMM_OK;
+}
+
+const char* gemm_status_string(gemm_status_t s)
+{
+    switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE";
+    case GEMM_ERR_NOT_SUPPORTED: return "GEMM_ERR_NOT_SUPPORTED";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC";
+    }
+    return "unknown status";
+}
+
+int gemm_variant_count(void) { return (int)dg::table().size(); }
+
+const char* gemm_variant_name(int id)
+{
+    if (id < 0 || id >= gemm_variant_count()) return nullptr;
+    return dg::table()[id].name;
+}
+
+int gemm_variant_dtype(int id)
+{
+    if (id < 0 || id >= gemm_variant_count()) return -1;
+    return dg::table()[id].dtype;
+}
+
+gemm_status_t gemm_variant_tile(int id, int* bm, int* bn, int* bk)
+{
+    if (id < 0 || id >= gemm_variant_count()) return GEMM_ERR_INVALID_VALUE;
+    const dg::Variant& v = dg::table()[id];
+    if (bm) *bm = v.bm;
+    if (bn) *bn = v.bn;
+    if (bk) *bk = v.bk;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_set_variant(gemm_handle_t h, int id)
+{
+    if (!h || id < -1 || id >= gemm_variant_count()) return GEMM_ERR_INVALID_VALUE;
+    h->forced_variant = id;
+    return GEMM_OK;
+}
+
+int gemm_last_variant(gemm_handle_t h) { return h ? h->last_variant : -1; }
+
+int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, int64_t M,
+                        int64_t N, int64_t K)
+{
+    if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32) ||
+        (transA != GEMM_OP_N && transA != GEMM_OP_T) || (transB != GEMM_OP_N && transB != GEMM_OP_T))
+        return -1;
+    return dg::select_variant(dtype, M, N, K);
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M, int64_t N,
+                       int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, const float* C, int64_t ldc, float* D, int64_t ldd,
+                       gemm_dtype_t dtype, hipStream_t stream)
+{
+    using namespace dg;
+    if (!h) return GEMM_ERR_INVALID_VALUE;
+    if ((transA != GEMM_OP_N && transA != GEMM_OP_T) || (transB != GEMM_OP_N && transB != GEMM_OP_T))
+        return GEMM_ERR_INVALID_VALUE;
+    if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32) return GEMM_ERR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+    const int64_t one = 1;
+    const int64_t min_lda = transA == GEMM_OP_N ? std::max(one, K) : std::max(one, M);
+    const int64_t min_ldb = transB == GEMM_OP_N ? std::max(one, N) : std::max(one, K);
+    const int64_t min_ldcd = std::max(one, N);
+    if (lda < min_lda || ldb < min_ldb || ldd < min_ldcd) return GEMM_ERR_INVALID_VALUE;
+    if (beta != 0.0f && ldc < min_ldcd) return GEMM_ERR_INVALID_VALUE;
+    h->last_variant = -1;
+    if (M == 0 || N == 0) return GEMM_OK;
+    const bool reads_ab = K > 0 && alpha != 0.0f;
+    if (!D) return GEMM_ERR_INVALID_VALUE;
+    if (beta != 0.0f && !C) return GEMM_ERR_INVALID_VALUE;
+    if (reads_ab && (!A || !B)) return GEMM_ERR_INVALID_VALUE;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX || lda > INT_MAX || ldb > INT_MAX ||
+        ldd > INT_MAX || (beta != 0.0f && ldc > INT_MAX))
+        return GEMM_ERR_NOT_SUPPORTED;
+    if (beta != 0.0f) {
+        const int64_t span_c = ((M - 1) * ldc + N) * 4, span_d = ((M - 1) * ldd + N) * 4;
+        if (static_cast<const void*>(C) == static_cast<const void*>(D)) {
+            if (ldc != ldd) return GEMM_ERR_INVALID_VALUE;
+        } else if (ranges_overlap(C, span_c, D, span_d)) {
+            return GEMM_ERR_INVALID_VALUE;
+        }
+    }
+
+    GemmArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = beta != 0.0f ? C : nullptr;
+    a.D = D;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = beta != 0.0f ? ldc : 0;
+    a.ldd = ldd;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.c_vec = beta != 0.0f && aligned16(C) && (ldc % 4) == 0;
+    a.d_vec = aligned16(D) && (ldd % 4) == 0;
+
+    if (!reads_ab) {
+        const int64_t blocks = std::min<int64_t>(ceil_div(M * N, 256), 65536);
+        void* args[] = {&a};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&scale_c_kernel),
+                                       dim3((unsigned)blocks), dim3(256), args, 0, stream);
+        return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    }
+
+    int id = h->forced_variant >= 0 ? h->forced_variant : select_variant(dtype, M, N, K);
+    const Variant& v = table()[id];
+    if (v.dtype != (int)dtype) return GEMM_ERR_NOT_SUPPORTED;
+    const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    const bool aligned = aligned16(A) && aligned16(B) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
+    a.tiles_m = (int)ceil_div(M, v.bm);
+    a.tiles_n = (int)ceil_div(N, v.bn);
+    a.group_m = std::min(a.tiles_m, 8);
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+    if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
+    LaunchFn fn = v.fn[aligned][transA == GEMM_OP_N][transB == GEMM_OP_T];
+    const hipError_t e = fn(a, (int)grid, stream);
+    if (e != hipSuccess) return GEMM_ERR_HIP;
+    h->last_variant = id;
+    return GEMM_OK;
+}
+
+}  // extern "C"

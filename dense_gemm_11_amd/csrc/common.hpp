@@ -1,0 +1,70 @@
+// Shared device/host definitions for the gfx950 dense GEMM kernels.
+//
+// The operation is D = alpha * op(A) * op(B) + beta * C ("GEMM on NVIDIA GPUs:
+// from a naive kernel to a tiled pipeline", section 1), row-major storage:
+//   op(A)(i,k) = transA == N ? A[i*lda + k] : A[k*lda + i]
+//   op(B)(k,j) = transB == N ? B[k*ldb + j] : B[j*ldb + k]
+// An operand is "k-contiguous" when consecutive k are adjacent in memory
+// (A with transA == N, B with transB == T) and "mn-contiguous" otherwise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef uint16_t bf16_t;  // bfloat16 operands are carried as raw 16-bit patterns
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Everything a kernel needs for one GEMM call (passed by value as kernarg).
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    const float* C;
+    float* D;
+    int64_t lda, ldb, ldc, ldd;  // leading dimensions, in elements
+    int M, N, K;
+    float alpha, beta;
+    int tiles_m, tiles_n;  // output tiles along M and N
+    int group_m;           // tile-rows walked together for L2 reuse
+    int c_vec;             // C rows allow 16-byte loads (pointer and ldc aligned)
+    int d_vec;             // D rows allow 16-byte stores
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumber them so that XCD x runs a contiguous range of logical tile
+// ids, then walk tiles in groups of `group_m` tile-rows so that concurrently
+// running workgroups on one XCD share A row-panels and B column-panels.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
+{
+    const int total = p.tiles_m * p.tiles_n;
+    int w = blockIdx.x;
+    constexpr int XCDS = 8;
+    const int full = (total / XCDS) * XCDS;
+    if (w < full) w = (w % XCDS) * (full / XCDS) + (w / XCDS);
+    const int per_group = p.group_m * p.tiles_n;
+    const int group = w / per_group;
+    const int first_m = group * p.group_m;
+    int gsize = p.tiles_m - first_m;
+    if (gsize > p.group_m) gsize = p.group_m;
+    const int in_group = w - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x);
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ float to_f32<bf16_t>(bf16_t x)
+{
+    return __uint_as_float(((uint32_t)x) << 16);
+}
+
+}  // namespace dg

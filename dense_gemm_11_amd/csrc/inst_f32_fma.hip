@@ -1,0 +1,21 @@
+// fp32 vector-FMA variants (register-blocked outer products, no matrix cores).
+#include "fma_gemm.hpp"
+#include "variants.hpp"
+
+namespace dg {
+
+using FmaBig = FmaConfig<128, 128, 16>;
+
+#define F32V_VARIANT(NAME, CFG) \
+    {NAME, 0, KIND_VECTOR_FMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(fma_gemm_kernel, CFG)}
+
+const Variant* f32fma_variant_table(int* count)
+{
+    static const Variant table[] = {
+    F32V_VARIANT("f32_vfma_128x128x16_t8x8", FmaBig),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace dg

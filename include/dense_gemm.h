@@ -1,0 +1,140 @@
+/*
+ * dense_gemm.h — C ABI of the gfx950 (MI355X) dense GEMM library.
+ *
+ * Operation (the general GEMM of "GEMM on NVIDIA GPUs: from a naive kernel to
+ * a tiled pipeline", section 1):
+ *
+ *     D = alpha * op(A) * op(B) + beta * C
+ *     D_ij = alpha * sum_{k=0}^{K-1} op(A)_ik op(B)_kj + beta * C_ij
+ *
+ * with op(X) = X or X^T, op(A) of size M x K, op(B) of size K x N, C and D of
+ * size M x N.  Throughput is counted as 2*M*N*K floating-point operations
+ * (alpha/beta work excluded, as in that section).
+ *
+ * Precisions (input / accumulate / output, the triple named in its section 5):
+ *   GEMM_DTYPE_F32      : A, B fp32 / fp32 / C, D fp32
+ *   GEMM_DTYPE_BF16_F32 : A, B bfloat16 (raw 16-bit patterns) / fp32 / C, D fp32
+ * The order in which the K products are summed is not specified; results are
+ * bitwise reproducible run to run for the same call and kernel variant.
+ *
+ * Storage: every matrix is row-major (element (r, c) at ptr[r*ld + c]).
+ *   transA == GEMM_OP_N : A stored M x K, lda >= max(1, K)
+ *   transA == GEMM_OP_T : A stored K x M, lda >= max(1, M)
+ *   transB == GEMM_OP_N : B stored K x N, ldb >= max(1, N)
+ *   transB == GEMM_OP_T : B stored N x K, ldb >= max(1, K)
+ *   C, D stored M x N, ldc >= max(1, N) (when C is read), ldd >= max(1, N)
+ * A column-major caller obtains the same result by computing
+ * D^T = op(B)^T op(A)^T, i.e. by swapping the operands.
+ *
+ * Ownership: A, B, C and D are device pointers owned by the caller; the
+ * library never allocates, frees or retains them.  A handle owns only the
+ * kernel-choice state below.  alpha and beta are host values.
+ *
+ * Execution: gemm_run validates its arguments on the host, then enqueues its
+ * kernel(s) on `stream` (0 = the default stream) and returns without waiting.
+ * The caller synchronizes before reading D.  Different handles may be used
+ * concurrently from different threads.
+ *
+ * Semantics of degenerate calls:
+ *   M == 0 or N == 0 : nothing is enqueued, GEMM_OK.
+ *   K == 0 or alpha == 0 : D = beta * C (D = 0 when beta == 0); A and B are
+ *                          not read and may be NULL.
+ *   beta == 0 : C is never read and may be NULL; NaN/Inf in C cannot reach D.
+ *   C == D (in place) is allowed when ldc == ldd; any other overlap of the C
+ *   and D address ranges is rejected.
+ *
+ * Errors: every entry point returns a status; nothing aborts or throws.
+ *   GEMM_ERR_INVALID_VALUE : checked before anything is enqueued — NULL
+ *       handle or output pointer, unknown enum, negative size, leading
+ *       dimension too small, NULL operand that must be read, overlapping C/D.
+ *   GEMM_ERR_NOT_SUPPORTED : a size beyond the library's limits (M, N, K and
+ *       every leading dimension below 2^31) or a forced kernel variant that
+ *       does not handle the call's dtype.
+ *   GEMM_ERR_HIP : the HIP runtime rejected the kernel launch.
+ *   GEMM_ERR_ALLOC : gemm_create could not allocate its handle.
+ * Pointer alignment is never an error: misaligned operands select kernels
+ * with narrower memory accesses.
+ */
+#ifndef DENSE_GEMM_H
+#define DENSE_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemm_handle_s* gemm_handle_t;
+
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
+
+typedef enum {
+    GEMM_DTYPE_F32 = 0,      /* A, B fp32; C, D fp32; fp32 accumulate */
+    GEMM_DTYPE_BF16_F32 = 1  /* A, B bf16; C, D fp32; fp32 accumulate */
+} gemm_dtype_t;
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1,
+    GEMM_ERR_NOT_SUPPORTED = 2,
+    GEMM_ERR_HIP = 3,
+    GEMM_ERR_ALLOC = 4
+} gemm_status_t;
+
+/* Create a handle (*out receives it).  Makes no HIP call. */
+gemm_status_t gemm_create(gemm_handle_t* out);
+
+/* Release a handle.  NULL is accepted and ignored.  Pending work on streams
+ * is not affected (the handle is not referenced by enqueued kernels). */
+gemm_status_t gemm_destroy(gemm_handle_t h);
+
+/* D = alpha*op(A)*op(B) + beta*C, enqueued on `stream`.  See the header
+ * comment for layouts, degenerate cases and errors.  A and B point to float
+ * (GEMM_DTYPE_F32) or to 16-bit bfloat16 patterns (GEMM_DTYPE_BF16_F32). */
+gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB,
+                       int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, const float* C, int64_t ldc,
+                       float* D, int64_t ldd, gemm_dtype_t dtype, hipStream_t stream);
+
+/* Static, human-readable text for a status code ("unknown status" otherwise). */
+const char* gemm_status_string(gemm_status_t s);
+
+/* ---- kernel variants (per-shape tile and occupancy selection) -------------
+ * The library holds a table of kernel variants (tile shape, wave grid,
+ * instruction kind).  By default gemm_run picks one per call from the dtype,
+ * transposes and M, N, K; a handle can instead force one (tests use this to
+ * exercise every variant, benchmarks to sweep them).                        */
+
+/* Number of variants in the table. */
+int gemm_variant_count(void);
+
+/* Static name of variant `id` (NULL when out of range), e.g.
+ * "bf16_mfma16x16x32_256x256x64_w2x2". */
+const char* gemm_variant_name(int id);
+
+/* dtype handled by variant `id` (-1 when out of range). */
+int gemm_variant_dtype(int id);
+
+/* Tile shape of variant `id` into bm/bn/bk (any may be NULL). */
+gemm_status_t gemm_variant_tile(int id, int* bm, int* bn, int* bk);
+
+/* Force variant `id` for later gemm_run calls on h; -1 restores automatic
+ * selection.  GEMM_ERR_INVALID_VALUE for an unknown id or NULL handle. */
+gemm_status_t gemm_set_variant(gemm_handle_t h, int id);
+
+/* Variant used by the last successful gemm_run on h (-1 if none or if that
+ * call launched no GEMM kernel). */
+int gemm_last_variant(gemm_handle_t h);
+
+/* The variant automatic selection would use for this problem (pure host
+ * logic, no HIP call); -1 for an invalid dtype/transpose. */
+int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB,
+                        int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_H */

@@ -1,0 +1,145 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/dense_gemm.h declares,
+and reject invalid arguments before anything is enqueued (argument checks run
+on the host before any HIP call, so they are exercised here without a GPU).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_11_amd as g
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dense_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gemm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(g.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert g.gemm_status_string(g.GEMM_OK) == "GEMM_OK"
+    assert g.gemm_status_string(g.GEMM_ERR_INVALID_VALUE) == "GEMM_ERR_INVALID_VALUE"
+    assert g.gemm_status_string(g.GEMM_ERR_NOT_SUPPORTED) == "GEMM_ERR_NOT_SUPPORTED"
+    assert g.gemm_status_string(g.GEMM_ERR_HIP) == "GEMM_ERR_HIP"
+    assert g.gemm_status_string(g.GEMM_ERR_ALLOC) == "GEMM_ERR_ALLOC"
+    assert g.gemm_status_string(77) == "unknown status"
+
+
+@pytest.fixture
+def h():
+    handle = g.gemm_create()
+    yield handle
+    assert g.gemm_destroy(handle) == g.GEMM_OK
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def run(h, **kw):
+    a = dict(transA=0, transB=0, M=4, N=5, K=6, alpha=1.0, A=FAKE, lda=6, B=FAKE, ldb=5,
+             beta=0.0, C=None, ldc=5, D=FAKE, ldd=5, dtype=0, stream=None)
+    a.update(kw)
+    return g.gemm_run(h, a["transA"], a["transB"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                      a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["D"], a["ldd"],
+                      a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(transA=2), dict(transB=-1), dict(dtype=2), dict(M=-1), dict(N=-3), dict(K=-1),
+    dict(lda=5), dict(transA=1, lda=3), dict(ldb=4), dict(transB=1, ldb=5), dict(ldd=4),
+    dict(beta=1.0, C=FAKE, ldc=4), dict(D=None), dict(beta=0.5, C=None), dict(A=None),
+    dict(B=None), dict(beta=1.0, C=FAKE, ldc=6, D=FAKE, ldd=5),          # C == D, ldc != ldd
+    dict(beta=1.0, C=FAKE, D=FAKE + 8),                                  # partial overlap
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_invalid_arguments_rejected(h, kw):
+    assert run(h, **kw) == g.GEMM_ERR_INVALID_VALUE
+
+
+def test_null_handle_rejected():
+    assert run(None) == g.GEMM_ERR_INVALID_VALUE
+
+
+def test_too_large_is_not_supported(h):
+    assert run(h, M=2 ** 31, N=4, K=4, lda=4, ldb=4, ldd=4) == g.GEMM_ERR_NOT_SUPPORTED
+
+
+def test_empty_output_is_a_noop(h):
+    # M == 0 or N == 0 returns before touching any pointer or the GPU
+    assert run(h, M=0, A=None, B=None, D=None) == g.GEMM_OK
+    assert run(h, N=0, A=None, B=None, D=None, ldb=1, ldd=1) == g.GEMM_OK
+    assert g.gemm_last_variant(h) == -1
+
+
+def test_forced_variant_of_other_dtype_not_supported(h):
+    bf16_ids = [i for i, _, dt, _ in g.variants() if dt == g.GEMM_DTYPE_BF16_F32]
+    assert g.gemm_set_variant(h, bf16_ids[0]) == g.GEMM_OK
+    assert run(h, dtype=g.GEMM_DTYPE_F32) == g.GEMM_ERR_NOT_SUPPORTED
+    assert g.gemm_set_variant(h, -1) == g.GEMM_OK
+
+
+def test_variant_table():
+    vs = g.variants()
+    assert len(vs) == g.gemm_variant_count() >= 4
+    names = [v[1] for v in vs]
+    assert len(set(names)) == len(names)
+    assert {v[2] for v in vs} == {g.GEMM_DTYPE_F32, g.GEMM_DTYPE_BF16_F32}
+    for i, name, dt, (bm, bn, bk) in vs:
+        assert name.startswith("bf16_" if dt else "f32_")
+        assert f"{bm}x{bn}x{bk}" in name
+    assert g.gemm_variant_name(len(vs)) is None and g.gemm_variant_dtype(-1) == -1
+    h = g.gemm_create()
+    assert g.gemm_set_variant(h, len(vs)) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_set_variant(h, -2) == g.GEMM_ERR_INVALID_VALUE
+    g.gemm_destroy(h)
+
+
+def test_selector_returns_matching_dtype_for_every_shape():
+    shapes = [(1, 1, 1), (256, 256, 256), (4096, 4096, 4096), (8192, 8192, 8192),
+              (4093, 2051, 1537), (8192, 12288, 4096), (8192, 4096, 14336), (130, 7, 9000)]
+    for dtype in (g.GEMM_DTYPE_F32, g.GEMM_DTYPE_BF16_F32):
+        for ta in (0, 1):
+            for tb in (0, 1):
+                for M, N, K in shapes:
+                    vid = g.gemm_select_variant(dtype, ta, tb, M, N, K)
+                    assert 0 <= vid < g.gemm_variant_count()
+                    assert g.gemm_variant_dtype(vid) == dtype
+    assert g.gemm_select_variant(5, 0, 0, 4, 4, 4) == -1
+    assert g.gemm_select_variant(0, 3, 0, 4, 4, 4) == -1
+
+
+def test_selector_takes_large_tiles_for_large_problems():
+    for dtype, M in ((g.GEMM_DTYPE_BF16_F32, 8192), (g.GEMM_DTYPE_F32, 4096)):
+        big = g.gemm_variant_tile(g.gemm_select_variant(dtype, 0, 0, M, M, M))
+        small = g.gemm_variant_tile(g.gemm_select_variant(dtype, 0, 0, 256, 256, 256))
+        assert big[0] * big[1] > small[0] * small[1]
+
+
+def test_binding_shares_one_hip_runtime_with_torch():
+    """Importing the package first must still leave exactly one HIP runtime
+    mapped (torch ships its own libamdhip64 with the system soname)."""
+    import subprocess
+    import sys
+    code = ("import dense_gemm_11_amd as g, torch\n"
+            "rt = g.hip_runtimes_loaded()\n"
+            "assert len(rt) == 1, rt\n"
+            "print(rt[0])\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr

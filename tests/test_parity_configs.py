@@ -1,0 +1,45 @@
+"""GPU vs oracle at the full sizes of the benchmarked and reported workloads,
+with the automatic kernel selection the benchmark uses.  The 256^3 case is
+checked on every output; the large ones on 64 rows x 64 columns (4096
+outputs) that always include the first and last row and column.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+from .gpu_support import announce, gpu_gemm, oracle_check, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle():
+    require_gpu()
+    import dense_gemm_11_amd as g
+    h = g.gemm_create()
+    yield h
+    g.gemm_destroy(h)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_workload_parity(handle, name):
+    w = workloads.WORKLOADS[name]
+    announce("workload", name, w.M, w.N, w.K)
+    A, B, C = workloads.make_inputs(w)
+    D, _, _ = gpu_gemm(handle, w.dtype, w.transA, w.transB, w.M, w.N, w.K, w.alpha, w.beta,
+                       A, B, C)
+    assert torch.isfinite(D).all()
+    if w.M * w.N <= 256 * 256:
+        err, tol = oracle_check(w.dtype, w.transA, w.transB, w.M, w.N, w.K, w.alpha, w.beta,
+                                A, B, C, D)
+    else:
+        rows, cols = workloads.sample_indices(w.M, w.N, w.seeds["sample"])
+        assert rows[0] == 0 and rows[-1] == w.M - 1 and cols[-1] == w.N - 1
+        err, tol = oracle_check(w.dtype, w.transA, w.transB, w.M, w.N, w.K, w.alpha, w.beta,
+                                A, B, C, D, rows=rows, cols=cols)
+    print(f"[result] {name} max_rel_err={err:.3e} tol={tol:g}", flush=True)
+    assert err <= tol
