@@ -62,7 +62,19 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(variant_name: str, workload: str):
+MFMA_KIND = {"mfma32x32x2": 0, "mfma16x16x4": 1, "mfma32x32x16": 2, "mfma16x16x32": 3}
+
+
+def kernel_name_key(variant_name: str, tile) -> str:
+    """Substring of the demangled kernel name that identifies a variant."""
+    bm, bn, bk = tile
+    for tag, kind in MFMA_KIND.items():
+        if f"_{tag}_" in variant_name:
+            return f"MfmaConfig<{kind}, {bm}, {bn}, {bk},"
+    return f"FmaConfig<{bm}, {bn}, {bk}>"
+
+
+def measured_traffic(variant_name: str, tile):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources; None otherwise."""
     try:
@@ -72,8 +84,9 @@ def measured_traffic(variant_name: str, workload: str):
         return None
     if rec.get("kernel_src_digest") != kernel_source_digest():
         return None
-    ent = rec.get("kernels", {}).get(f"{workload}:{variant_name}")
-    return None if ent is None else ent.get("hbm_bytes_per_launch")
+    key = kernel_name_key(variant_name, tile)
+    hits = [v["hbm_bytes_per_launch"] for k, v in rec.get("kernels", {}).items() if key in k]
+    return hits[0] if len(hits) == 1 else None
 
 
 class Part:
@@ -131,11 +144,55 @@ def oracle_sample_rate(part: Part, cores: int, budget_s: float):
                            B.shape[1], w.beta, C_np, w.N, ii, jj, nthreads=cores)
         return time.perf_counter() - t0
 
-    t = run(max(cores * 4, 64))          # calibrate
-    rate = max(cores * 4, 64) / max(t, 1e-6)
-    n = int(min(max(rate * budget_s, 256), 4_000_000))
+    n = max(cores * 64, 256)             # calibrate: grow until a run takes budget/8
+    t = run(n)
+    while t < budget_s / 8 and n < 4_000_000:
+        n *= 4
+        t = run(n)
+    n = int(min(n * budget_s / max(t, 1e-6), 16_000_000))
     t = run(n)
     return {"outputs": n, "seconds": t, "tflops": 2.0 * w.K * n / t / 1e12}
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
+    the copy kernel's reading against its known byte count."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        acc = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                acc.setdefault(name, []).append(float(row["Counter_Value"]))
+        return {k: float(np.mean(v)) for k, v in acc.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    if not copy:
+        print("no copy kernel found in the counter CSV", file=sys.stderr)
+        return 1
+    ck = max(copy, key=lambda k: fetch[k])
+    copy_bytes = float(os.environ.get("COPY_PROBE_BYTES", 512 << 20))
+    f_scale = copy_bytes / (fetch[ck] * 1024.0)
+    w_scale = copy_bytes / (write.get(ck, fetch[ck]) * 1024.0)
+    rec = {"kernel_src_digest": kernel_source_digest(), "copy_kernel": ck,
+           "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": {}}
+    for k in fetch:
+        m = re.search(r"mfma_gemm_kernel|fma_gemm_kernel", k)
+        if not m:
+            continue
+        rec["kernels"][k] = {
+            "fetch_kib_raw": fetch[k], "write_kib_raw": write.get(k),
+            "hbm_bytes_per_launch": fetch[k] * 1024.0 * f_scale
+            + (write.get(k, 0.0) * 1024.0 * w_scale)}
+    print(json.dumps(rec, indent=1))
+    return 0
 
 
 def main(argv=None):
@@ -144,10 +201,18 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=2, help="buffer sets per workload")
-    ap.add_argument("--cpu-budget", type=float, default=6.0,
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle work per workload for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (a known-size kernel "
+                         "for scaling HBM byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
+                         "a --copy-probe run into the HBM-traffic record, then exit")
     args = ap.parse_args(argv)
+    if args.ingest_pmc:
+        return ingest_pmc(*args.ingest_pmc)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -167,6 +232,14 @@ def main(argv=None):
         for p in parts:
             p.launch(sh)
     torch.cuda.synchronize()
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -186,7 +259,6 @@ def main(argv=None):
     for p in parts:
         kms = p.kernel_ms()
         tf = p.w.flops / (kms * 1e-3) / 1e12
-        vid = g.gemm_last_variant(h) if False else None
         report_parts[p.name] = {"kernel_ms": round(kms, 4), "tflops": round(tf, 2),
                                 "frac_of_peak": round(tf / PEAK_TFLOPS[p.w.dtype], 4),
                                 "peak_tflops": PEAK_TFLOPS[p.w.dtype]}
@@ -196,7 +268,9 @@ def main(argv=None):
         w = p.w
         g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB, alpha=w.alpha,
                       beta=w.beta)
-        report_parts[p.name]["variant"] = g.gemm_variant_name(g.gemm_last_variant(h))
+        vid = g.gemm_last_variant(h)
+        report_parts[p.name]["variant"] = g.gemm_variant_name(vid)
+        report_parts[p.name]["tile"] = list(g.gemm_variant_tile(vid))
     torch.cuda.synchronize()
 
     dom = max(parts, key=lambda p: report_parts[p.name]["kernel_ms"])
@@ -205,7 +279,7 @@ def main(argv=None):
     roofline = {"bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_TFLOPS[dom.w.dtype], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[dom.w.dtype], 4),
-                "traffic": measured_traffic(drep["variant"], dom.name),
+                "traffic": measured_traffic(drep["variant"], drep["tile"]),
                 "kernel": drep["variant"], "workload": dom.name,
                 "compulsory_bytes": compulsory_bytes(dom.w)}
 

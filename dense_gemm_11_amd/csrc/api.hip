@@ -63,13 +63,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // tails and small shapes).
 int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/)
 {
-    static const int bf16_big = find_variant("bf16_mfma16x16x32_256x256x64_w2x2");
+    static const int bf16_big = find_variant("bf16_mfma32x32x16_256x256x64_w2x2");
     static const int bf16_mid = find_variant("bf16_mfma16x16x32_128x128x64_w2x2");
     static const int f32_big = find_variant("f32_mfma32x32x2_256x256x32_w2x2");
     static const int f32_mid = find_variant("f32_mfma32x32x2_128x128x32_w2x2");
     const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
-    if (dtype == GEMM_DTYPE_BF16_F32) return big_tiles >= 192 ? bf16_big : bf16_mid;
-    return big_tiles >= 192 ? f32_big : f32_mid;
+    if (dtype == GEMM_DTYPE_BF16_F32) return big_tiles >= 96 ? bf16_big : bf16_mid;
+    return big_tiles >= 96 ? f32_big : f32_mid;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
