@@ -36,7 +36,8 @@ const std::vector<Variant>& table()
 {
     static const std::vector<Variant> t = [] {
         std::vector<Variant> v;
-        for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table}) {
+        for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
+                         bf16dma_variant_table}) {
             int n = 0;
             const Variant* t = get(&n);
             v.insert(v.end(), t, t + n);
@@ -60,16 +61,24 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (the tile's input intensity grows with BM*BN/(BM+BN), "GEMM on NVIDIA
 // GPUs", section 3) but fewer workgroups; small problems take the smaller
 // tile so that enough of the 256 compute units get work (section 5 on
-// tails and small shapes).
-int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/)
+// tails and small shapes).  bf16 operands whose rows are 16-byte aligned use
+// the direct-to-LDS kernels; misaligned ones (element loads on every step)
+// use the register-staged kernel, which measured faster on that path.
+int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool aligned)
 {
+    static const int bf16_dma_big = find_variant("bf16_dma32x32x16_256x256x32_w2x2_s4");
+    static const int bf16_dma_mid = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4");
     static const int bf16_big = find_variant("bf16_mfma32x32x16_256x256x64_w2x2");
     static const int bf16_mid = find_variant("bf16_mfma16x16x32_128x128x64_w2x2");
     static const int f32_big = find_variant("f32_mfma32x32x2_256x256x32_w2x2");
     static const int f32_mid = find_variant("f32_mfma32x32x2_128x128x32_w2x2");
     const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
-    if (dtype == GEMM_DTYPE_BF16_F32) return big_tiles >= 96 ? bf16_big : bf16_mid;
-    return big_tiles >= 96 ? f32_big : f32_mid;
+    const bool big = big_tiles >= 96;
+    if (dtype == GEMM_DTYPE_BF16_F32) {
+        if (aligned) return big ? bf16_dma_big : bf16_dma_mid;
+        return big ? bf16_big : bf16_mid;
+    }
+    return big ? f32_big : f32_mid;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -151,7 +160,7 @@ int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, 
     if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32) ||
         (transA != GEMM_OP_N && transA != GEMM_OP_T) || (transB != GEMM_OP_N && transB != GEMM_OP_T))
         return -1;
-    return dg::select_variant(dtype, M, N, K);
+    return dg::select_variant(dtype, M, N, K, true);
 }
 
 gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M, int64_t N,
@@ -214,11 +223,11 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
         return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     }
 
-    int id = h->forced_variant >= 0 ? h->forced_variant : select_variant(dtype, M, N, K);
-    const Variant& v = table()[id];
-    if (v.dtype != (int)dtype) return GEMM_ERR_NOT_SUPPORTED;
     const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
     const bool aligned = aligned16(A) && aligned16(B) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
+    int id = h->forced_variant >= 0 ? h->forced_variant : select_variant(dtype, M, N, K, aligned);
+    const Variant& v = table()[id];
+    if (v.dtype != (int)dtype) return GEMM_ERR_NOT_SUPPORTED;
     a.tiles_m = (int)ceil_div(M, v.bm);
     a.tiles_n = (int)ceil_div(N, v.bn);
     a.group_m = std::min(a.tiles_m, 8);

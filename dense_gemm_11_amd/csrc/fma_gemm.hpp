@@ -97,7 +97,7 @@ struct FmaLoader {
 };
 
 template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED>
-__global__ __launch_bounds__(256) void fma_gemm_kernel(GemmArgs p)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) void fma_gemm_kernel(GemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, SA = Cfg::SA, SB = Cfg::SB;
     __shared__ __attribute__((aligned(16))) float smem[2 * Cfg::STAGE_FLOATS];
@@ -148,18 +148,27 @@ __global__ __launch_bounds__(256) void fma_gemm_kernel(GemmArgs p)
         if (more) load_step(kt + 1);
         const float* As = smem + cur * Cfg::STAGE_FLOATS;
         const float* Bs = As + BK * SA;
+        // operands of k+1 are read while the 64 FMAs of k run; the scheduling
+        // barrier keeps the compiler from hoisting every k's reads at once
+        f32x4 a0 = *reinterpret_cast<const f32x4*>(As + ty * 4);
+        f32x4 a1 = *reinterpret_cast<const f32x4*>(As + BM / 2 + ty * 4);
+        f32x4 b0 = *reinterpret_cast<const f32x4*>(Bs + tx * 4);
+        f32x4 b1 = *reinterpret_cast<const f32x4*>(Bs + BN / 2 + tx * 4);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(As + k * SA + ty * 4);
-            const f32x4 a1 = *reinterpret_cast<const f32x4*>(As + k * SA + BM / 2 + ty * 4);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(Bs + k * SB + tx * 4);
-            const f32x4 b1 = *reinterpret_cast<const f32x4*>(Bs + k * SB + BN / 2 + tx * 4);
             const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            if (k + 1 < BK) {
+                a0 = *reinterpret_cast<const f32x4*>(As + (k + 1) * SA + ty * 4);
+                a1 = *reinterpret_cast<const f32x4*>(As + (k + 1) * SA + BM / 2 + ty * 4);
+                b0 = *reinterpret_cast<const f32x4*>(Bs + (k + 1) * SB + tx * 4);
+                b1 = *reinterpret_cast<const f32x4*>(Bs + (k + 1) * SB + BN / 2 + tx * 4);
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (more) {
             float* nxt = smem + (cur ^ 1) * Cfg::STAGE_FLOATS;

@@ -1,0 +1,510 @@
+// bf16 matrix-core GEMM for gfx950 with direct-to-LDS loads and an S-stage
+// LDS ring: D = alpha * op(A) * op(B) + beta * C, bf16 operands, fp32 out.
+//
+// Same hierarchical tiling as mfma_gemm.hpp ("GEMM on NVIDIA GPUs: from a
+// naive kernel to a tiled pipeline", section 4), with the load/compute
+// overlap of its "load-compute overlap" part made deeper:
+//
+//  * Each operand tile of a K-step goes from global memory straight into LDS
+//    with global_load_lds_dwordx4 (lane l of a wave writes its 16 bytes at the
+//    instruction's LDS base + 16*l), so no registers hold tiles in flight and
+//    no VALU or LDS-write instructions are spent on staging.  Which global
+//    16-byte chunk a lane fetches is chosen so the LDS image comes out in the
+//    swizzled layout below.
+//  * Operands keep their memory orientation in LDS.  A k-contiguous operand
+//    (A with transA == N, B with transB == T) is stored [mn][k] in 16-byte
+//    chunks with the chunk index XOR-swizzled by row, and its MFMA fragments
+//    are read with ds_read_b128.  An mn-contiguous operand (A with T, B with N)
+//    is stored [k][mn] with 32-byte blocks XOR-swizzled by a table indexed by
+//    (k mod 4), and its
+//    fragments are read with two ds_read_b64_tr_b16: within each 16-lane
+//    group, lane r+4j supplies the address of (k0+j, mn0+4r..4r+3) and lane
+//    4r+e receives element e of lanes r, r+4, r+8, r+12, i.e. four
+//    consecutive k of column mn0+4r+e — exactly an MFMA operand slice.
+//  * S >= 3 stages in separate __shared__ arrays (static indices keep the
+//    compiler's LDS-DMA dependency tracking exact).  One barrier per stage,
+//    placed half way through the stage's MFMAs: before it each wave waits
+//    until the next stage's DMA has landed; after it the DMA for the stage
+//    S-1 ahead is issued (into the buffer every wave has finished reading)
+//    and the next stage's first fragments are read while the MFMAs run.
+//  * MFMA operands are swapped (B fragment first), so each lane's
+//    accumulators hold 4 adjacent output columns of one row: the epilogue
+//    writes 16-byte vectors.
+//  * Edge tiles, the ragged last K-step and misaligned operands take a
+//    register-staged path with per-element zero fill that writes the same
+//    LDS layout (ds_write_b128).
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "mfma_gemm.hpp"
+
+namespace dg {
+
+template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_>
+struct DmaConfig {
+    static constexpr int KIND = KIND_, BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_;
+    using T = bf16_t;
+    static constexpr int VEC = 8;                      // bf16 per 16-byte chunk
+    static constexpr int FM = MfmaShape<KIND>::FM;
+    static constexpr int ACC = MfmaShape<KIND>::ACC;
+    static constexpr int KG = 64 / FM;                 // lane groups along k
+    static constexpr int KSTEP = KG * VEC;             // k per fragment
+    static constexpr int NKS = BK / KSTEP;             // fragment steps per stage
+    static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int MF = WTM / FM, NF = WTN / FM;
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int A_DMA = A_BYTES / (1024 * WAVES);  // DMA instructions per wave
+    static constexpr int B_DMA = B_BYTES / (1024 * WAVES);
+    static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
+    static_assert(KIND == MFMA_BF16_32x32x16 || KIND == MFMA_BF16_16x16x32, "bf16 only");
+    static_assert(S >= 3 && S <= 4, "stage count");
+    static_assert(NKS >= 2 && NKS % 2 == 0, "barrier sits between fragment steps");
+    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "DMA split");
+    static_assert(BM % (WM * FM) == 0 && BN % (WN * FM) == 0, "wave tile");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+    static_assert(DMA_PER_STAGE * (S - 2) < 64, "vmcnt range");
+};
+
+// XOR applied to the 16-byte chunk index of row k of an [k][mn] tile: {0, 4,
+// 10, 14} for k mod 4 = 0..3.  A transposed fragment read touches 4 rows and,
+// per 16 lanes, 2 adjacent chunks (32 bytes): with these masks the 4 rows'
+// chunk pairs fill a 128-byte bank window exactly, and the two 16-lane groups
+// of a 32-lane half (chunks 2 apart) fill a 256-byte window exactly.
+__device__ __forceinline__ int mn_swz(int k) { return (0x0E0A0400 >> (8 * (k & 3))) & 0xFF; }
+
+// LDS layout of one operand tile.  R = rows of the tile in the mn direction.
+template <class Cfg, int R, bool KC>
+struct Layout {
+    static constexpr int BK = Cfg::BK;
+    static constexpr int CPR_K = BK / 8;   // chunks per [mn][k] row
+    static constexpr int CPR_M = R / 8;    // chunks per [k][mn] row
+    static_assert(!KC || CPR_K == 4 || CPR_K == 8, "k-major swizzle");
+    static_assert(KC || CPR_M >= 16, "mn-major swizzle needs >= 16 chunks per row");
+    // byte offset of 16-byte chunk `chunk` in LDS row `row`
+    __device__ static __forceinline__ int off(int row, int chunk)
+    {
+        if constexpr (KC)
+            return row * (CPR_K * 16) + ((chunk ^ swz<CPR_K>(row)) << 4);
+        else
+            return row * (CPR_M * 16) + ((chunk ^ mn_swz(row)) << 4);
+    }
+    static constexpr int ROWS = KC ? R : BK;        // LDS rows
+    static constexpr int CPR = KC ? CPR_K : CPR_M;  // chunks per LDS row
+};
+
+template <class Cfg, int R, bool KC, bool ALIGNED>
+struct DmaOperand {
+    using L = Layout<Cfg, R, KC>;
+    static constexpr int ND = (R * Cfg::BK * 2) / (1024 * Cfg::WAVES);  // DMA instructions per wave
+    static constexpr int CHUNKS = L::ROWS * L::CPR;
+    static constexpr int GL = (CHUNKS + Cfg::THREADS - 1) / Cfg::THREADS;  // guarded loads per thread
+
+    int64_t goff[ND];  // per-lane element offsets of this lane's DMA chunks (k0 = 0)
+
+    // Element offset (from the panel start, k0 = 0) of logical chunk c of LDS
+    // row `row`: row = mn and chunks along k (KC), or row = k and chunks along mn.
+    __device__ static __forceinline__ int64_t chunk_src(int row, int c, int64_t ld)
+    {
+        return (int64_t)row * ld + c * 8;
+    }
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
+    {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+            const int pos = (wave * ND + d) * 1024 + lane * 16;  // byte position in the tile
+            const int row = pos / (L::CPR * 16);
+            const int pc = (pos % (L::CPR * 16)) >> 4;
+            // invert the swizzle: which logical chunk lives at physical chunk pc
+            int c;
+            if constexpr (KC) c = pc ^ swz<L::CPR_K>(row);
+            else c = pc ^ mn_swz(row);
+            goff[d] = chunk_src(row, c, ld);
+        }
+    }
+
+    // Asynchronous copy of the step at k0 into `lds` (tile base in LDS).  Issued
+    // through inline asm: the kernel orders these copies itself with explicit
+    // s_waitcnt vmcnt + s_barrier, so the compiler's own (conservative) LDS-DMA
+    // tracking does not add waits; any wait it inserts for its own loads can
+    // only become stronger because of these extra outstanding operations.
+    __device__ __forceinline__ void dma(const bf16_t* panel, int64_t ld, int k0, char* lds,
+                                        int wave) const
+    {
+        const int64_t kstep = KC ? (int64_t)k0 : (int64_t)k0 * ld;
+        const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+            const bf16_t* src = panel + kstep + goff[d];
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                         :
+                         : "s"(lds_base + d * 1024), "v"(src)
+                         : "memory", "m0");
+        }
+    }
+
+    // The d-th DMA copy instruction of dma() on its own (for interleaving).
+    __device__ __forceinline__ void dma_one(int d, const bf16_t* panel, int64_t ld, int k0,
+                                            char* lds, int wave) const
+    {
+        const int64_t kstep = KC ? (int64_t)k0 : (int64_t)k0 * ld;
+        const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
+        const bf16_t* src = panel + kstep + goff[d];
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(lds_base + d * 1024), "v"(src)
+                     : "memory", "m0");
+    }
+
+    // Register-staged copy with zero fill outside [0, rlim) x [0, K).
+    __device__ __forceinline__ void guarded(const bf16_t* panel, int64_t ld, int rlim, int k0,
+                                            int K, char* lds, int tid) const
+    {
+        u32x4 v[GL];
+#pragma unroll
+        for (int i = 0; i < GL; ++i) {
+            const int q = tid + i * Cfg::THREADS;
+            if (CHUNKS % Cfg::THREADS != 0 && q >= CHUNKS) break;
+            const int row = q / L::CPR, c = q % L::CPR;
+            bf16_t e[8];
+            if constexpr (KC) {   // row = mn, elements along k
+                const int k = k0 + c * 8;
+                const bf16_t* src = panel + (int64_t)row * ld + k;
+                if (ALIGNED && row < rlim && k + 8 <= K) {
+                    v[i] = *reinterpret_cast<const u32x4*>(src);
+                    continue;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[j] = (row < rlim && k + j < K) ? src[j] : bf16_t(0);
+            } else {              // row = k, elements along mn
+                const int k = k0 + row, mn = c * 8;
+                const bf16_t* src = panel + (int64_t)k * ld + mn;
+                if (ALIGNED && k < K && mn + 8 <= rlim) {
+                    v[i] = *reinterpret_cast<const u32x4*>(src);
+                    continue;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) e[j] = (k < K && mn + j < rlim) ? src[j] : bf16_t(0);
+            }
+            v[i] = pack_chunk<bf16_t>(e);
+        }
+#pragma unroll
+        for (int i = 0; i < GL; ++i) {
+            const int q = tid + i * Cfg::THREADS;
+            if (CHUNKS % Cfg::THREADS != 0 && q >= CHUNKS) break;
+            *reinterpret_cast<u32x4*>(lds + L::off(q / L::CPR, q % L::CPR)) = v[i];
+        }
+    }
+
+    // Half h (k-slots 4h..4h+3) of an mn-major fragment via one transposing read.
+    __device__ static __forceinline__ uint64_t frag_tr_half(const char* lds, int mn0, int ks, int lane,
+                                                           int h)
+    {
+        constexpr int FM = Cfg::FM;
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const int g = lane >> 4, q = lane & 15, r = q & 3, j = q >> 2;
+        int mn, k;
+        if constexpr (FM == 32) {
+            mn = mn0 + 16 * (g & 1) + 4 * r;
+            k = ks * Cfg::KSTEP + 8 * (g >> 1) + 4 * h + j;
+        } else {
+            mn = mn0 + 4 * r;
+            k = ks * Cfg::KSTEP + 8 * g + 4 * h + j;
+        }
+        const int o = L::off(k, mn >> 3) + (mn & 7) * 2;
+        return __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                (__attribute__((address_space(3))) s4*)(lds + o)));
+    }
+
+    // MFMA operand fragment: rows mn0 .. mn0+FM-1 (by lane), k-slots of step ks.
+    __device__ static __forceinline__ u32x4 frag(const char* lds, int mn0, int ks, int lane)
+    {
+        constexpr int FM = Cfg::FM;
+        if constexpr (KC) {
+            const int row = mn0 + lane % FM;
+            const int chunk = ks * Cfg::KG + lane / FM;
+            return *reinterpret_cast<const u32x4*>(lds + L::off(row, chunk));
+        } else {
+            const uint64_t lo = frag_tr_half(lds, mn0, ks, lane, 0);
+            const uint64_t hi = frag_tr_half(lds, mn0, ks, lane, 1);
+            return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+        }
+    }
+
+    // The n-th of the NREAD memory instructions that read one fragment set
+    // piece by piece (KC: one 16-byte read per fragment; MN: two halves).
+    static constexpr int NREAD_PER_FRAG = KC ? 1 : 2;
+};
+
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt fields at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0), expcnt untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED>
+__global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
+    constexpr int MF = Cfg::MF, NF = Cfg::NF, NKS = Cfg::NKS;
+    using Acc = typename AccType<Cfg::KIND>::type;
+    using OpA = DmaOperand<Cfg, BM, A_KC, ALIGNED>;
+    using OpB = DmaOperand<Cfg, BN, B_KC, ALIGNED>;
+
+    __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[Cfg::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? Cfg::STAGE_BYTES : 16];
+    auto stage = [&](int s) -> char* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_m0 = (wave / Cfg::WN) * Cfg::WTM;
+    const int wave_n0 = (wave % Cfg::WN) * Cfg::WTN;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rlim_a = p.M - m0, rlim_b = p.N - n0;
+    const bool edge = rlim_a < BM || rlim_b < BN;
+    const bf16_t* A = static_cast<const bf16_t*>(p.A);
+    const bf16_t* B = static_cast<const bf16_t*>(p.B);
+    const bf16_t* panel_a = A_KC ? A + (int64_t)m0 * p.lda : A + m0;
+    const bf16_t* panel_b = B_KC ? B + (int64_t)n0 * p.ldb : B + n0;
+
+    OpA oa;
+    OpB ob;
+    oa.init(wave, lane, p.lda);
+    ob.init(wave, lane, p.ldb);
+
+    const int nk = (p.K + BK - 1) / BK;
+    const bool k_ragged = (p.K % BK) != 0;
+    // steps that can be copied by DMA: whole step in range and aligned
+    const int nk_dma = (ALIGNED && !edge) ? (k_ragged ? nk - 1 : nk) : 0;
+
+    auto load = [&](int kt, char* base) {
+        const int k0 = kt * BK;
+        if (kt < nk_dma) {
+            oa.dma(panel_a, p.lda, k0, base, wave);
+            ob.dma(panel_b, p.ldb, k0, base + Cfg::A_BYTES, wave);
+        } else {
+            oa.guarded(panel_a, p.lda, rlim_a, k0, p.K, base, tid);
+            ob.guarded(panel_b, p.ldb, rlim_b, k0, p.K, base + Cfg::A_BYTES, tid);
+        }
+    };
+
+    Acc acc[MF][NF];
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int j = 0; j < NF; ++j) acc[i][j] = Acc{};
+
+    // prologue: steps 0 .. S-2 in flight, wait for step 0
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (s < nk) load(s, stage(s));
+    if (nk >= S - 1) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (S - 2)>();
+    else wait_vm_lgkm0<0>();
+    barrier_only();
+
+    u32x4 fa[2][MF], fb[2][NF];
+    auto read_frags = [&](const char* base, int ks, int buf) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i) fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+            fb[buf][j] = OpB::frag(base + Cfg::A_BYTES, wave_n0 + j * FM, ks, lane);
+    };
+    read_frags(stage(0), 0, 0);
+
+    // One K-step held in LDS stage CUR (static, so every LDS address is a
+    // compile-time offset from its own __shared__ array).  STEADY: the step
+    // S-1 ahead exists and is copied by DMA, so no run-time conditions.
+    auto step = [&](auto cur_c, auto steady_c, int kt) {
+        constexpr int CUR = decltype(cur_c)::value;
+        constexpr bool STEADY = decltype(steady_c)::value;
+        constexpr int NXT = (CUR + 1) % S;
+        constexpr int FAR = (CUR + S - 1) % S;
+        const char* base = stage(CUR);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if (ks == NKS / 2) {
+                // the next step must have landed in every wave's part of LDS
+                if (STEADY || kt + S - 1 <= nk) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (S - 3)>();
+                else wait_vm_lgkm0<0>();
+                barrier_only();
+                if (STEADY) {
+                    oa.dma(panel_a, p.lda, (kt + S - 1) * BK, stage(FAR), wave);
+                    ob.dma(panel_b, p.ldb, (kt + S - 1) * BK, stage(FAR) + Cfg::A_BYTES, wave);
+                } else if (kt + S - 1 < nk) {
+                    load(kt + S - 1, stage(FAR));
+                }
+            }
+            const int cb = ks & 1;
+            if (ks + 1 < NKS) read_frags(base, ks + 1, cb ^ 1);
+            else if (STEADY || kt + 1 < nk) read_frags(stage(NXT), 0, cb ^ 1);
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int j = 0; j < NF; ++j) mfma_step<Cfg::KIND>(fb[cb][j], fa[cb][i], acc[i][j]);
+        }
+    };
+    // Steady-state step with a pinned instruction order: every MFMA of a
+    // fragment step is followed by one or two memory instructions (the next
+    // fragment set's LDS reads and, in the second half, the DMA copies of the
+    // step S-1 ahead), so the matrix core is fed while loads are in flight.
+    constexpr int RA = OpA::NREAD_PER_FRAG, RB = OpB::NREAD_PER_FRAG;
+    constexpr int NREAD = MF * RA + NF * RB;
+    constexpr int NMFMA = MF * NF;
+    constexpr int NDMA = OpA::ND + OpB::ND;
+    auto read_op = [&](int n, const char* base, int ks, int buf) {
+        if (n < MF * RA) {
+            const int i = n / RA;
+            if constexpr (RA == 1) {
+                fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
+            } else {
+                const uint64_t v = OpA::frag_tr_half(base, wave_m0 + i * FM, ks, lane, n % RA);
+                fa[buf][i][2 * (n % RA)] = (uint32_t)v;
+                fa[buf][i][2 * (n % RA) + 1] = (uint32_t)(v >> 32);
+            }
+        } else {
+            const int m = n - MF * RA, j = m / RB;
+            const char* bb = base + Cfg::A_BYTES;
+            if constexpr (RB == 1) {
+                fb[buf][j] = OpB::frag(bb, wave_n0 + j * FM, ks, lane);
+            } else {
+                const uint64_t v = OpB::frag_tr_half(bb, wave_n0 + j * FM, ks, lane, m % RB);
+                fb[buf][j][2 * (m % RB)] = (uint32_t)v;
+                fb[buf][j][2 * (m % RB) + 1] = (uint32_t)(v >> 32);
+            }
+        }
+    };
+    auto steady = [&](auto cur_c, int kt) {
+        constexpr int CUR = decltype(cur_c)::value;
+        constexpr int NXT = (CUR + 1) % S;
+        constexpr int FAR = (CUR + S - 1) % S;
+        const char* base = stage(CUR);
+        const int kfar = (kt + S - 1) * BK;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int cb = ks & 1;
+            const bool mid = ks == NKS / 2;
+            if (mid) {
+                wait_vm<Cfg::DMA_PER_STAGE * (S - 3)>();
+                barrier_only();
+            }
+            const char* rbase = ks + 1 < NKS ? base : stage(NXT);
+            const int rks = ks + 1 < NKS ? ks + 1 : 0;
+            const int nops = NREAD + (mid ? NDMA : 0);
+#pragma unroll
+            for (int e = 0; e < NMFMA; ++e) {
+                mfma_step<Cfg::KIND>(fb[cb][e % NF], fa[cb][e / NF], acc[e / NF][e % NF]);
+                __builtin_amdgcn_sched_barrier(0);
+                // front-load: fragment reads go out over the first half of the
+                // MFMAs (two per MFMA), DMA copies over the rest
+                constexpr int HALF = NMFMA / 2;
+                const int lo = e < HALF ? e * NREAD / HALF
+                                        : NREAD + (e - HALF) * (nops - NREAD) / (NMFMA - HALF);
+                const int hi = e + 1 < HALF ? (e + 1) * NREAD / HALF
+                             : e + 1 == HALF ? NREAD
+                                             : NREAD + (e + 1 - HALF) * (nops - NREAD) / (NMFMA - HALF);
+#pragma unroll
+                for (int o = lo; o < hi; ++o) {
+                    if (o < NREAD) read_op(o, rbase, rks, cb ^ 1);
+                    else if (o - NREAD < OpA::ND)
+                        oa.dma_one(o - NREAD, panel_a, p.lda, kfar, stage(FAR), wave);
+                    else
+                        ob.dma_one(o - NREAD - OpA::ND, panel_b, p.ldb, kfar,
+                                   stage(FAR) + Cfg::A_BYTES, wave);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    int kt = 0;
+    // steady state: every step of the group issues a DMA copy S-1 steps ahead
+    for (; kt + 2 * S - 2 < nk_dma; kt += S) {
+        steady(I0{}, kt);
+        steady(I1{}, kt + 1);
+        steady(I2{}, kt + 2);
+        if constexpr (S > 3) steady(I3{}, kt + 3);
+    }
+    // tail: remaining steps with run-time checks (guarded copies allowed)
+    for (; kt < nk; kt += S) {
+        step(I0{}, F_{}, kt);
+        if (kt + 1 < nk) step(I1{}, F_{}, kt + 1);
+        if (kt + 2 < nk) step(I2{}, F_{}, kt + 2);
+        if constexpr (S > 3)
+            if (kt + 3 < nk) step(I3{}, F_{}, kt + 3);
+    }
+
+    // ---- epilogue: lane holds 4 adjacent columns of one row per accumulator group
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+        const int row = m0 + wave_m0 + i * FM + lane % FM;
+        if (row >= p.M) continue;
+        float* drow = p.D + (int64_t)row * p.ldd;
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+#pragma unroll
+            for (int vg = 0; vg < Cfg::ACC / 4; ++vg) {
+                const int col = n0 + wave_n0 + j * FM +
+                                (FM == 32 ? 8 * vg + 4 * (lane >> 5) : 4 * (lane >> 4));
+                float out[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) out[s] = alpha * acc[i][j][4 * vg + s];
+                if (p.d_vec && col + 4 <= p.N) {
+                    if (beta != 0.0f) {
+                        const float* crow = p.C + (int64_t)row * p.ldc;
+                        if (p.c_vec) {
+                            const f32x4 c = *reinterpret_cast<const f32x4*>(crow + col);
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) out[s] += beta * c[s];
+                        } else {
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) out[s] += beta * crow[col + s];
+                        }
+                    }
+                    *reinterpret_cast<f32x4*>(drow + col) = f32x4{out[0], out[1], out[2], out[3]};
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        if (col + s < p.N) {
+                            float o = out[s];
+                            if (beta != 0.0f) o += beta * p.C[(int64_t)row * p.ldc + col + s];
+                            drow[col + s] = o;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace dg

@@ -33,6 +33,7 @@ hipError_t launch_kernel(const GemmArgs& a, int grid, hipStream_t s)
 const Variant* bf16_variant_table(int* count);
 const Variant* f32mfma_variant_table(int* count);
 const Variant* f32fma_variant_table(int* count);
+const Variant* bf16dma_variant_table(int* count);
 
 }  // namespace dg
 

@@ -128,8 +128,9 @@ gemm_status_t gemm_set_variant(gemm_handle_t h, int id);
  * call launched no GEMM kernel). */
 int gemm_last_variant(gemm_handle_t h);
 
-/* The variant automatic selection would use for this problem (pure host
- * logic, no HIP call); -1 for an invalid dtype/transpose. */
+/* The variant automatic selection would use for this problem when A and B
+ * are 16-byte aligned with 16-byte-multiple row pitches (pure host logic, no
+ * HIP call); -1 for an invalid dtype/transpose. */
 int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB,
                         int64_t M, int64_t N, int64_t K);
 

@@ -40,7 +40,8 @@ def test_small_shapes_automatic_selection(handle, dtype, ta, tb):
         assert err <= tol, (dtype, ta, tb, M, N, K, alpha, beta, err)
 
 
-VARIANT_SHAPES = [(300, 200, 100), (257, 513, 77), (256, 256, 128), (1, 300, 40), (520, 9, 300)]
+VARIANT_SHAPES = [(300, 200, 100), (257, 513, 77), (256, 256, 128), (1, 300, 40), (520, 9, 300),
+                  (512, 256, 1000), (256, 512, 1024)]
 
 
 def _variant_ids(dtype):
