@@ -127,6 +127,49 @@ class Part:
         return float(np.mean([a.elapsed_time(b) for a, b in self.events]))
 
 
+def roofline_tflops(w: workloads.Workload) -> float:
+    """min(compute peak, HBM bandwidth x compulsory intensity), in TFLOP/s
+    ("GEMM on NVIDIA GPUs", section 2, roofline bound)."""
+    return min(PEAK_TFLOPS[w.dtype], HBM_GBS * 1e9 * w.flops / compulsory_bytes(w) / 1e12)
+
+
+def time_extra(g, h, name: str, variant_name, reps: int, warmup: int):
+    """Time one workload outside the step (own buffers, HIP events)."""
+    w = workloads.WORKLOADS[name]
+    A, B, C = workloads.make_inputs(w)
+    A, B = A.cuda(), B.cuda()
+    C = None if C is None else C.cuda()
+    D = torch.empty(w.M, w.N, dtype=torch.float32, device="cuda")
+    vid = -1
+    if variant_name is not None:
+        vid = [i for i, n, _, _ in g.variants() if n == variant_name][0]
+    g.gemm_set_variant(h, vid)
+    try:
+        run = lambda: g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
+                                    alpha=w.alpha, beta=w.beta)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        used = g.gemm_variant_name(g.gemm_last_variant(h))
+    finally:
+        g.gemm_set_variant(h, -1)
+    ms = e0.elapsed_time(e1) / reps
+    tf = w.flops / (ms * 1e-3) / 1e12
+    roof = roofline_tflops(w)
+    del A, B, C, D
+    return {"kernel_ms": round(ms, 4), "tflops": round(tf, 2), "variant": used,
+            "peak_tflops": PEAK_TFLOPS[w.dtype], "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+            "roofline_tflops": round(roof, 1), "frac_of_roofline": round(tf / roof, 4),
+            "workload": w.description}
+
+
 def oracle_sample_rate(part: Part, cores: int, budget_s: float):
     """Time the CPU oracle on a sample of outputs of the part's workload."""
     import oracle
@@ -204,6 +247,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle work per workload for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the untimed-for-value vector-FMA and edge-workload rows")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (a known-size kernel "
                          "for scaling HBM byte counters)")
@@ -283,6 +328,15 @@ def main(argv=None):
                 "kernel": drep["variant"], "workload": dom.name,
                 "compulsory_bytes": compulsory_bytes(dom.w)}
 
+    # the remaining hot-path rows, timed outside the step: the fp32 vector-FMA
+    # mainloop at 4096^3, and the full alpha/beta epilogue with ragged edges
+    extras = {}
+    if not args.no_extras:
+        extras["fp32_4096_vector_fma"] = time_extra(g, h, "fp32_4096", "f32_vfma_128x128x8_t8x8",
+                                                    reps=10, warmup=3)
+        extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
+                                                       warmup=5)
+
     cpu = None
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
@@ -301,7 +355,7 @@ def main(argv=None):
         "dtype": "fp32 + bf16-in/fp32-acc", "data": "synthetic",
         "config": {"workload": "fp32 GEMM 4096^3 + bf16->fp32 GEMM 8192^3 (NN, alpha=1, beta=0)",
                    "parallelism": "single GPU", "buffer_sets": args.sets},
-        "parts": report_parts, "roofline": roofline, "cpu_baseline": cpu,
+        "parts": report_parts, "extra_rows": extras, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     g.gemm_destroy(h)

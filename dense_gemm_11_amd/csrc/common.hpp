@@ -31,7 +31,7 @@ struct GemmArgs {
     int M, N, K;
     float alpha, beta;
     int tiles_m, tiles_n;  // output tiles along M and N
-    int group_m;           // tile-rows walked together for L2 reuse
+    int group_m;           // tile-rows walked together for L2/MALL reuse
     int c_vec;             // C rows allow 16-byte loads (pointer and ldc aligned)
     int d_vec;             // D rows allow 16-byte stores
 };

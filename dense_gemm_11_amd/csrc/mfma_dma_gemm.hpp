@@ -62,7 +62,7 @@ struct DmaConfig {
     static constexpr int B_DMA = B_BYTES / (1024 * WAVES);
     static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
     static_assert(KIND == MFMA_BF16_32x32x16 || KIND == MFMA_BF16_16x16x32, "bf16 only");
-    static_assert(S >= 3 && S <= 4, "stage count");
+    static_assert(S >= 3 && S <= 5, "stage count");
     static_assert(NKS >= 2 && NKS % 2 == 0, "barrier sits between fragment steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "DMA split");
     static_assert(BM % (WM * FM) == 0 && BN % (WN * FM) == 0, "wave tile");
@@ -274,7 +274,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st2[Cfg::STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? Cfg::STAGE_BYTES : 16];
-    auto stage = [&](int s) -> char* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
+    __shared__ __attribute__((aligned(1024))) char st4[S > 4 ? Cfg::STAGE_BYTES : 16];
+    auto stage = [&](int s) -> char* {
+        return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : s == 3 ? st3 : st4;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wave_m0 = (wave / Cfg::WN) * Cfg::WTM;
@@ -445,6 +448,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
 
     int kt = 0;
     // steady state: every step of the group issues a DMA copy S-1 steps ahead
@@ -453,6 +457,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         steady(I1{}, kt + 1);
         steady(I2{}, kt + 2);
         if constexpr (S > 3) steady(I3{}, kt + 3);
+        if constexpr (S > 4) steady(I4{}, kt + 4);
     }
     // tail: remaining steps with run-time checks (guarded copies allowed)
     for (; kt < nk; kt += S) {
@@ -461,6 +466,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         if (kt + 2 < nk) step(I2{}, F_{}, kt + 2);
         if constexpr (S > 3)
             if (kt + 3 < nk) step(I3{}, F_{}, kt + 3);
+        if constexpr (S > 4)
+            if (kt + 4 < nk) step(I4{}, F_{}, kt + 4);
     }
 
     // ---- epilogue: lane holds 4 adjacent columns of one row per accumulator group
