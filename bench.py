@@ -71,6 +71,9 @@ def kernel_name_key(variant_name: str, tile) -> str:
     for tag, kind in MFMA_KIND.items():
         if f"_{tag}_" in variant_name:
             return f"MfmaConfig<{kind}, {bm}, {bn}, {bk},"
+        if f"_dma{tag[4:]}_" in variant_name:
+            stages = variant_name.rsplit("_s", 1)[1]
+            return f"DmaConfig<{kind}, {bm}, {bn}, {bk}, 2, 2, {stages}>"
     return f"FmaConfig<{bm}, {bn}, {bk}>"
 
 
@@ -227,7 +230,7 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
            "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
            "kernels": {}}
     for k in fetch:
-        m = re.search(r"mfma_gemm_kernel|fma_gemm_kernel", k)
+        m = re.search(r"gemm_kernel<", k)
         if not m:
             continue
         rec["kernels"][k] = {
