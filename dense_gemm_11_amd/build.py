@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libdense_gemm.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "inst_bf16.hip", "inst_bf16_dma.hip", "inst_f32_mfma.hip",
-           "inst_f32_fma.hip"]
+           "inst_f32_dma.hip", "inst_f32_fma.hip"]
 
 
 def hipcc() -> str:

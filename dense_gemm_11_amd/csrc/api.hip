@@ -37,7 +37,7 @@ const std::vector<Variant>& table()
     static const std::vector<Variant> t = [] {
         std::vector<Variant> v;
         for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
-                         bf16dma_variant_table}) {
+                         bf16dma_variant_table, f32dma_variant_table}) {
             int n = 0;
             const Variant* t = get(&n);
             v.insert(v.end(), t, t + n);
@@ -61,9 +61,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (the tile's input intensity grows with BM*BN/(BM+BN), "GEMM on NVIDIA
 // GPUs", section 3) but fewer workgroups; small problems take the smaller
 // tile so that enough of the 256 compute units get work (section 5 on
-// tails and small shapes).  bf16 operands whose rows are 16-byte aligned use
-// the direct-to-LDS kernels; misaligned ones (element loads on every step)
-// use the register-staged kernel, which measured faster on that path.
+// tails and small shapes).  Operands whose rows are 16-byte aligned use the
+// direct-to-LDS kernels; misaligned ones (element loads on every step) use
+// the register-staged kernels, which measured faster on that path.
 int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool aligned)
 {
     static const int bf16_dma_big = find_variant("bf16_dma32x32x16_256x256x32_w2x2_s4");
@@ -72,12 +72,15 @@ int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool aligned)
     static const int bf16_mid = find_variant("bf16_mfma16x16x32_128x128x64_w2x2");
     static const int f32_big = find_variant("f32_mfma32x32x2_256x256x32_w2x2");
     static const int f32_mid = find_variant("f32_mfma32x32x2_128x128x32_w2x2");
+    static const int f32_dma_big = find_variant("f32_dma32x32x2_256x256x16_w2x2_s4");
+    static const int f32_dma_mid = find_variant("f32_dma32x32x2_128x128x16_w2x2_s4");
     const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
     const bool big = big_tiles >= 96;
     if (dtype == GEMM_DTYPE_BF16_F32) {
         if (aligned) return big ? bf16_dma_big : bf16_dma_mid;
         return big ? bf16_big : bf16_mid;
     }
+    if (aligned) return big ? f32_dma_big : f32_dma_mid;
     return big ? f32_big : f32_mid;
 }
 

@@ -1,0 +1,23 @@
+// fp32 matrix-core variants with direct-to-LDS loads and an S-stage LDS ring.
+#include "mfma_dma_gemm.hpp"
+#include "variants.hpp"
+
+namespace dg {
+
+using F32Dma256s4 = DmaConfig<MFMA_F32_32x32x2, 256, 256, 16, 2, 2, 4>;
+using F32Dma128s4 = DmaConfig<MFMA_F32_32x32x2, 128, 128, 16, 2, 2, 4>;
+
+#define F32_DMA_VARIANT(NAME, CFG) \
+    {NAME, 0, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
+
+const Variant* f32dma_variant_table(int* count)
+{
+    static const Variant table[] = {
+        F32_DMA_VARIANT("f32_dma32x32x2_256x256x16_w2x2_s4", F32Dma256s4),
+        F32_DMA_VARIANT("f32_dma32x32x2_128x128x16_w2x2_s4", F32Dma128s4),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace dg

@@ -45,8 +45,9 @@ namespace dg {
 template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_>
 struct DmaConfig {
     static constexpr int KIND = KIND_, BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_;
-    using T = bf16_t;
-    static constexpr int VEC = 8;                      // bf16 per 16-byte chunk
+    using T = typename MfmaShape<KIND>::T;
+    static constexpr int ES = sizeof(T);
+    static constexpr int VEC = 16 / ES;                // elements per 16-byte chunk
     static constexpr int FM = MfmaShape<KIND>::FM;
     static constexpr int ACC = MfmaShape<KIND>::ACC;
     static constexpr int KG = 64 / FM;                 // lane groups along k
@@ -55,13 +56,15 @@ struct DmaConfig {
     static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MF = WTM / FM, NF = WTN / FM;
-    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = S * STAGE_BYTES;
     static constexpr int A_DMA = A_BYTES / (1024 * WAVES);  // DMA instructions per wave
     static constexpr int B_DMA = B_BYTES / (1024 * WAVES);
     static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
-    static_assert(KIND == MFMA_BF16_32x32x16 || KIND == MFMA_BF16_16x16x32, "bf16 only");
+    static_assert(KIND == MFMA_BF16_32x32x16 || KIND == MFMA_BF16_16x16x32 ||
+                      KIND == MFMA_F32_32x32x2,
+                  "instruction kinds with a defined fragment mapping");
     static_assert(S >= 3 && S <= 5, "stage count");
     static_assert(NKS >= 2 && NKS % 2 == 0, "barrier sits between fragment steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "DMA split");
@@ -81,17 +84,26 @@ __device__ __forceinline__ int mn_swz(int k) { return (0x0E0A0400 >> (8 * (k & 3
 template <class Cfg, int R, bool KC>
 struct Layout {
     static constexpr int BK = Cfg::BK;
-    static constexpr int CPR_K = BK / 8;   // chunks per [mn][k] row
-    static constexpr int CPR_M = R / 8;    // chunks per [k][mn] row
+    static constexpr int CPR_K = BK / Cfg::VEC;   // chunks per [mn][k] row
+    static constexpr int CPR_M = R / Cfg::VEC;    // chunks per [k][mn] row
     static_assert(!KC || CPR_K == 4 || CPR_K == 8, "k-major swizzle");
     static_assert(KC || CPR_M >= 16, "mn-major swizzle needs >= 16 chunks per row");
+    // XOR for row k of an [k][mn] tile: bf16 rows are read 4 at a time by the
+    // transposing reads (table above); fp32 rows are read by 32-bit reads in
+    // which the two half-waves take rows 4 apart, so rows with bit 2 of k set
+    // move to the other 128-byte half of each 256-byte window.
+    __device__ static __forceinline__ int mswz(int k)
+    {
+        if constexpr (Cfg::ES == 2) return mn_swz(k);
+        else return ((k >> 2) & 1) << 3;
+    }
     // byte offset of 16-byte chunk `chunk` in LDS row `row`
     __device__ static __forceinline__ int off(int row, int chunk)
     {
         if constexpr (KC)
             return row * (CPR_K * 16) + ((chunk ^ swz<CPR_K>(row)) << 4);
         else
-            return row * (CPR_M * 16) + ((chunk ^ mn_swz(row)) << 4);
+            return row * (CPR_M * 16) + ((chunk ^ mswz(row)) << 4);
     }
     static constexpr int ROWS = KC ? R : BK;        // LDS rows
     static constexpr int CPR = KC ? CPR_K : CPR_M;  // chunks per LDS row
@@ -100,7 +112,9 @@ struct Layout {
 template <class Cfg, int R, bool KC, bool ALIGNED>
 struct DmaOperand {
     using L = Layout<Cfg, R, KC>;
-    static constexpr int ND = (R * Cfg::BK * 2) / (1024 * Cfg::WAVES);  // DMA instructions per wave
+    using T = typename Cfg::T;
+    static constexpr int VEC = Cfg::VEC;
+    static constexpr int ND = (R * Cfg::BK * Cfg::ES) / (1024 * Cfg::WAVES);  // DMA instructions per wave
     static constexpr int CHUNKS = L::ROWS * L::CPR;
     static constexpr int GL = (CHUNKS + Cfg::THREADS - 1) / Cfg::THREADS;  // guarded loads per thread
 
@@ -110,7 +124,7 @@ struct DmaOperand {
     // row `row`: row = mn and chunks along k (KC), or row = k and chunks along mn.
     __device__ static __forceinline__ int64_t chunk_src(int row, int c, int64_t ld)
     {
-        return (int64_t)row * ld + c * 8;
+        return (int64_t)row * ld + c * VEC;
     }
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
@@ -123,17 +137,18 @@ struct DmaOperand {
             // invert the swizzle: which logical chunk lives at physical chunk pc
             int c;
             if constexpr (KC) c = pc ^ swz<L::CPR_K>(row);
-            else c = pc ^ mn_swz(row);
+            else c = pc ^ L::mswz(row);
             goff[d] = chunk_src(row, c, ld);
         }
     }
 
     // Asynchronous copy of the step at k0 into `lds` (tile base in LDS).  Issued
-    // through inline asm: the kernel orders these copies itself with explicit
+    // through inline asm (the LDS destination goes in as an m0 operand, so the
+    // compiler sets m0 itself): the kernel orders these copies itself with explicit
     // s_waitcnt vmcnt + s_barrier, so the compiler's own (conservative) LDS-DMA
     // tracking does not add waits; any wait it inserts for its own loads can
     // only become stronger because of these extra outstanding operations.
-    __device__ __forceinline__ void dma(const bf16_t* panel, int64_t ld, int k0, char* lds,
+    __device__ __forceinline__ void dma(const T* panel, int64_t ld, int k0, char* lds,
                                         int wave) const
     {
         const int64_t kstep = KC ? (int64_t)k0 : (int64_t)k0 * ld;
@@ -141,31 +156,31 @@ struct DmaOperand {
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-            const bf16_t* src = panel + kstep + goff[d];
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+            const T* src = panel + kstep + goff[d];
+            asm volatile("global_load_lds_dwordx4 %1, off"
                          :
-                         : "s"(lds_base + d * 1024), "v"(src)
-                         : "memory", "m0");
+                         : "{m0}"(lds_base + d * 1024), "v"(src)
+                         : "memory");
         }
     }
 
     // The d-th DMA copy instruction of dma() on its own (for interleaving).
-    __device__ __forceinline__ void dma_one(int d, const bf16_t* panel, int64_t ld, int k0,
+    __device__ __forceinline__ void dma_one(int d, const T* panel, int64_t ld, int k0,
                                             char* lds, int wave) const
     {
         const int64_t kstep = KC ? (int64_t)k0 : (int64_t)k0 * ld;
         const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
-        const bf16_t* src = panel + kstep + goff[d];
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+        const T* src = panel + kstep + goff[d];
+        asm volatile("global_load_lds_dwordx4 %1, off"
                      :
-                     : "s"(lds_base + d * 1024), "v"(src)
-                     : "memory", "m0");
+                     : "{m0}"(lds_base + d * 1024), "v"(src)
+                     : "memory");
     }
 
     // Register-staged copy with zero fill outside [0, rlim) x [0, K).
-    __device__ __forceinline__ void guarded(const bf16_t* panel, int64_t ld, int rlim, int k0,
-                                            int K, char* lds, int tid) const
+    __device__ __forceinline__ void guarded(const T* panel, int64_t ld, int rlim, int k0, int K,
+                                            char* lds, int tid) const
     {
         u32x4 v[GL];
 #pragma unroll
@@ -173,27 +188,27 @@ struct DmaOperand {
             const int q = tid + i * Cfg::THREADS;
             if (CHUNKS % Cfg::THREADS != 0 && q >= CHUNKS) break;
             const int row = q / L::CPR, c = q % L::CPR;
-            bf16_t e[8];
+            T e[VEC];
             if constexpr (KC) {   // row = mn, elements along k
-                const int k = k0 + c * 8;
-                const bf16_t* src = panel + (int64_t)row * ld + k;
-                if (ALIGNED && row < rlim && k + 8 <= K) {
+                const int k = k0 + c * VEC;
+                const T* src = panel + (int64_t)row * ld + k;
+                if (ALIGNED && row < rlim && k + VEC <= K) {
                     v[i] = *reinterpret_cast<const u32x4*>(src);
                     continue;
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) e[j] = (row < rlim && k + j < K) ? src[j] : bf16_t(0);
+                for (int j = 0; j < VEC; ++j) e[j] = (row < rlim && k + j < K) ? src[j] : T(0);
             } else {              // row = k, elements along mn
-                const int k = k0 + row, mn = c * 8;
-                const bf16_t* src = panel + (int64_t)k * ld + mn;
-                if (ALIGNED && k < K && mn + 8 <= rlim) {
+                const int k = k0 + row, mn = c * VEC;
+                const T* src = panel + (int64_t)k * ld + mn;
+                if (ALIGNED && k < K && mn + VEC <= rlim) {
                     v[i] = *reinterpret_cast<const u32x4*>(src);
                     continue;
                 }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) e[j] = (k < K && mn + j < rlim) ? src[j] : bf16_t(0);
+                for (int j = 0; j < VEC; ++j) e[j] = (k < K && mn + j < rlim) ? src[j] : T(0);
             }
-            v[i] = pack_chunk<bf16_t>(e);
+            v[i] = pack_chunk<T>(e);
         }
 #pragma unroll
         for (int i = 0; i < GL; ++i) {
@@ -201,6 +216,17 @@ struct DmaOperand {
             if (CHUNKS % Cfg::THREADS != 0 && q >= CHUNKS) break;
             *reinterpret_cast<u32x4*>(lds + L::off(q / L::CPR, q % L::CPR)) = v[i];
         }
+    }
+
+    // fp32 [k][mn] fragment piece e: one 32-bit read of k-slot e.  Lanes below
+    // 32 take k0+e and lanes from 32 take k0+4+e, matching the k-major
+    // operand's 16-byte read (4 consecutive k per half-wave).
+    __device__ static __forceinline__ uint32_t frag_f32_piece(const char* lds, int mn0, int ks,
+                                                             int lane, int e)
+    {
+        const int mn = mn0 + (lane & 31);
+        const int k = ks * Cfg::KSTEP + 4 * (lane >> 5) + e;
+        return *reinterpret_cast<const uint32_t*>(lds + L::off(k, mn / VEC) + (mn % VEC) * 4);
     }
 
     // Half h (k-slots 4h..4h+3) of an mn-major fragment via one transposing read.
@@ -231,6 +257,9 @@ struct DmaOperand {
             const int row = mn0 + lane % FM;
             const int chunk = ks * Cfg::KG + lane / FM;
             return *reinterpret_cast<const u32x4*>(lds + L::off(row, chunk));
+        } else if constexpr (Cfg::ES == 4) {
+            return u32x4{frag_f32_piece(lds, mn0, ks, lane, 0), frag_f32_piece(lds, mn0, ks, lane, 1),
+                         frag_f32_piece(lds, mn0, ks, lane, 2), frag_f32_piece(lds, mn0, ks, lane, 3)};
         } else {
             const uint64_t lo = frag_tr_half(lds, mn0, ks, lane, 0);
             const uint64_t hi = frag_tr_half(lds, mn0, ks, lane, 1);
@@ -240,7 +269,7 @@ struct DmaOperand {
 
     // The n-th of the NREAD memory instructions that read one fragment set
     // piece by piece (KC: one 16-byte read per fragment; MN: two halves).
-    static constexpr int NREAD_PER_FRAG = KC ? 1 : 2;
+    static constexpr int NREAD_PER_FRAG = KC ? 1 : (Cfg::ES == 2 ? 2 : 4);
 };
 
 // s_waitcnt vmcnt(n) only (expcnt and lgkmcnt fields at their maxima).
@@ -287,10 +316,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     const int m0 = tm * BM, n0 = tn * BN;
     const int rlim_a = p.M - m0, rlim_b = p.N - n0;
     const bool edge = rlim_a < BM || rlim_b < BN;
-    const bf16_t* A = static_cast<const bf16_t*>(p.A);
-    const bf16_t* B = static_cast<const bf16_t*>(p.B);
-    const bf16_t* panel_a = A_KC ? A + (int64_t)m0 * p.lda : A + m0;
-    const bf16_t* panel_b = B_KC ? B + (int64_t)n0 * p.ldb : B + n0;
+    using T = typename Cfg::T;
+    const T* A = static_cast<const T*>(p.A);
+    const T* B = static_cast<const T*>(p.B);
+    const T* panel_a = A_KC ? A + (int64_t)m0 * p.lda : A + m0;
+    const T* panel_b = B_KC ? B + (int64_t)n0 * p.ldb : B + n0;
 
     OpA oa;
     OpB ob;
@@ -382,6 +412,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
             const int i = n / RA;
             if constexpr (RA == 1) {
                 fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
+            } else if constexpr (RA == 4) {
+                fa[buf][i][n % RA] = OpA::frag_f32_piece(base, wave_m0 + i * FM, ks, lane, n % RA);
             } else {
                 const uint64_t v = OpA::frag_tr_half(base, wave_m0 + i * FM, ks, lane, n % RA);
                 fa[buf][i][2 * (n % RA)] = (uint32_t)v;
@@ -392,6 +424,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
             const char* bb = base + Cfg::A_BYTES;
             if constexpr (RB == 1) {
                 fb[buf][j] = OpB::frag(bb, wave_n0 + j * FM, ks, lane);
+            } else if constexpr (RB == 4) {
+                fb[buf][j][m % RB] = OpB::frag_f32_piece(bb, wave_n0 + j * FM, ks, lane, m % RB);
             } else {
                 const uint64_t v = OpB::frag_tr_half(bb, wave_n0 + j * FM, ks, lane, m % RB);
                 fb[buf][j][2 * (m % RB)] = (uint32_t)v;

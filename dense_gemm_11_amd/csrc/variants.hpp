@@ -34,6 +34,7 @@ const Variant* bf16_variant_table(int* count);
 const Variant* f32mfma_variant_table(int* count);
 const Variant* f32fma_variant_table(int* count);
 const Variant* bf16dma_variant_table(int* count);
+const Variant* f32dma_variant_table(int* count);
 
 }  // namespace dg
 
