@@ -64,7 +64,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -m dense_gemm_11_amd.build)")
+            "(python dense_gemm_11_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     runtimes = hip_runtimes_loaded()
     if len(runtimes) > 1:
