@@ -61,10 +61,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // (the tile's input intensity grows with BM*BN/(BM+BN), "GEMM on NVIDIA
 // GPUs", section 3) but fewer workgroups; small problems take the smaller
 // tile so that enough of the 256 compute units get work (section 5 on
-// tails and small shapes).  Operands whose rows are 16-byte aligned use the
-// direct-to-LDS kernels; misaligned ones (element loads on every step) use
-// the register-staged kernels, which measured faster on that path.
-int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool aligned)
+// tails and small shapes).  The direct-to-LDS kernels take every call whose
+// operands are element-aligned and whose per-lane buffer offsets fit in 31
+// bits; the register-staged kernels take the rest.
+int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
 {
     static const int bf16_dma_big = find_variant("bf16_dma32x32x16_256x256x32_w2x2_s4");
     static const int bf16_dma_mid = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4");
@@ -77,14 +77,31 @@ int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool aligned)
     const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
     const bool big = big_tiles >= 96;
     if (dtype == GEMM_DTYPE_BF16_F32) {
-        if (aligned) return big ? bf16_dma_big : bf16_dma_mid;
+        if (dma) return big ? bf16_dma_big : bf16_dma_mid;
         return big ? bf16_big : bf16_mid;
     }
-    if (aligned) return big ? f32_dma_big : f32_dma_mid;
+    if (dma) return big ? f32_dma_big : f32_dma_mid;
     return big ? f32_big : f32_mid;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, int64_t bytes)
+{
+    return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)bytes) == 0;
+}
+
+// The direct-to-LDS kernels address a workgroup's operand panel with 32-bit
+// byte offsets from the panel start: a k-contiguous panel spans (rows-1) rows
+// of ld plus K elements (plus one step of overhang), an mn-contiguous one K-1
+// rows of ld plus its width.  Both must stay below 2^32.
+bool dma_offsets_fit(const Variant& v, bool a_kc, bool b_kc, int64_t K, int64_t lda,
+                     int64_t ldb, int64_t es)
+{
+    const int64_t kk = K + v.bk;
+    const int64_t span_a = a_kc ? (v.bm - 1) * lda + kk : kk * lda + v.bm;
+    const int64_t span_b = b_kc ? (v.bn - 1) * ldb + kk : kk * ldb + v.bn;
+    const int64_t lim = ((int64_t)1 << 32) - 64;
+    return span_a * es < lim && span_b * es < lim;
+}
 
 bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes)
 {
@@ -215,8 +232,10 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     a.K = (int)K;
     a.alpha = alpha;
     a.beta = beta;
-    a.c_vec = beta != 0.0f && aligned16(C) && (ldc % 4) == 0;
-    a.d_vec = aligned16(D) && (ldd % 4) == 0;
+    // 16-byte accesses need only element alignment: the memory system serves
+    // unaligned vector loads and stores whole
+    a.c_vec = beta != 0.0f && aligned_to(C, 4);
+    a.d_vec = aligned_to(D, 4);
 
     if (!reads_ab) {
         const int64_t blocks = std::min<int64_t>(ceil_div(M * N, 256), 65536);
@@ -227,10 +246,20 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     }
 
     const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
-    const bool aligned = aligned16(A) && aligned16(B) && (lda * es) % 16 == 0 && (ldb * es) % 16 == 0;
-    int id = h->forced_variant >= 0 ? h->forced_variant : select_variant(dtype, M, N, K, aligned);
+    const bool a_kc = transA == GEMM_OP_N, b_kc = transB == GEMM_OP_T;
+    // wide (16-byte) operand access needs element-aligned A and B only
+    const bool wide = aligned_to(A, es) && aligned_to(B, es);
+    int id = h->forced_variant;
+    if (id < 0) {
+        const Variant& big = table()[select_variant(dtype, M, N, K, true)];
+        id = select_variant(dtype, M, N, K, wide && dma_offsets_fit(big, a_kc, b_kc, K, lda, ldb, es));
+    }
     const Variant& v = table()[id];
     if (v.dtype != (int)dtype) return GEMM_ERR_NOT_SUPPORTED;
+    // a direct-to-LDS kernel whose offsets would overflow stages every step
+    // through registers instead (its ALIGNED == false instantiation)
+    const bool aligned =
+        wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, a_kc, b_kc, K, lda, ldb, es));
     a.tiles_m = (int)ceil_div(M, v.bm);
     a.tiles_n = (int)ceil_div(N, v.bn);
     // 4 tile-rows per group measured best on 8192^3 bf16 (groups of 1, 2, 3, 4, 6,
@@ -238,7 +267,7 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     a.group_m = std::min(a.tiles_m, 4);
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
-    LaunchFn fn = v.fn[aligned][transA == GEMM_OP_N][transB == GEMM_OP_T];
+    LaunchFn fn = v.fn[aligned][a_kc][b_kc];
     const hipError_t e = fn(a, (int)grid, stream);
     if (e != hipSuccess) return GEMM_ERR_HIP;
     h->last_variant = id;

@@ -11,7 +11,7 @@ using Dma256s5 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 5>;
 
 
 #define BF16_DMA_VARIANT(NAME, CFG) \
-    {NAME, 1, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
+    {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
 
 const Variant* bf16dma_variant_table(int* count)
 {

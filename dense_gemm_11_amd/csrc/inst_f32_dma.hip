@@ -8,7 +8,7 @@ using F32Dma256s4 = DmaConfig<MFMA_F32_32x32x2, 256, 256, 16, 2, 2, 4>;
 using F32Dma128s4 = DmaConfig<MFMA_F32_32x32x2, 128, 128, 16, 2, 2, 4>;
 
 #define F32_DMA_VARIANT(NAME, CFG) \
-    {NAME, 0, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
+    {NAME, 0, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
 
 const Variant* f32dma_variant_table(int* count)
 {

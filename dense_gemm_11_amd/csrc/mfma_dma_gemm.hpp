@@ -6,11 +6,15 @@
 // overlap of its "load-compute overlap" part made deeper:
 //
 //  * Each operand tile of a K-step goes from global memory straight into LDS
-//    with global_load_lds_dwordx4 (lane l of a wave writes its 16 bytes at the
-//    instruction's LDS base + 16*l), so no registers hold tiles in flight and
-//    no VALU or LDS-write instructions are spent on staging.  Which global
+//    with buffer_load_dwordx4 ... lds (lane l of a wave writes its 16 bytes at
+//    the instruction's LDS base + 16*l), so no registers hold tiles in flight
+//    and no VALU or LDS-write instructions are spent on staging.  Which global
 //    16-byte chunk a lane fetches is chosen so the LDS image comes out in the
-//    swizzled layout below.
+//    swizzled layout below.  One buffer resource per operand starts at the
+//    workgroup's panel and ends where the stored matrix ends: a lane's offset
+//    is its fixed in-step offset plus the step's, and reads past the matrix
+//    return zero.  Addresses need only element alignment (16-byte loads at 2-
+//    or 4-byte aligned addresses are served whole by the memory system).
 //  * Operands keep their memory orientation in LDS.  A k-contiguous operand
 //    (A with transA == N, B with transB == T) is stored [mn][k] in 16-byte
 //    chunks with the chunk index XOR-swizzled by row, and its MFMA fragments
@@ -30,9 +34,10 @@
 //  * MFMA operands are swapped (B fragment first), so each lane's
 //    accumulators hold 4 adjacent output columns of one row: the epilogue
 //    writes 16-byte vectors.
-//  * Edge tiles, the ragged last K-step and misaligned operands take a
+//  * The ragged last K-step and the last step of edge tiles take a
 //    register-staged path with per-element zero fill that writes the same
-//    LDS layout (ds_write_b128).
+//    LDS layout (ds_write_b128); so does every step when the host finds a
+//    panel whose byte offsets would not fit in 32 bits (ALIGNED == false).
 #pragma once
 
 #include <type_traits>
@@ -97,17 +102,41 @@ struct Layout {
         if constexpr (Cfg::ES == 2) return mn_swz(k);
         else return ((k >> 2) & 1) << 3;
     }
+    // XOR for row mn of an [mn][k] tile.  A fragment read covers 32 (or 16)
+    // consecutive rows at one or two chunks.  With 8 chunks per row the rows
+    // swizzled by (r ^ r>>3) already spread every 16 lanes over all banks.
+    // With 4 chunks per row (64-byte rows) measured bank-conflict counts on
+    // gfx950 are zero for (r ^ r>>2) & 3 but four cycles per ds_read_b128 for
+    // any swizzle that mixes in row bit 3, such as ((r>>1) ^ (r>>3)) & 3.
+    __device__ static __forceinline__ int kswz(int r)
+    {
+        if constexpr (CPR_K == 4) return (r ^ (r >> 2)) & 3;
+        else return swz<CPR_K>(r);
+    }
     // byte offset of 16-byte chunk `chunk` in LDS row `row`
     __device__ static __forceinline__ int off(int row, int chunk)
     {
         if constexpr (KC)
-            return row * (CPR_K * 16) + ((chunk ^ swz<CPR_K>(row)) << 4);
+            return row * (CPR_K * 16) + ((chunk ^ kswz(row)) << 4);
         else
             return row * (CPR_M * 16) + ((chunk ^ mswz(row)) << 4);
     }
     static constexpr int ROWS = KC ? R : BK;        // LDS rows
     static constexpr int CPR = KC ? CPR_K : CPR_M;  // chunks per LDS row
 };
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (stride 0) over the bytes [base, base + nrec).  A 16-byte
+// load through it returns zero for every 4-byte word that does not lie wholly
+// below nrec, and touches no memory for it.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t nrec)
+{
+    const uint64_t a = reinterpret_cast<uintptr_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+                 __builtin_amdgcn_readfirstlane((int)nrec), 0x00020000};
+}
 
 template <class Cfg, int R, bool KC, bool ALIGNED>
 struct DmaOperand {
@@ -118,14 +147,10 @@ struct DmaOperand {
     static constexpr int CHUNKS = L::ROWS * L::CPR;
     static constexpr int GL = (CHUNKS + Cfg::THREADS - 1) / Cfg::THREADS;  // guarded loads per thread
 
-    int64_t goff[ND];  // per-lane element offsets of this lane's DMA chunks (k0 = 0)
-
-    // Element offset (from the panel start, k0 = 0) of logical chunk c of LDS
-    // row `row`: row = mn and chunks along k (KC), or row = k and chunks along mn.
-    __device__ static __forceinline__ int64_t chunk_src(int row, int c, int64_t ld)
-    {
-        return (int64_t)row * ld + c * VEC;
-    }
+    // Per-lane byte offsets of this lane's DMA chunks from the start of a step
+    // (row = mn and chunks along k for KC, row = k and chunks along mn
+    // otherwise).  The host keeps every offset within the panel below 2^32.
+    uint32_t voff[ND];
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
     {
@@ -136,46 +161,49 @@ struct DmaOperand {
             const int pc = (pos % (L::CPR * 16)) >> 4;
             // invert the swizzle: which logical chunk lives at physical chunk pc
             int c;
-            if constexpr (KC) c = pc ^ swz<L::CPR_K>(row);
+            if constexpr (KC) c = pc ^ L::kswz(row);
             else c = pc ^ L::mswz(row);
-            goff[d] = chunk_src(row, c, ld);
+            voff[d] = (uint32_t)(((int64_t)row * ld + c * VEC) * Cfg::ES);
         }
     }
 
-    // Asynchronous copy of the step at k0 into `lds` (tile base in LDS).  Issued
-    // through inline asm (the LDS destination goes in as an m0 operand, so the
-    // compiler sets m0 itself): the kernel orders these copies itself with explicit
-    // s_waitcnt vmcnt + s_barrier, so the compiler's own (conservative) LDS-DMA
-    // tracking does not add waits; any wait it inserts for its own loads can
-    // only become stronger because of these extra outstanding operations.
-    __device__ __forceinline__ void dma(const T* panel, int64_t ld, int k0, char* lds,
-                                        int wave) const
+    // Buffer resource of the panel: based at the panel start, with its range
+    // ending where the stored matrix ends (`end`), so chunks of rows past the
+    // matrix read as zero instead of touching memory.
+    __device__ static __forceinline__ i32x4 panel_rsrc(const T* panel, const char* end)
     {
-        const int64_t kstep = KC ? (int64_t)k0 : (int64_t)k0 * ld;
-        const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-            const T* src = panel + kstep + goff[d];
-            asm volatile("global_load_lds_dwordx4 %1, off"
-                         :
-                         : "{m0}"(lds_base + d * 1024), "v"(src)
-                         : "memory");
-        }
+        const int64_t left = end - reinterpret_cast<const char*>(panel);
+        return buffer_rsrc(panel, left > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)left);
     }
 
-    // The d-th DMA copy instruction of dma() on its own (for interleaving).
-    __device__ __forceinline__ void dma_one(int d, const T* panel, int64_t ld, int k0,
-                                            char* lds, int wave) const
+    // Byte offset of the step at k0 from the panel start.
+    __device__ static __forceinline__ uint32_t step_bytes(int k0, int64_t ld)
     {
-        const int64_t kstep = KC ? (int64_t)k0 : (int64_t)k0 * ld;
+        return (uint32_t)((KC ? (int64_t)k0 : (int64_t)k0 * ld) * Cfg::ES);
+    }
+
+    // The d-th DMA copy of a step: 16 bytes per lane from the buffer into LDS at
+    // the instruction's base + 16 * lane.  Issued through inline asm (the LDS
+    // destination goes in as an m0 operand, so the compiler sets m0 itself): the
+    // kernel orders these copies itself with explicit s_waitcnt vmcnt + s_barrier,
+    // so the compiler's own (conservative) LDS-DMA tracking adds no waits; any
+    // wait it inserts for its own loads can only become stronger because of these
+    // extra outstanding operations.
+    __device__ __forceinline__ void dma_one(int d, i32x4 rsrc, uint32_t kbytes, char* lds,
+                                            int wave) const
+    {
         const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
-        const T* src = panel + kstep + goff[d];
-        asm volatile("global_load_lds_dwordx4 %1, off"
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                      :
-                     : "{m0}"(lds_base + d * 1024), "v"(src)
+                     : "v"(voff[d] + kbytes), "s"(rsrc), "{m0}"(lds_base + d * 1024)
                      : "memory");
+    }
+
+    __device__ __forceinline__ void dma(i32x4 rsrc, uint32_t kbytes, char* lds, int wave) const
+    {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dma_one(d, rsrc, kbytes, lds, wave);
     }
 
     // Register-staged copy with zero fill outside [0, rlim) x [0, K).
@@ -326,17 +354,29 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     OpB ob;
     oa.init(wave, lane, p.lda);
     ob.init(wave, lane, p.ldb);
+    // end of each stored matrix: A is M x K (k-contiguous) or K x M, B likewise
+    const char* end_a = reinterpret_cast<const char*>(
+        A + (A_KC ? (int64_t)(p.M - 1) * p.lda + p.K : (int64_t)(p.K - 1) * p.lda + p.M));
+    const char* end_b = reinterpret_cast<const char*>(
+        B + (B_KC ? (int64_t)(p.N - 1) * p.ldb + p.K : (int64_t)(p.K - 1) * p.ldb + p.N));
+    const i32x4 rsrc_a = OpA::panel_rsrc(panel_a, end_a);
+    const i32x4 rsrc_b = OpB::panel_rsrc(panel_b, end_b);
 
     const int nk = (p.K + BK - 1) / BK;
     const bool k_ragged = (p.K % BK) != 0;
-    // steps that can be copied by DMA: whole step in range and aligned
-    const int nk_dma = (ALIGNED && !edge) ? (k_ragged ? nk - 1 : nk) : 0;
+    // Steps copied by DMA.  Rows past the matrix read as zero through the
+    // buffer range and chunks that run past a row's end only feed outputs the
+    // epilogue masks, so edge tiles use DMA too, except on their last step: a
+    // chunk that straddles the end of the matrix would lose its last valid
+    // bf16 element to the word-granular range check.  A ragged last step needs
+    // exact zeros past K and is always register-staged.
+    const int nk_dma = ALIGNED ? ((k_ragged || edge) ? nk - 1 : nk) : 0;
 
     auto load = [&](int kt, char* base) {
         const int k0 = kt * BK;
         if (kt < nk_dma) {
-            oa.dma(panel_a, p.lda, k0, base, wave);
-            ob.dma(panel_b, p.ldb, k0, base + Cfg::A_BYTES, wave);
+            oa.dma(rsrc_a, OpA::step_bytes(k0, p.lda), base, wave);
+            ob.dma(rsrc_b, OpB::step_bytes(k0, p.ldb), base + Cfg::A_BYTES, wave);
         } else {
             oa.guarded(panel_a, p.lda, rlim_a, k0, p.K, base, tid);
             ob.guarded(panel_b, p.ldb, rlim_b, k0, p.K, base + Cfg::A_BYTES, tid);
@@ -384,8 +424,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                 else wait_vm_lgkm0<0>();
                 barrier_only();
                 if (STEADY) {
-                    oa.dma(panel_a, p.lda, (kt + S - 1) * BK, stage(FAR), wave);
-                    ob.dma(panel_b, p.ldb, (kt + S - 1) * BK, stage(FAR) + Cfg::A_BYTES, wave);
+                    const int kf = (kt + S - 1) * BK;
+                    oa.dma(rsrc_a, OpA::step_bytes(kf, p.lda), stage(FAR), wave);
+                    ob.dma(rsrc_b, OpB::step_bytes(kf, p.ldb), stage(FAR) + Cfg::A_BYTES, wave);
                 } else if (kt + S - 1 < nk) {
                     load(kt + S - 1, stage(FAR));
                 }
@@ -439,6 +480,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         constexpr int FAR = (CUR + S - 1) % S;
         const char* base = stage(CUR);
         const int kfar = (kt + S - 1) * BK;
+        const uint32_t ka = OpA::step_bytes(kfar, p.lda), kb = OpB::step_bytes(kfar, p.ldb);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int cb = ks & 1;
@@ -466,10 +508,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                 for (int o = lo; o < hi; ++o) {
                     if (o < NREAD) read_op(o, rbase, rks, cb ^ 1);
                     else if (o - NREAD < OpA::ND)
-                        oa.dma_one(o - NREAD, panel_a, p.lda, kfar, stage(FAR), wave);
+                        oa.dma_one(o - NREAD, rsrc_a, ka, stage(FAR), wave);
                     else
-                        ob.dma_one(o - NREAD - OpA::ND, panel_b, p.ldb, kfar,
-                                   stage(FAR) + Cfg::A_BYTES, wave);
+                        ob.dma_one(o - NREAD - OpA::ND, rsrc_b, kb, stage(FAR) + Cfg::A_BYTES, wave);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }

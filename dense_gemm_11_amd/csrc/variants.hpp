@@ -8,14 +8,14 @@ namespace dg {
 
 typedef hipError_t (*LaunchFn)(const GemmArgs&, int grid, hipStream_t);
 
-enum VariantKind { KIND_VECTOR_FMA = 0, KIND_MFMA = 1 };
+enum VariantKind { KIND_VECTOR_FMA = 0, KIND_MFMA = 1, KIND_MFMA_DMA = 2 };
 
 struct Variant {
     const char* name;
     int dtype;   // 0 = fp32 operands, 1 = bf16 operands
     int kind;    // VariantKind
     int bm, bn, bk, threads, lds_bytes;
-    LaunchFn fn[2][2][2];  // [operands 16-byte aligned][A k-contiguous][B k-contiguous]
+    LaunchFn fn[2][2][2];  // [wide access][A k-contiguous][B k-contiguous]
 };
 
 // Launch through hipLaunchKernel so the launch status is returned directly.
