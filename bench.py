@@ -72,8 +72,10 @@ def kernel_name_key(variant_name: str, tile) -> str:
         if f"_{tag}_" in variant_name:
             return f"MfmaConfig<{kind}, {bm}, {bn}, {bk},"
         if f"_dma{tag[4:]}_" in variant_name:
-            stages = variant_name.rsplit("_s", 1)[1]
-            return f"DmaConfig<{kind}, {bm}, {bn}, {bk}, 2, 2, {stages}>"
+            late = variant_name.endswith("_late")
+            stages = variant_name.removesuffix("_late").rsplit("_s", 1)[1]
+            return (f"DmaConfig<{kind}, {bm}, {bn}, {bk}, 2, 2, {stages}, "
+                    f"{'true' if late else 'false'}>")
     return f"FmaConfig<{bm}, {bn}, {bk}>"
 
 
@@ -200,6 +202,18 @@ def oracle_sample_rate(part: Part, cores: int, budget_s: float):
     return {"outputs": n, "seconds": t, "tflops": 2.0 * w.K * n / t / 1e12}
 
 
+PMC_COMMANDS = {
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch --output-format csv "
+             "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras "
+             "--copy-probe 512",
+    "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write --output-format csv "
+             "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras "
+             "--copy-probe 512",
+    "ingest": "python bench.py --ingest-pmc gpurun_out/pmc_fetch/fetch_counter_collection.csv "
+              "gpurun_out/pmc_write/write_counter_collection.csv > profiles/hbm_traffic.json",
+}
+
+
 def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
     the copy kernel's reading against its known byte count."""
@@ -228,7 +242,9 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
     w_scale = copy_bytes / (write.get(ck, fetch[ck]) * 1024.0)
     rec = {"kernel_src_digest": kernel_source_digest(), "copy_kernel": ck,
            "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
-           "kernels": {}}
+           "kernels": {}, "commands": PMC_COMMANDS,
+           "note": ("FETCH_SIZE/WRITE_SIZE are KiB per dispatch; each is scaled by "
+                    "bytes/(counter*1024) of a 512 MiB device copy recorded in the same run.")}
     for k in fetch:
         m = re.search(r"gemm_kernel<", k)
         if not m:

@@ -7,8 +7,9 @@ namespace dg {
 using Dma256s4 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4>;
 using Dma256s3 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3>;
 using Dma128s4 = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4>;
-using Dma256s5 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 5>;
-
+using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
+using Dma256s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true>;
+using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
 
 #define BF16_DMA_VARIANT(NAME, CFG) \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
@@ -19,8 +20,9 @@ const Variant* bf16dma_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4", Dma256s4),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3", Dma256s3),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4", Dma128s4),
-        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s5", Dma256s5),
-
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3_late", Dma256s3L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late", Dma256s4L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late", Dma128s3L),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -25,12 +25,15 @@
 //    group, lane r+4j supplies the address of (k0+j, mn0+4r..4r+3) and lane
 //    4r+e receives element e of lanes r, r+4, r+8, r+12, i.e. four
 //    consecutive k of column mn0+4r+e — exactly an MFMA operand slice.
-//  * S >= 3 stages in separate __shared__ arrays (static indices keep the
-//    compiler's LDS-DMA dependency tracking exact).  One barrier per stage,
-//    placed half way through the stage's MFMAs: before it each wave waits
-//    until the next stage's DMA has landed; after it the DMA for the stage
-//    S-1 ahead is issued (into the buffer every wave has finished reading)
-//    and the next stage's first fragments are read while the MFMAs run.
+//  * S stages in separate __shared__ arrays (static indices keep the
+//    compiler's LDS-DMA dependency tracking exact).  One barrier per stage:
+//    before it each wave waits until the next stage's DMA has landed; after
+//    it the DMA for a later step is issued into a buffer every wave has
+//    finished reading, and the next stage's first fragments are read while
+//    the MFMAs run.  The barrier sits either half way through the stage's
+//    MFMAs (copying S-1 steps ahead into the previous step's buffer, S >= 3)
+//    or before its last fragment step (copying S steps ahead into the
+//    current buffer once this wave's reads of it are done, S >= 2).
 //  * MFMA operands are swapped (B fragment first), so each lane's
 //    accumulators hold 4 adjacent output columns of one row: the epilogue
 //    writes 16-byte vectors.
@@ -47,9 +50,17 @@
 
 namespace dg {
 
-template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_>
+// LATE_ selects where a step's barrier sits: false = half way through the
+// step's fragment steps, copying the step S-1 ahead into the stage read one
+// step earlier; true = before the step's last fragment step, once this wave's
+// reads of the step have completed, copying the step S ahead into the stage
+// just read.  The late barrier hides one more step of copy latency with the
+// same number of stages, so two stages suffice.
+template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_, bool LATE_ = false>
 struct DmaConfig {
     static constexpr int KIND = KIND_, BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_;
+    static constexpr bool LATE = LATE_;
+    static constexpr int AHEAD = LATE ? S : S - 1;  // steps between a copy and its use
     using T = typename MfmaShape<KIND>::T;
     static constexpr int ES = sizeof(T);
     static constexpr int VEC = 16 / ES;                // elements per 16-byte chunk
@@ -70,12 +81,12 @@ struct DmaConfig {
     static_assert(KIND == MFMA_BF16_32x32x16 || KIND == MFMA_BF16_16x16x32 ||
                       KIND == MFMA_F32_32x32x2,
                   "instruction kinds with a defined fragment mapping");
-    static_assert(S >= 3 && S <= 5, "stage count");
+    static_assert(S >= (LATE ? 2 : 3) && S <= 5, "stage count");
     static_assert(NKS >= 2 && NKS % 2 == 0, "barrier sits between fragment steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "DMA split");
     static_assert(BM % (WM * FM) == 0 && BN % (WN * FM) == 0, "wave tile");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
-    static_assert(DMA_PER_STAGE * (S - 2) < 64, "vmcnt range");
+    static_assert(DMA_PER_STAGE * (AHEAD - 1) < 64, "vmcnt range");
 };
 
 // XOR applied to the 16-byte chunk index of row k of an [k][mn] tile: {0, 4,
@@ -210,39 +221,45 @@ struct DmaOperand {
     __device__ __forceinline__ void guarded(const T* panel, int64_t ld, int rlim, int k0, int K,
                                             char* lds, int tid) const
     {
-        u32x4 v[GL];
+        // in batches of GB chunks per thread, which bounds the registers this
+        // path adds on top of the accumulators and fragments
+        constexpr int GB = GL < 4 ? GL : 4;
 #pragma unroll
-        for (int i = 0; i < GL; ++i) {
-            const int q = tid + i * Cfg::THREADS;
-            if (CHUNKS % Cfg::THREADS != 0 && q >= CHUNKS) break;
-            const int row = q / L::CPR, c = q % L::CPR;
-            T e[VEC];
-            if constexpr (KC) {   // row = mn, elements along k
-                const int k = k0 + c * VEC;
-                const T* src = panel + (int64_t)row * ld + k;
-                if (ALIGNED && row < rlim && k + VEC <= K) {
-                    v[i] = *reinterpret_cast<const u32x4*>(src);
-                    continue;
+        for (int i0 = 0; i0 < GL; i0 += GB) {
+            u32x4 v[GB];
+#pragma unroll
+            for (int b = 0; b < GB; ++b) {
+                const int q = tid + (i0 + b) * Cfg::THREADS;
+                if ((CHUNKS % Cfg::THREADS != 0 || GL % GB != 0) && (i0 + b >= GL || q >= CHUNKS)) break;
+                const int row = q / L::CPR, c = q % L::CPR;
+                T e[VEC];
+                if constexpr (KC) {   // row = mn, elements along k
+                    const int k = k0 + c * VEC;
+                    const T* src = panel + (int64_t)row * ld + k;
+                    if (ALIGNED && row < rlim && k + VEC <= K) {
+                        v[b] = *reinterpret_cast<const u32x4*>(src);
+                        continue;
+                    }
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) e[j] = (row < rlim && k + j < K) ? src[j] : T(0);
+                } else {              // row = k, elements along mn
+                    const int k = k0 + row, mn = c * VEC;
+                    const T* src = panel + (int64_t)k * ld + mn;
+                    if (ALIGNED && k < K && mn + VEC <= rlim) {
+                        v[b] = *reinterpret_cast<const u32x4*>(src);
+                        continue;
+                    }
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) e[j] = (k < K && mn + j < rlim) ? src[j] : T(0);
                 }
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) e[j] = (row < rlim && k + j < K) ? src[j] : T(0);
-            } else {              // row = k, elements along mn
-                const int k = k0 + row, mn = c * VEC;
-                const T* src = panel + (int64_t)k * ld + mn;
-                if (ALIGNED && k < K && mn + VEC <= rlim) {
-                    v[i] = *reinterpret_cast<const u32x4*>(src);
-                    continue;
-                }
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) e[j] = (k < K && mn + j < rlim) ? src[j] : T(0);
+                v[b] = pack_chunk<T>(e);
             }
-            v[i] = pack_chunk<T>(e);
-        }
 #pragma unroll
-        for (int i = 0; i < GL; ++i) {
-            const int q = tid + i * Cfg::THREADS;
-            if (CHUNKS % Cfg::THREADS != 0 && q >= CHUNKS) break;
-            *reinterpret_cast<u32x4*>(lds + L::off(q / L::CPR, q % L::CPR)) = v[i];
+            for (int b = 0; b < GB; ++b) {
+                const int q = tid + (i0 + b) * Cfg::THREADS;
+                if ((CHUNKS % Cfg::THREADS != 0 || GL % GB != 0) && (i0 + b >= GL || q >= CHUNKS)) break;
+                *reinterpret_cast<u32x4*>(lds + L::off(q / L::CPR, q % L::CPR)) = v[b];
+            }
         }
     }
 
@@ -389,11 +406,12 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = Acc{};
 
-    // prologue: steps 0 .. S-2 in flight, wait for step 0
+    // prologue: steps 0 .. AHEAD-1 in flight, wait for step 0
+    constexpr int AHEAD = Cfg::AHEAD;
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
+    for (int s = 0; s < AHEAD; ++s)
         if (s < nk) load(s, stage(s));
-    if (nk >= S - 1) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (S - 2)>();
+    if (nk >= AHEAD) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 1)>();
     else wait_vm_lgkm0<0>();
     barrier_only();
 
@@ -407,28 +425,35 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     };
     read_frags(stage(0), 0, 0);
 
+    // Fragment step of a K-step at which the barrier sits, and the stage the
+    // copy issued after it fills (relative to the current stage).
+    constexpr int BAR_KS = Cfg::LATE ? NKS - 1 : NKS / 2;
+    constexpr int FILL = Cfg::LATE ? 0 : S - 1;
+
     // One K-step held in LDS stage CUR (static, so every LDS address is a
     // compile-time offset from its own __shared__ array).  STEADY: the step
-    // S-1 ahead exists and is copied by DMA, so no run-time conditions.
+    // AHEAD ahead exists and is copied by DMA, so no run-time conditions.
     auto step = [&](auto cur_c, auto steady_c, int kt) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr bool STEADY = decltype(steady_c)::value;
         constexpr int NXT = (CUR + 1) % S;
-        constexpr int FAR = (CUR + S - 1) % S;
+        constexpr int FAR = (CUR + FILL) % S;
         const char* base = stage(CUR);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            if (ks == NKS / 2) {
+            if (ks == BAR_KS) {
                 // the next step must have landed in every wave's part of LDS
-                if (STEADY || kt + S - 1 <= nk) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (S - 3)>();
+                // (and, with the late barrier, this wave's reads of the stage
+                // about to be refilled must be complete: lgkmcnt(0))
+                if (STEADY || kt + AHEAD <= nk) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
                 else wait_vm_lgkm0<0>();
                 barrier_only();
                 if (STEADY) {
-                    const int kf = (kt + S - 1) * BK;
+                    const int kf = (kt + AHEAD) * BK;
                     oa.dma(rsrc_a, OpA::step_bytes(kf, p.lda), stage(FAR), wave);
                     ob.dma(rsrc_b, OpB::step_bytes(kf, p.ldb), stage(FAR) + Cfg::A_BYTES, wave);
-                } else if (kt + S - 1 < nk) {
-                    load(kt + S - 1, stage(FAR));
+                } else if (kt + AHEAD < nk) {
+                    load(kt + AHEAD, stage(FAR));
                 }
             }
             const int cb = ks & 1;
@@ -443,7 +468,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     // Steady-state step with a pinned instruction order: every MFMA of a
     // fragment step is followed by one or two memory instructions (the next
     // fragment set's LDS reads and, in the second half, the DMA copies of the
-    // step S-1 ahead), so the matrix core is fed while loads are in flight.
+    // step AHEAD ahead), so the matrix core is fed while loads are in flight.
     constexpr int RA = OpA::NREAD_PER_FRAG, RB = OpB::NREAD_PER_FRAG;
     constexpr int NREAD = MF * RA + NF * RB;
     constexpr int NMFMA = MF * NF;
@@ -477,16 +502,17 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     auto steady = [&](auto cur_c, int kt) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int NXT = (CUR + 1) % S;
-        constexpr int FAR = (CUR + S - 1) % S;
+        constexpr int FAR = (CUR + FILL) % S;
         const char* base = stage(CUR);
-        const int kfar = (kt + S - 1) * BK;
+        const int kfar = (kt + AHEAD) * BK;
         const uint32_t ka = OpA::step_bytes(kfar, p.lda), kb = OpB::step_bytes(kfar, p.ldb);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int cb = ks & 1;
-            const bool mid = ks == NKS / 2;
+            const bool mid = ks == BAR_KS;
             if (mid) {
-                wait_vm<Cfg::DMA_PER_STAGE * (S - 3)>();
+                if constexpr (Cfg::LATE) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
+                else wait_vm<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
                 barrier_only();
             }
             const char* rbase = ks + 1 < NKS ? base : stage(NXT);
@@ -526,11 +552,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     using I4 = std::integral_constant<int, 4>;
 
     int kt = 0;
-    // steady state: every step of the group issues a DMA copy S-1 steps ahead
-    for (; kt + 2 * S - 2 < nk_dma; kt += S) {
+    // steady state: every step of the group issues a DMA copy AHEAD steps ahead
+    for (; kt + S - 1 + AHEAD < nk_dma; kt += S) {
         steady(I0{}, kt);
         steady(I1{}, kt + 1);
-        steady(I2{}, kt + 2);
+        if constexpr (S > 2) steady(I2{}, kt + 2);
         if constexpr (S > 3) steady(I3{}, kt + 3);
         if constexpr (S > 4) steady(I4{}, kt + 4);
     }
@@ -538,7 +564,8 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     for (; kt < nk; kt += S) {
         step(I0{}, F_{}, kt);
         if (kt + 1 < nk) step(I1{}, F_{}, kt + 1);
-        if (kt + 2 < nk) step(I2{}, F_{}, kt + 2);
+        if constexpr (S > 2)
+            if (kt + 2 < nk) step(I2{}, F_{}, kt + 2);
         if constexpr (S > 3)
             if (kt + 3 < nk) step(I3{}, F_{}, kt + 3);
         if constexpr (S > 4)
