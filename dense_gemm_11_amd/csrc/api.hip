@@ -81,9 +81,10 @@ int device_cus()
 // on tails and small shapes).  The direct-to-LDS kernels take every call
 // whose operands are element-aligned and whose panel offsets fit in 32 bits;
 // the register-staged kernels take the rest.  The direct-to-LDS variants
-// chosen place their barrier before the last fragment step of a K-step
-// (three stages): measured 8-10 % faster than the half-way barrier with
-// four stages on bf16 8192^3 with k-contiguous A.
+// chosen place their barrier before the last fragment step of a K-step:
+// three 32-deep stages for bf16 (measured 8-10 % faster than the half-way
+// barrier with four stages on 8192^3 with k-contiguous A) and two 32-deep
+// stages for fp32 (1 % faster than three 16-deep ones on 4096^3).
 int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
 {
     static const int bf16_dma_big = find_variant("bf16_dma32x32x16_256x256x32_w2x2_s3_late");
@@ -92,7 +93,7 @@ int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
     static const int bf16_mid = find_variant("bf16_mfma16x16x32_128x128x64_w2x2");
     static const int f32_big = find_variant("f32_mfma32x32x2_256x256x32_w2x2");
     static const int f32_mid = find_variant("f32_mfma32x32x2_128x128x32_w2x2");
-    static const int f32_dma_big = find_variant("f32_dma32x32x2_256x256x16_w2x2_s3_late");
+    static const int f32_dma_big = find_variant("f32_dma32x32x2_256x256x32_w2x2_s2_late");
     static const int f32_dma_mid = find_variant("f32_dma32x32x2_128x128x16_w2x2_s3_late");
     const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
     const bool big = 4 * big_tiles >= 3 * (int64_t)device_cus();

@@ -11,6 +11,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace dg {
 
 typedef uint16_t bf16_t;  // bfloat16 operands are carried as raw 16-bit patterns
@@ -55,6 +58,20 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
     const int in_group = w - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1: every index is
+// a compile-time constant however large the body, so register arrays indexed
+// by it never fall back to private (scratch) memory.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <typename T>

@@ -10,6 +10,7 @@ using Dma128s4 = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4>;
 using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
 using Dma256s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true>;
 using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+using Dma256k64s2L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 2, 2, true>;
 
 #define BF16_DMA_VARIANT(NAME, CFG) \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
@@ -23,6 +24,7 @@ const Variant* bf16dma_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3_late", Dma256s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late", Dma256s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late", Dma128s3L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x2_s2_late", Dma256k64s2L),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -203,8 +203,12 @@ struct DmaOperand {
     __device__ __forceinline__ void dma_one(int d, i32x4 rsrc, uint32_t kbytes, char* lds,
                                             int wave) const
     {
-        const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+        uint32_t lds_base = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(lds) + wave * ND * 1024);
+        // Opaque to the optimizer, so each copy's m0 is one scalar add at its
+        // use: hoisted out of the loop, the per-copy values of every stage
+        // would each hold an SGPR and exhaust them.
+        asm volatile("" : "+s"(lds_base));
         asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                      :
                      : "v"(voff[d] + kbytes), "s"(rsrc), "{m0}"(lds_base + d * 1024)
@@ -260,6 +264,8 @@ struct DmaOperand {
                 if ((CHUNKS % Cfg::THREADS != 0 || GL % GB != 0) && (i0 + b >= GL || q >= CHUNKS)) break;
                 *reinterpret_cast<u32x4*>(lds + L::off(q / L::CPR, q % L::CPR)) = v[b];
             }
+            // keep the next batch's loads behind this batch's stores
+            asm volatile("" ::: "memory");
         }
     }
 
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     __shared__ __attribute__((aligned(1024))) char st2[Cfg::STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? Cfg::STAGE_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) char st4[S > 4 ? Cfg::STAGE_BYTES : 16];
-    auto stage = [&](int s) -> char* {
+    auto stage = [&](int s) __attribute__((always_inline)) -> char* {
         return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : s == 3 ? st3 : st4;
     };
 
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     // exact zeros past K and is always register-staged.
     const int nk_dma = ALIGNED ? ((k_ragged || edge) ? nk - 1 : nk) : 0;
 
-    auto load = [&](int kt, char* base) {
+    auto load = [&](int kt, char* base) __attribute__((always_inline)) {
         const int k0 = kt * BK;
         if (kt < nk_dma) {
             oa.dma(rsrc_a, OpA::step_bytes(k0, p.lda), base, wave);
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     barrier_only();
 
     u32x4 fa[2][MF], fb[2][NF];
-    auto read_frags = [&](const char* base, int ks, int buf) {
+    auto read_frags = [&](const char* base, int ks, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < MF; ++i) fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
 #pragma unroll
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     // One K-step held in LDS stage CUR (static, so every LDS address is a
     // compile-time offset from its own __shared__ array).  STEADY: the step
     // AHEAD ahead exists and is copied by DMA, so no run-time conditions.
-    auto step = [&](auto cur_c, auto steady_c, int kt) {
+    auto step = [&](auto cur_c, auto steady_c, int kt) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr bool STEADY = decltype(steady_c)::value;
         constexpr int NXT = (CUR + 1) % S;
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     constexpr int NREAD = MF * RA + NF * RB;
     constexpr int NMFMA = MF * NF;
     constexpr int NDMA = OpA::ND + OpB::ND;
-    auto read_op = [&](int n, const char* base, int ks, int buf) {
+    auto read_op = [&](int n, const char* base, int ks, int buf) __attribute__((always_inline)) {
         if (n < MF * RA) {
             const int i = n / RA;
             if constexpr (RA == 1) {
@@ -499,48 +505,48 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
             }
         }
     };
-    auto steady = [&](auto cur_c, int kt) {
+    auto steady = [&](auto cur_c, int kt) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         constexpr int NXT = (CUR + 1) % S;
         constexpr int FAR = (CUR + FILL) % S;
         const char* base = stage(CUR);
         const int kfar = (kt + AHEAD) * BK;
         const uint32_t ka = OpA::step_bytes(kfar, p.lda), kb = OpB::step_bytes(kfar, p.ldb);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int cb = ks & 1;
-            const bool mid = ks == BAR_KS;
-            if (mid) {
+        static_for<NKS>([&](auto ks_c) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ks_c)::value;
+            constexpr int cb = ks & 1;
+            constexpr bool mid = ks == BAR_KS;
+            if constexpr (mid) {
                 if constexpr (Cfg::LATE) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
                 else wait_vm<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
                 barrier_only();
             }
             const char* rbase = ks + 1 < NKS ? base : stage(NXT);
-            const int rks = ks + 1 < NKS ? ks + 1 : 0;
-            const int nops = NREAD + (mid ? NDMA : 0);
-#pragma unroll
-            for (int e = 0; e < NMFMA; ++e) {
+            constexpr int rks = ks + 1 < NKS ? ks + 1 : 0;
+            constexpr int nops = NREAD + (mid ? NDMA : 0);
+            static_for<NMFMA>([&](auto e_c) __attribute__((always_inline)) {
+                constexpr int e = decltype(e_c)::value;
                 mfma_step<Cfg::KIND>(fb[cb][e % NF], fa[cb][e / NF], acc[e / NF][e % NF]);
                 __builtin_amdgcn_sched_barrier(0);
                 // front-load: fragment reads go out over the first half of the
                 // MFMAs (two per MFMA), DMA copies over the rest
                 constexpr int HALF = NMFMA / 2;
-                const int lo = e < HALF ? e * NREAD / HALF
-                                        : NREAD + (e - HALF) * (nops - NREAD) / (NMFMA - HALF);
-                const int hi = e + 1 < HALF ? (e + 1) * NREAD / HALF
-                             : e + 1 == HALF ? NREAD
-                                             : NREAD + (e + 1 - HALF) * (nops - NREAD) / (NMFMA - HALF);
-#pragma unroll
-                for (int o = lo; o < hi; ++o) {
-                    if (o < NREAD) read_op(o, rbase, rks, cb ^ 1);
-                    else if (o - NREAD < OpA::ND)
+                constexpr int lo = e < HALF ? e * NREAD / HALF
+                                            : NREAD + (e - HALF) * (nops - NREAD) / (NMFMA - HALF);
+                constexpr int hi = e + 1 < HALF ? (e + 1) * NREAD / HALF
+                                 : e + 1 == HALF ? NREAD
+                                                 : NREAD + (e + 1 - HALF) * (nops - NREAD) / (NMFMA - HALF);
+                static_for<hi - lo>([&](auto oo_c) __attribute__((always_inline)) {
+                    constexpr int o = lo + decltype(oo_c)::value;
+                    if constexpr (o < NREAD) read_op(o, rbase, rks, cb ^ 1);
+                    else if constexpr (o - NREAD < OpA::ND)
                         oa.dma_one(o - NREAD, rsrc_a, ka, stage(FAR), wave);
                     else
                         ob.dma_one(o - NREAD - OpA::ND, rsrc_b, kb, stage(FAR) + Cfg::A_BYTES, wave);
-                }
+                });
                 __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+            });
+        });
     };
 
     using T_ = std::true_type;
