@@ -37,7 +37,8 @@ GEMM_ERR_ALLOC = 4
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
            "gemm_variant_count", "gemm_variant_name", "gemm_variant_dtype",
            "gemm_variant_tile", "gemm_set_variant", "gemm_last_variant",
-           "gemm_select_variant")
+           "gemm_select_variant", "gemm_stream_k_workspace_bytes", "gemm_set_workspace",
+           "gemm_set_stream_k", "gemm_last_stream_k")
 
 
 class GemmError(RuntimeError):
@@ -95,6 +96,14 @@ def _load():
     lib.gemm_last_variant.restype = i32
     lib.gemm_select_variant.argtypes = [i32, i32, i32, i64, i64, i64]
     lib.gemm_select_variant.restype = i32
+    lib.gemm_stream_k_workspace_bytes.argtypes = []
+    lib.gemm_stream_k_workspace_bytes.restype = ctypes.c_size_t
+    lib.gemm_set_workspace.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.gemm_set_workspace.restype = i32
+    lib.gemm_set_stream_k.argtypes = [vp, i32]
+    lib.gemm_set_stream_k.restype = i32
+    lib.gemm_last_stream_k.argtypes = [vp]
+    lib.gemm_last_stream_k.restype = i32
     return lib
 
 
@@ -155,6 +164,38 @@ def gemm_last_variant(h) -> int:
 
 def gemm_select_variant(dtype, transA, transB, M, N, K) -> int:
     return lib.gemm_select_variant(dtype, transA, transB, M, N, K)
+
+
+def gemm_stream_k_workspace_bytes() -> int:
+    return lib.gemm_stream_k_workspace_bytes()
+
+
+def gemm_set_workspace(h, ws, nbytes: int, stream) -> int:
+    """Raw call: ws and stream are integers (0/None for NULL)."""
+    return lib.gemm_set_workspace(h, ws, nbytes, stream)
+
+
+def gemm_set_stream_k(h, mode: int) -> int:
+    return lib.gemm_set_stream_k(h, mode)
+
+
+def gemm_last_stream_k(h) -> int:
+    return lib.gemm_last_stream_k(h)
+
+
+def attach_workspace(h, nbytes=None, device=None):
+    """Allocate a stream-K workspace as a torch uint8 tensor on `device` (the
+    current device by default), hand it to h and return it; the caller keeps
+    the tensor alive as long as h may use it."""
+    import torch
+
+    nbytes = gemm_stream_k_workspace_bytes() if nbytes is None else int(nbytes)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+    stream = torch.cuda.current_stream(ws.device).cuda_stream
+    s = gemm_set_workspace(h, ws.data_ptr(), nbytes, stream)
+    if s != GEMM_OK:
+        raise GemmError(s, "gemm_set_workspace")
+    return ws
 
 
 def variants():

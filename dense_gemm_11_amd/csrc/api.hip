@@ -14,6 +14,10 @@
 struct gemm_handle_s {
     int forced_variant;  // -1: automatic selection
     int last_variant;
+    int stream_k_mode;   // -1: automatic, 0: never, 1: whenever the variant and workspace allow
+    int last_stream_k;   // stream-K workgroups of the last call (0: data-parallel)
+    void* ws;            // caller-owned device workspace for stream-K, or null
+    size_t ws_bytes;
 };
 
 namespace dg {
@@ -30,14 +34,25 @@ __global__ __launch_bounds__(256) void scale_c_kernel(GemmArgs p)
 }
 
 
+// Zero the stream-K flags of a workspace.
+__global__ __launch_bounds__(256) void clear_flags_kernel(unsigned* flags, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) flags[i] = 0u;
+}
+
 namespace {
+
+// Stream-K workspace layout: SK_MAX_WG flags, then one BM*BN fp32 slot per workgroup.
+constexpr int SK_MAX_WG = 4096;
+constexpr size_t SK_FLAG_BYTES = SK_MAX_WG * sizeof(unsigned);
 
 const std::vector<Variant>& table()
 {
     static const std::vector<Variant> t = [] {
         std::vector<Variant> v;
         for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
-                         bf16dma_variant_table, f32dma_variant_table}) {
+                         bf16dma_variant_table, f32dma_variant_table,
+                         bf16dma_sweep_variant_table, f32dma_sweep_variant_table}) {
             int n = 0;
             const Variant* t = get(&n);
             v.insert(v.end(), t, t + n);
@@ -85,16 +100,27 @@ int device_cus()
 // three 32-deep stages for bf16 (measured 8-10 % faster than the half-way
 // barrier with four stages on 8192^3 with k-contiguous A) and two 32-deep
 // stages for fp32 (1 % faster than three 16-deep ones on 4096^3).
+// The direct-to-LDS variant with 256x256 (big) or 128x128 tiles for a dtype.
+int dma_variant(int dtype, bool big)
+{
+    static const int ids[2][2] = {
+        {find_variant("f32_dma32x32x2_128x128x16_w2x2_s3_late"),
+         find_variant("f32_dma32x32x2_256x256x32_w2x2_s2_late")},
+        {find_variant("bf16_dma32x32x16_128x128x32_w2x2_s3_late"),
+         find_variant("bf16_dma32x32x16_256x256x32_w2x2_s3_late")}};
+    return ids[dtype == GEMM_DTYPE_BF16_F32][big];
+}
+
 int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
 {
-    static const int bf16_dma_big = find_variant("bf16_dma32x32x16_256x256x32_w2x2_s3_late");
-    static const int bf16_dma_mid = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s3_late");
+    const int bf16_dma_big = dma_variant(GEMM_DTYPE_BF16_F32, true);
+    const int bf16_dma_mid = dma_variant(GEMM_DTYPE_BF16_F32, false);
     static const int bf16_big = find_variant("bf16_mfma32x32x16_256x256x64_w2x2");
     static const int bf16_mid = find_variant("bf16_mfma16x16x32_128x128x64_w2x2");
     static const int f32_big = find_variant("f32_mfma32x32x2_256x256x32_w2x2");
     static const int f32_mid = find_variant("f32_mfma32x32x2_128x128x32_w2x2");
-    static const int f32_dma_big = find_variant("f32_dma32x32x2_256x256x32_w2x2_s2_late");
-    static const int f32_dma_mid = find_variant("f32_dma32x32x2_128x128x16_w2x2_s3_late");
+    const int f32_dma_big = dma_variant(GEMM_DTYPE_F32, true);
+    const int f32_dma_mid = dma_variant(GEMM_DTYPE_F32, false);
     const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
     const bool big = 4 * big_tiles >= 3 * (int64_t)device_cus();
     if (dtype == GEMM_DTYPE_BF16_F32) {
@@ -103,6 +129,83 @@ int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
     }
     if (dma) return big ? f32_dma_big : f32_dma_mid;
     return big ? f32_big : f32_mid;
+}
+
+// Time of one K-step of a tile of variant v for a workgroup alone on a
+// compute unit, in microseconds: measured on MI355X for 256x256x32 steps
+// (bf16 0.85 us, fp32 7.3 us; 8192^3 and 4096^3 runs) and scaled by the
+// step's FLOPs for other tiles (128x128x32 bf16 measured 0.245 us).
+double step_us(const Variant& v)
+{
+    const double base = v.dtype == GEMM_DTYPE_BF16_F32 ? 0.85 : 7.3;
+    return base * ((double)v.bm * v.bn * v.bk) / (256.0 * 256.0 * 32.0);
+}
+
+int variant_occupancy(const Variant& v)
+{
+    static int cache[64] = {0};
+    const int vid = (int)(&v - table().data());
+    if (!v.sk_occ || vid < 0 || vid >= 64) return v.bm * v.bn >= 256 * 256 ? 1 : 2;
+    if (cache[vid] == 0) cache[vid] = std::max(1, v.sk_occ());
+    return cache[vid];
+}
+
+// Estimated time of the data-parallel launch: waves of concurrently resident
+// tiles, each K-step slowed by the workgroups sharing its compute unit.
+double data_parallel_us(const Variant& v, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t cus = device_cus(), occ = variant_occupancy(v);
+    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
+    const int64_t waves = ceil_div(tiles, cus * occ);
+    const double share = std::min<double>((double)occ, std::max(1.0, (double)tiles / cus));
+    return waves * ceil_div(K, v.bk) * step_us(v) * share;
+}
+
+// Stream-K plan for a direct-to-LDS variant: the number of workgroups to
+// split the (tile, K-step) iterations over, or 0 for data-parallel tiles.
+// Stream-K divides the work evenly but pays a fix-up ("GEMM on NVIDIA GPUs",
+// section 5): every workgroup that ends inside a tile writes a BM x BN fp32
+// partial that the tile's finisher reads back (device-scope traffic, taken
+// at 3 TB/s), and a finisher reduces its contributors one after another (one
+// memory round trip, ~1.5 us, per fragment row and contributor).  The grid
+// is chosen among 2, 4, 8, ... workgroups per tile (at least one per tile,
+// since the kernel gives a workgroup at most one tile's iterations, and at
+// most the device's workgroup slots); mode 1 takes the best of these
+// regardless, automatic mode only when it beats the data-parallel estimate
+// `dp_us` by a fifth.
+int stream_k_grid(const Variant& v, int64_t M, int64_t N, int64_t K, int mode, size_t ws_bytes,
+                  double dp_us, double* est_us = nullptr)
+{
+    if (mode == 0 || !v.sk_occ || ws_bytes == 0) return 0;
+    const int64_t slots = std::min<int64_t>((int64_t)device_cus() * variant_occupancy(v), SK_MAX_WG);
+    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
+    const int64_t nk = ceil_div(K, v.bk);
+    const int64_t W = tiles * nk;
+    const double tile_bytes = (double)v.bm * v.bn * sizeof(float);
+    const int mf = v.bm / 2 / 32;  // fragment rows per wave (2x2 waves, 32-row fragments)
+    int64_t best_g = 0;
+    double best_us = 0.0;
+    for (int64_t g = 2 * tiles;; g *= 2) {
+        const int64_t gg = std::min<int64_t>(std::min(g, slots), W / 4);
+        if (gg < tiles || gg < 2) break;
+        const size_t need = SK_FLAG_BYTES + (size_t)gg * v.bm * v.bn * sizeof(float);
+        if (need <= ws_bytes) {
+            const int64_t per = ceil_div(W, gg);
+            const int64_t splits = ceil_div(nk, W / gg);  // workgroups meeting one tile
+            const double contrib = (double)std::max<int64_t>(gg - tiles, 0);
+            const double us = per * step_us(v) + 2.0 * contrib * tile_bytes / 3e12 * 1e6 +
+                              (double)(splits - 1) * mf * 1.5 + 5.0;
+            if (best_g == 0 || us < best_us) {
+                best_g = gg;
+                best_us = us;
+            }
+        }
+        if (gg != g) break;  // capped: larger grids give the same one
+    }
+    if (best_g == 0) return 0;
+    if (mode < 0 && !(best_us < 0.8 * dp_us)) return 0;
+    if (est_us) *est_us = best_us;
+    return (int)best_g;
 }
 
 bool aligned_to(const void* p, int64_t bytes)
@@ -138,7 +241,7 @@ extern "C" {
 gemm_status_t gemm_create(gemm_handle_t* out)
 {
     if (!out) return GEMM_ERR_INVALID_VALUE;
-    gemm_handle_t h = new (std::nothrow) gemm_handle_s{-1, -1};
+    gemm_handle_t h = new (std::nothrow) gemm_handle_s{-1, -1, -1, 0, nullptr, 0};
     if (!h) return GEMM_ERR_ALLOC;
     *out = h;
     return GEMM_OK;
@@ -195,6 +298,48 @@ gemm_status_t gemm_set_variant(gemm_handle_t h, int id)
 
 int gemm_last_variant(gemm_handle_t h) { return h ? h->last_variant : -1; }
 
+int gemm_last_stream_k(gemm_handle_t h) { return h ? h->last_stream_k : -1; }
+
+size_t gemm_stream_k_workspace_bytes(void)
+{
+    using namespace dg;
+    size_t most = 0;
+    for (const Variant& v : table()) {
+        if (!v.sk_occ) continue;
+        const size_t g = std::min<size_t>((size_t)device_cus() * variant_occupancy(v), SK_MAX_WG);
+        most = std::max(most, g * v.bm * v.bn * sizeof(float));
+    }
+    return SK_FLAG_BYTES + most;
+}
+
+gemm_status_t gemm_set_workspace(gemm_handle_t h, void* ws, size_t bytes, hipStream_t stream)
+{
+    using namespace dg;
+    if (!h) return GEMM_ERR_INVALID_VALUE;
+    if (!ws || bytes == 0) {
+        h->ws = nullptr;
+        h->ws_bytes = 0;
+        return GEMM_OK;
+    }
+    if (!aligned_to(ws, 256) || bytes < SK_FLAG_BYTES) return GEMM_ERR_INVALID_VALUE;
+    unsigned* flags = static_cast<unsigned*>(ws);
+    int n = SK_MAX_WG;
+    void* kargs[] = {&flags, &n};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_flags_kernel), dim3(16), dim3(256),
+                        kargs, 0, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    h->ws = ws;
+    h->ws_bytes = bytes;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_set_stream_k(gemm_handle_t h, int mode)
+{
+    if (!h || mode < -1 || mode > 1) return GEMM_ERR_INVALID_VALUE;
+    h->stream_k_mode = mode;
+    return GEMM_OK;
+}
+
 int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, int64_t M,
                         int64_t N, int64_t K)
 {
@@ -222,6 +367,7 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     if (lda < min_lda || ldb < min_ldb || ldd < min_ldcd) return GEMM_ERR_INVALID_VALUE;
     if (beta != 0.0f && ldc < min_ldcd) return GEMM_ERR_INVALID_VALUE;
     h->last_variant = -1;
+    h->last_stream_k = 0;
     if (M == 0 || N == 0) return GEMM_OK;
     const bool reads_ab = K > 0 && alpha != 0.0f;
     if (!D) return GEMM_ERR_INVALID_VALUE;
@@ -257,6 +403,8 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     // unaligned vector loads and stores whole
     a.c_vec = beta != 0.0f && aligned_to(C, 4);
     a.d_vec = aligned_to(D, 4);
+    a.sk_partials = nullptr;
+    a.sk_flags = nullptr;
 
     if (!reads_ab) {
         const int64_t blocks = std::min<int64_t>(ceil_div(M * N, 256), 65536);
@@ -281,17 +429,44 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     // through registers instead (its ALIGNED == false instantiation)
     const bool aligned =
         wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, a_kc, b_kc, K, lda, ldb, es));
-    a.tiles_m = (int)ceil_div(M, v.bm);
-    a.tiles_n = (int)ceil_div(N, v.bn);
+    const double dp_us = data_parallel_us(v, M, N, K);
+    double sk_us = 0.0;
+    int sk = (aligned && v.kind == KIND_MFMA_DMA)
+                 ? stream_k_grid(v, M, N, K, h->stream_k_mode, h->ws_bytes, dp_us, &sk_us)
+                 : 0;
+    if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0) {
+        // With a workspace, stream-K on the other tile size competes too; the
+        // lowest estimate wins.
+        const int other = dma_variant(dtype, v.bm < 256);
+        if (other != id && dma_offsets_fit(table()[other], a_kc, b_kc, K, lda, ldb, es)) {
+            double o_us = 0.0;
+            const int sk_o = stream_k_grid(table()[other], M, N, K, h->stream_k_mode, h->ws_bytes,
+                                           dp_us, &o_us);
+            if (sk_o > 0 && (sk == 0 || o_us < sk_us)) {
+                id = other;
+                sk = sk_o;
+            }
+        }
+    }
+    const Variant& vr = table()[id];
+    a.tiles_m = (int)ceil_div(M, vr.bm);
+    a.tiles_n = (int)ceil_div(N, vr.bn);
     // 4 tile-rows per group measured best on 8192^3 bf16 (groups of 1, 2, 3, 4, 6,
     // 8, 16 and 32 tried, with and without the XCD renumbering)
     a.group_m = std::min(a.tiles_m, 4);
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
-    LaunchFn fn = v.fn[aligned][a_kc][b_kc];
-    const hipError_t e = fn(a, (int)grid, stream);
+    hipError_t e;
+    if (sk > 0) {
+        a.sk_flags = static_cast<unsigned*>(h->ws);
+        a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
+        e = vr.sk_fn[a_kc][b_kc](a, sk, stream);
+    } else {
+        e = vr.fn[aligned][a_kc][b_kc](a, (int)grid, stream);
+    }
     if (e != hipSuccess) return GEMM_ERR_HIP;
     h->last_variant = id;
+    h->last_stream_k = sk;
     return GEMM_OK;
 }
 

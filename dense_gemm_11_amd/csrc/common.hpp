@@ -37,19 +37,16 @@ struct GemmArgs {
     int group_m;           // tile-rows walked together for L2/MALL reuse
     int c_vec;             // C rows allow 16-byte loads (pointer and ldc aligned)
     int d_vec;             // D rows allow 16-byte stores
+    // stream-K only: one BM*BN partial-sum slot and one flag per workgroup
+    float* sk_partials;
+    unsigned* sk_flags;
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Renumber them so that XCD x runs a contiguous range of logical tile
-// ids, then walk tiles in groups of `group_m` tile-rows so that concurrently
-// running workgroups on one XCD share A row-panels and B column-panels.
-__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
+// Tile (tm, tn) of logical tile id w: tiles are walked in groups of group_m
+// tile-rows, column by column within a group, so that workgroups running at
+// the same time share A row-panels and B column-panels.
+__device__ __forceinline__ void tile_of(const GemmArgs& p, int w, int& tm, int& tn)
 {
-    const int total = p.tiles_m * p.tiles_n;
-    int w = blockIdx.x;
-    constexpr int XCDS = 8;
-    const int full = (total / XCDS) * XCDS;
-    if (w < full) w = (w % XCDS) * (full / XCDS) + (w / XCDS);
     const int per_group = p.group_m * p.tiles_n;
     const int group = w / per_group;
     const int first_m = group * p.group_m;
@@ -58,6 +55,19 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
     const int in_group = w - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Renumber them so that XCD x runs a contiguous range of logical tile
+// ids, then map the logical id to a tile as above.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
+{
+    const int total = p.tiles_m * p.tiles_n;
+    int w = blockIdx.x;
+    constexpr int XCDS = 8;
+    const int full = (total / XCDS) * XCDS;
+    if (w < full) w = (w % XCDS) * (full / XCDS) + (w / XCDS);
+    tile_of(p, w, tm, tn);
 }
 
 // Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1: every index is

@@ -341,7 +341,7 @@ __device__ __forceinline__ void wait_vm_lgkm0()
 
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED>
+template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false>
 __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
@@ -362,16 +362,9 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wave_m0 = (wave / Cfg::WN) * Cfg::WTM;
     const int wave_n0 = (wave % Cfg::WN) * Cfg::WTN;
-    int tm, tn;
-    tile_coords(p, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int rlim_a = p.M - m0, rlim_b = p.N - n0;
-    const bool edge = rlim_a < BM || rlim_b < BN;
     using T = typename Cfg::T;
     const T* A = static_cast<const T*>(p.A);
     const T* B = static_cast<const T*>(p.B);
-    const T* panel_a = A_KC ? A + (int64_t)m0 * p.lda : A + m0;
-    const T* panel_b = B_KC ? B + (int64_t)n0 * p.ldb : B + n0;
 
     OpA oa;
     OpB ob;
@@ -382,21 +375,34 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         A + (A_KC ? (int64_t)(p.M - 1) * p.lda + p.K : (int64_t)(p.K - 1) * p.lda + p.M));
     const char* end_b = reinterpret_cast<const char*>(
         B + (B_KC ? (int64_t)(p.N - 1) * p.ldb + p.K : (int64_t)(p.K - 1) * p.ldb + p.N));
+    const int nk_all = (p.K + BK - 1) / BK;  // K-steps of a whole tile
+    const bool k_ragged = (p.K % BK) != 0;
+
+    Acc acc[MF][NF];
+    u32x4 fa[2][MF], fb[2][NF];
+
+    // The K-steps [k_lo, k_hi) of output tile (tm, tn), accumulated into acc
+    // from zero.  Every wave enters with the LDS stages free.
+    auto tile_work = [&](int tm, int tn, int k_lo, int k_hi) __attribute__((always_inline)) {
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rlim_a = p.M - m0, rlim_b = p.N - n0;
+    const bool edge = rlim_a < BM || rlim_b < BN;
+    const T* panel_a = A_KC ? A + (int64_t)m0 * p.lda : A + m0;
+    const T* panel_b = B_KC ? B + (int64_t)n0 * p.ldb : B + n0;
     const i32x4 rsrc_a = OpA::panel_rsrc(panel_a, end_a);
     const i32x4 rsrc_b = OpB::panel_rsrc(panel_b, end_b);
-
-    const int nk = (p.K + BK - 1) / BK;
-    const bool k_ragged = (p.K % BK) != 0;
+    const int nk = k_hi - k_lo;              // steps of this range; step kt is K-step k_lo + kt
+    const bool last = k_hi == nk_all;
     // Steps copied by DMA.  Rows past the matrix read as zero through the
     // buffer range and chunks that run past a row's end only feed outputs the
     // epilogue masks, so edge tiles use DMA too, except on their last step: a
     // chunk that straddles the end of the matrix would lose its last valid
     // bf16 element to the word-granular range check.  A ragged last step needs
     // exact zeros past K and is always register-staged.
-    const int nk_dma = ALIGNED ? ((k_ragged || edge) ? nk - 1 : nk) : 0;
+    const int nk_dma = ALIGNED ? ((last && (k_ragged || edge)) ? nk - 1 : nk) : 0;
 
     auto load = [&](int kt, char* base) __attribute__((always_inline)) {
-        const int k0 = kt * BK;
+        const int k0 = (k_lo + kt) * BK;
         if (kt < nk_dma) {
             oa.dma(rsrc_a, OpA::step_bytes(k0, p.lda), base, wave);
             ob.dma(rsrc_b, OpB::step_bytes(k0, p.ldb), base + Cfg::A_BYTES, wave);
@@ -406,7 +412,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         }
     };
 
-    Acc acc[MF][NF];
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -421,7 +426,6 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     else wait_vm_lgkm0<0>();
     barrier_only();
 
-    u32x4 fa[2][MF], fb[2][NF];
     auto read_frags = [&](const char* base, int ks, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < MF; ++i) fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                 else wait_vm_lgkm0<0>();
                 barrier_only();
                 if (STEADY) {
-                    const int kf = (kt + AHEAD) * BK;
+                    const int kf = (k_lo + kt + AHEAD) * BK;
                     oa.dma(rsrc_a, OpA::step_bytes(kf, p.lda), stage(FAR), wave);
                     ob.dma(rsrc_b, OpB::step_bytes(kf, p.ldb), stage(FAR) + Cfg::A_BYTES, wave);
                 } else if (kt + AHEAD < nk) {
@@ -510,7 +514,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         constexpr int NXT = (CUR + 1) % S;
         constexpr int FAR = (CUR + FILL) % S;
         const char* base = stage(CUR);
-        const int kfar = (kt + AHEAD) * BK;
+        const int kfar = (k_lo + kt + AHEAD) * BK;
         const uint32_t ka = OpA::step_bytes(kfar, p.lda), kb = OpB::step_bytes(kfar, p.ldb);
         static_for<NKS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
@@ -577,48 +581,179 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         if constexpr (S > 4)
             if (kt + 4 < nk) step(I4{}, F_{}, kt + 4);
     }
+    };  // tile_work
 
-    // ---- epilogue: lane holds 4 adjacent columns of one row per accumulator group
+    // Index (in f32x4 units) of a thread's accumulator group (i, j, vg) in a
+    // stream-K partial-sum slot: consecutive threads hold consecutive 16 bytes.
+    constexpr int TILE_F = BM * BN;
+    auto part_index = [&](int i, int j, int vg) __attribute__((always_inline)) {
+        return ((i * NF + j) * (Cfg::ACC / 4) + vg) * Cfg::THREADS + tid;
+    };
+    // Partial-sum slot of workgroup c as a buffer, accessed at device scope
+    // (cache policy SC1): stores are written through to where every XCD sees
+    // them and loads do not return lines another XCD's L2 may hold stale, so
+    // the hand-off needs no whole-cache write-back or invalidate.
+    constexpr int CPOL_SC1 = 16;
+    auto part_rsrc = [&](int64_t c) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc(p.sk_partials + c * TILE_F, 0, TILE_F * 4,
+                                                 0x00020000);
+    };
+
+    // ---- epilogue: lane holds 4 adjacent columns of one row per accumulator
+    // group.  One fragment row at a time: every load the row needs (beta*C,
+    // and a stream-K finisher's contributors' partial sums, added in
+    // workgroup order) is issued before any of its stores, so the row waits
+    // for memory once instead of once per 16-byte group.  c0..c1 are the
+    // contributing workgroups (none when c0 == c1).
+    auto epilogue = [&](int tm, int tn, int64_t c0, int64_t c1) __attribute__((always_inline)) {
+    const int m0 = tm * BM, n0 = tn * BN;
     const float alpha = p.alpha, beta = p.beta;
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
+    constexpr int VG = Cfg::ACC / 4;
+    auto col_of = [&](int j, int vg) __attribute__((always_inline)) {
+        return n0 + wave_n0 + j * FM + (FM == 32 ? 8 * vg + 4 * (lane >> 5) : 4 * (lane >> 4));
+    };
+    static_for<MF>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
         const int row = m0 + wave_m0 + i * FM + lane % FM;
-        if (row >= p.M) continue;
-        float* drow = p.D + (int64_t)row * p.ldd;
+        const bool row_ok = row < p.M;
+        f32x4 sum[NF][VG];
 #pragma unroll
-        for (int j = 0; j < NF; ++j) {
+        for (int j = 0; j < NF; ++j)
 #pragma unroll
-            for (int vg = 0; vg < Cfg::ACC / 4; ++vg) {
-                const int col = n0 + wave_n0 + j * FM +
-                                (FM == 32 ? 8 * vg + 4 * (lane >> 5) : 4 * (lane >> 4));
-                float out[4];
+            for (int vg = 0; vg < VG; ++vg)
+                sum[j][vg] = f32x4{acc[i][j][4 * vg], acc[i][j][4 * vg + 1], acc[i][j][4 * vg + 2],
+                                   acc[i][j][4 * vg + 3]};
+        f32x4 cv[NF][VG];
+        if (beta != 0.0f) {
+            const float* crow = p.C + (int64_t)(row_ok ? row : 0) * p.ldc;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) out[s] = alpha * acc[i][j][4 * vg + s];
-                if (p.d_vec && col + 4 <= p.N) {
-                    if (beta != 0.0f) {
-                        const float* crow = p.C + (int64_t)row * p.ldc;
-                        if (p.c_vec) {
-                            const f32x4 c = *reinterpret_cast<const f32x4*>(crow + col);
+            for (int j = 0; j < NF; ++j)
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) out[s] += beta * c[s];
-                        } else {
+                for (int vg = 0; vg < VG; ++vg) {
+                    const int col = col_of(j, vg);
+                    if (row_ok && p.c_vec && col + 4 <= p.N) {
+                        cv[j][vg] = *reinterpret_cast<const f32x4*>(crow + col);
+                    } else {
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) out[s] += beta * crow[col + s];
-                        }
-                    }
-                    *reinterpret_cast<f32x4*>(drow + col) = f32x4{out[0], out[1], out[2], out[3]};
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        if (col + s < p.N) {
-                            float o = out[s];
-                            if (beta != 0.0f) o += beta * p.C[(int64_t)row * p.ldc + col + s];
-                            drow[col + s] = o;
-                        }
+                        for (int s = 0; s < 4; ++s)
+                            cv[j][vg][s] = (row_ok && col + s < p.N) ? crow[col + s] : 0.0f;
                     }
                 }
+        }
+        if constexpr (SK) {
+            for (int64_t c = c0; c < c1; ++c) {
+                const auto rsrc = part_rsrc(c);
+                f32x4 v[NF][VG];
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+#pragma unroll
+                    for (int vg = 0; vg < VG; ++vg)
+                        v[j][vg] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rsrc, part_index(i, j, vg) * 16, 0, CPOL_SC1));
+#pragma unroll
+                for (int j = 0; j < NF; ++j)
+#pragma unroll
+                    for (int vg = 0; vg < VG; ++vg) sum[j][vg] += v[j][vg];
             }
         }
+        if (!row_ok) return;
+        float* drow = p.D + (int64_t)row * p.ldd;
+#pragma unroll
+        for (int j = 0; j < NF; ++j)
+#pragma unroll
+            for (int vg = 0; vg < VG; ++vg) {
+                const int col = col_of(j, vg);
+                f32x4 out = alpha * sum[j][vg];
+                if (beta != 0.0f) out += beta * cv[j][vg];
+                if (p.d_vec && col + 4 <= p.N) {
+                    *reinterpret_cast<f32x4*>(drow + col) = out;
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        if (col + s < p.N) drow[col + s] = out[s];
+                }
+            }
+    });
+    };  // epilogue
+
+    if constexpr (!SK) {
+        int tm, tn;
+        tile_coords(p, tm, tn);
+        tile_work(tm, tn, 0, nk_all);
+        epilogue(tm, tn, 0, 0);
+    } else {
+        // Stream-K ("GEMM on NVIDIA GPUs", section 5: split-K partial sums
+        // P^(s) = sum over a K range, reduced afterwards).  The grid's G >=
+        // tiles workgroups split the W = tiles * nk_all (tile, K-step)
+        // iterations evenly: workgroup g takes [g*W/G, (g+1)*W/G), at most one
+        // tile's worth, so it meets at most two tiles: the end of one and the
+        // start of the next.  A tile is finished by the workgroup that reaches
+        // its last K-step; every other workgroup touching the tile ends its
+        // range inside it, stores its partial sums to its own workspace slot
+        // and raises its flag.  A workgroup does that contributing segment
+        // first, so no contribution waits behind another tile's fix-up.  The
+        // finisher waits for the lower-numbered contributors, adds their
+        // partials in workgroup (= K) order, so the result is reproducible,
+        // and runs the epilogue.  Contributions are published before any wait,
+        // so the waits cannot deadlock; they are bounded as well.
+        const int64_t W = (int64_t)p.tiles_m * p.tiles_n * nk_all;
+        const int64_t G = gridDim.x, g = blockIdx.x;
+        const int64_t w_end = (g + 1) * W / G;
+        // one segment: the iterations from w to the end of w's tile or of the
+        // range, whichever comes first
+        auto segment = [&](int64_t w) __attribute__((always_inline)) {
+            const int t = (int)(w / nk_all);
+            const int k_lo = (int)(w - (int64_t)t * nk_all);
+            const int64_t t_end = (int64_t)(t + 1) * nk_all;
+            const int k_hi = (int)((w_end < t_end ? w_end : t_end) - (int64_t)t * nk_all);
+            int tm, tn;
+            tile_of(p, t, tm, tn);
+            __syncthreads();  // the previous segment's reads of the LDS stages are done
+            tile_work(tm, tn, k_lo, k_hi);
+            if (k_hi == nk_all) {
+                // contributors: the workgroups owning iterations t*nk_all .. w-1
+                const int64_t c0 = k_lo > 0 ? ((int64_t)t * nk_all * G + G - 1) / W : g;
+                if (c0 < g) {
+                    if (tid == 0) {
+                        for (int64_t c = c0; c < g; ++c) {
+                            for (int it = 0; it < (1 << 20); ++it) {
+                                if (__hip_atomic_load(p.sk_flags + c, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                                    break;
+                                __builtin_amdgcn_s_sleep(2);
+                            }
+                            __hip_atomic_store(p.sk_flags + c, 0u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                    }
+                    __syncthreads();
+                }
+                epilogue(tm, tn, c0, g);
+            } else {
+                const auto rsrc = part_rsrc(g);
+#pragma unroll
+                for (int i = 0; i < MF; ++i)
+#pragma unroll
+                    for (int j = 0; j < NF; ++j)
+#pragma unroll
+                        for (int vg = 0; vg < Cfg::ACC / 4; ++vg)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * vg], acc[i][j][4 * vg + 1],
+                                                                acc[i][j][4 * vg + 2],
+                                                                acc[i][j][4 * vg + 3]}),
+                                rsrc, part_index(i, j, vg) * 16, 0, CPOL_SC1);
+                wait_vm<0>();     // every partial store has been acknowledged
+                __syncthreads();  // ... in every wave
+                if (tid == 0)
+                    __hip_atomic_store(p.sk_flags + g, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        const int64_t w0 = g * W / G;
+        const int64_t t0_end = (w0 / nk_all + 1) * nk_all;
+        if (w_end > t0_end) segment(t0_end);  // start of the next tile (contributes)
+        segment(w0);
     }
 }
 

@@ -7,6 +7,7 @@
 namespace dg {
 
 typedef hipError_t (*LaunchFn)(const GemmArgs&, int grid, hipStream_t);
+typedef int (*OccFn)();  // workgroups of the kernel that fit on one compute unit
 
 enum VariantKind { KIND_VECTOR_FMA = 0, KIND_MFMA = 1, KIND_MFMA_DMA = 2 };
 
@@ -16,6 +17,8 @@ struct Variant {
     int kind;    // VariantKind
     int bm, bn, bk, threads, lds_bytes;
     LaunchFn fn[2][2][2];  // [wide access][A k-contiguous][B k-contiguous]
+    LaunchFn sk_fn[2][2];  // stream-K instantiations (wide access only), or null
+    OccFn sk_occ;          // occupancy of the stream-K kernel, or null
 };
 
 // Launch through hipLaunchKernel so the launch status is returned directly.
@@ -28,6 +31,16 @@ hipError_t launch_kernel(const GemmArgs& a, int grid, hipStream_t s)
                            0, s);
 }
 
+template <auto KERNEL, int THREADS>
+int occupancy()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(KERNEL),
+                                                     THREADS, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
 // Table fragments, one per instantiation file (host functions returning a
 // static array, so the device compile never sees host function pointers).
 const Variant* bf16_variant_table(int* count);
@@ -35,6 +48,8 @@ const Variant* f32mfma_variant_table(int* count);
 const Variant* f32fma_variant_table(int* count);
 const Variant* bf16dma_variant_table(int* count);
 const Variant* f32dma_variant_table(int* count);
+const Variant* bf16dma_sweep_variant_table(int* count);
+const Variant* f32dma_sweep_variant_table(int* count);
 
 }  // namespace dg
 
@@ -52,3 +67,11 @@ const Variant* f32dma_variant_table(int* count);
              dg::launch_kernel<KERNEL<CFG, true, true, true>, CFG::THREADS>}            \
         }                                                                               \
     }
+
+// Stream-K entries for a direct-to-LDS kernel template K<Cfg, A_KC, B_KC, ALIGNED, SK>.
+#define DG_SK_TABLE(KERNEL, CFG)                                                    \
+    {{dg::launch_kernel<KERNEL<CFG, false, false, true, true>, CFG::THREADS>,       \
+      dg::launch_kernel<KERNEL<CFG, false, true, true, true>, CFG::THREADS>},       \
+     {dg::launch_kernel<KERNEL<CFG, true, false, true, true>, CFG::THREADS>,        \
+      dg::launch_kernel<KERNEL<CFG, true, true, true, true>, CFG::THREADS>}},       \
+        &dg::occupancy<KERNEL<CFG, true, false, true, true>, CFG::THREADS>

@@ -58,6 +58,7 @@
 #ifndef DENSE_GEMM_H
 #define DENSE_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -129,10 +130,54 @@ gemm_status_t gemm_set_variant(gemm_handle_t h, int id);
 int gemm_last_variant(gemm_handle_t h);
 
 /* The variant automatic selection would use for this problem when A and B
- * are 16-byte aligned with 16-byte-multiple row pitches (pure host logic, no
- * HIP call); -1 for an invalid dtype/transpose. */
+ * are 16-byte aligned with 16-byte-multiple row pitches (host logic; it only
+ * queries the current device's compute-unit count, assuming 256 when no
+ * device answers); -1 for an invalid dtype/transpose. */
 int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB,
                         int64_t M, int64_t N, int64_t K);
+
+/* ---- stream-K (split-K with an even split of the whole iteration space) ----
+ * "GEMM on NVIDIA GPUs: from a naive kernel to a tiled pipeline", section 5:
+ * split-K lets several workers share one output tile's K range, each forming
+ * a partial sum P^(s)_ij over its range K_s, and reduces P_ij = sum_s P^(s)_ij
+ * afterwards; stream-K divides all (tile, K-step) iterations evenly over the
+ * workers at the price of that fix-up.  Its section 6 lists the workspace
+ * limit among the fields that decide a GEMM configuration.
+ *
+ * A handle with a workspace may run a call as stream-K: a grid of about one
+ * workgroup per workgroup slot of the GPU, each taking an equal run of the
+ * iterations; a tile split between workgroups is finished by the one that
+ * reaches its last K-step, which adds the others' partial sums in a fixed
+ * order (results stay bitwise reproducible for a given call, variant and GPU).
+ * Automatic mode uses it only when whole tiles would leave at least a tenth
+ * of the last wave's slots idle.  Only 16-byte-capable direct-to-LDS variants
+ * have stream-K kernels; other calls run data-parallel as before.          */
+
+/* Bytes of workspace that let every stream-K variant run at its full grid on
+ * the current device (a smaller workspace restricts stream-K to the calls it
+ * can hold). */
+size_t gemm_stream_k_workspace_bytes(void);
+
+/* Give h a device workspace: caller-owned memory of `bytes` bytes, 256-byte
+ * aligned, used by h's stream-K calls until replaced or cleared (ws == NULL or
+ * bytes == 0).  Enqueues one small kernel on `stream` that clears the
+ * workspace's flag area; the calls that use it must be ordered after that
+ * kernel.  Layout: 4096 32-bit flags, then one BM*BN fp32 partial-sum slot
+ * per workgroup.  Each stream-K call leaves every flag zero again.  Calls that
+ * share a workspace must not overlap in time (use one handle and workspace
+ * per concurrently used stream).  GEMM_ERR_INVALID_VALUE: NULL handle, a
+ * misaligned pointer or fewer bytes than the flag area; GEMM_ERR_HIP: the
+ * clearing kernel could not be launched. */
+gemm_status_t gemm_set_workspace(gemm_handle_t h, void* ws, size_t bytes, hipStream_t stream);
+
+/* Stream-K policy of h: -1 automatic (default), 0 never, 1 whenever the
+ * variant and the workspace allow (tests use this to exercise the split on
+ * small shapes).  GEMM_ERR_INVALID_VALUE for another mode or a NULL handle. */
+gemm_status_t gemm_set_stream_k(gemm_handle_t h, int mode);
+
+/* Stream-K workgroups used by the last gemm_run on h (0: data-parallel tiles;
+ * -1 for a NULL handle). */
+int gemm_last_stream_k(gemm_handle_t h);
 
 #ifdef __cplusplus
 }

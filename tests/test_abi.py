@@ -143,3 +143,25 @@ def test_binding_shares_one_hip_runtime_with_torch():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
     assert out.returncode == 0, out.stderr
+
+
+def test_stream_k_controls_validate_arguments(h):
+    assert g.gemm_last_stream_k(None) == -1
+    assert g.gemm_last_stream_k(h) == 0
+    for mode in (-1, 0, 1):
+        assert g.gemm_set_stream_k(h, mode) == g.GEMM_OK
+    assert g.gemm_set_stream_k(h, 2) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_set_stream_k(None, 0) == g.GEMM_ERR_INVALID_VALUE
+    # rejected before any HIP call: NULL handle, misaligned pointer, too small
+    assert g.gemm_set_workspace(None, FAKE, 1 << 20, None) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_set_workspace(h, FAKE + 4, 1 << 20, None) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_set_workspace(h, FAKE, 64, None) == g.GEMM_ERR_INVALID_VALUE
+    # clearing the workspace makes no HIP call either
+    assert g.gemm_set_workspace(h, None, 0, None) == g.GEMM_OK
+
+
+def test_stream_k_workspace_size_covers_the_flag_area_and_one_slot_per_workgroup():
+    n = g.gemm_stream_k_workspace_bytes()
+    # 4096 flags, then at least one 256x256 fp32 slot per compute unit
+    assert n >= 4096 * 4 + 256 * 256 * 4
+    assert (n - 4096 * 4) % (128 * 128 * 4) == 0
