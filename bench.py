@@ -163,6 +163,7 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int):
         e1.record()
         torch.cuda.synchronize()
         used = g.gemm_variant_name(g.gemm_last_variant(h))
+        sk = g.gemm_last_stream_k(h)
     finally:
         g.gemm_set_variant(h, -1)
     ms = e0.elapsed_time(e1) / reps
@@ -170,6 +171,7 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int):
     roof = roofline_tflops(w)
     del A, B, C, D
     return {"kernel_ms": round(ms, 4), "tflops": round(tf, 2), "variant": used,
+            "stream_k_workgroups": sk,
             "peak_tflops": PEAK_TFLOPS[w.dtype], "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
             "roofline_tflops": round(roof, 1), "frac_of_roofline": round(tf / roof, 4),
             "workload": w.description}
@@ -288,6 +290,9 @@ def main(argv=None):
     import dense_gemm_11_amd as g
     torch.cuda.set_device(0)
     h = g.gemm_create()
+    # a stream-K workspace (the automatic policy keeps the two step workloads
+    # on whole tiles; it splits the few-tile, long-K extra row)
+    workspace = g.attach_workspace(h)
     parts = [Part(g, h, n, args.sets) for n in STEP_WORKLOADS]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -348,13 +353,33 @@ def main(argv=None):
                 "compulsory_bytes": compulsory_bytes(dom.w)}
 
     # the remaining hot-path rows, timed outside the step: the fp32 vector-FMA
-    # mainloop at 4096^3, and the full alpha/beta epilogue with ragged edges
+    # mainloop at 4096^3, the full alpha/beta epilogue with ragged edges, the
+    # transformer-layer sweep (and one GPU's share of it under an 8-way
+    # split), and a few-tile long-K shape that the stream-K path takes
     extras = {}
     if not args.no_extras:
         extras["fp32_4096_vector_fma"] = time_extra(g, h, "fp32_4096", "f32_vfma_128x128x8_t8x8",
                                                     reps=10, warmup=3)
         extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
                                                        warmup=5)
+        for group, names in (("transformer_layer", ("bf16_qkv", "bf16_outproj", "bf16_mlp_up",
+                                                    "bf16_mlp_down")),
+                             ("transformer_layer_tp8_shard", ("bf16_qkv_tp8", "bf16_outproj_tp8",
+                                                              "bf16_mlp_up_tp8",
+                                                              "bf16_mlp_down_tp8"))):
+            rows = {n: time_extra(g, h, n, None, reps=10, warmup=3) for n in names}
+            fl = sum(workloads.WORKLOADS[n].flops for n in names)
+            t = sum(rows[n]["kernel_ms"] for n in names)
+            extras[group] = {"rows": rows, "aggregate_tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                             "aggregate": "sum of FLOPs / sum of kernel times"}
+        extras["bf16_small_mn_long_k"] = time_extra(g, h, "bf16_small_mn_long_k", None, reps=10,
+                                                    warmup=3)
+        g.gemm_set_stream_k(h, 0)
+        try:
+            whole = time_extra(g, h, "bf16_small_mn_long_k", None, reps=5, warmup=2)
+        finally:
+            g.gemm_set_stream_k(h, -1)
+        extras["bf16_small_mn_long_k"]["whole_tiles_kernel_ms"] = whole["kernel_ms"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -377,7 +402,9 @@ def main(argv=None):
         "parts": report_parts, "extra_rows": extras, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    g.gemm_set_workspace(h, None, 0, None)
     g.gemm_destroy(h)
+    del workspace
     return 0
 
 

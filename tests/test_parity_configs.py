@@ -1,5 +1,6 @@
 """GPU vs oracle at the full sizes of the benchmarked and reported workloads,
-with the automatic kernel selection the benchmark uses.  The 256^3 case is
+with the automatic kernel selection (stream-K workspace attached) the
+benchmark uses.  The 256^3 case is
 checked on every output; the large ones on 64 rows x 64 columns (4096
 outputs) that always include the first and last row and column.
 """
@@ -18,11 +19,16 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(scope="module")
 def handle():
+    """A handle with a stream-K workspace, as the benchmark uses it."""
     require_gpu()
     import dense_gemm_11_amd as g
     h = g.gemm_create()
+    ws = g.attach_workspace(h)
+    torch.cuda.synchronize()
     yield h
+    g.gemm_set_workspace(h, None, 0, None)
     g.gemm_destroy(h)
+    del ws
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))

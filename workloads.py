@@ -81,6 +81,19 @@ WORKLOADS = {
                  description="transformer MLP up X[8192,4096]*W[4096,14336]"),
         Workload("bf16_mlp_down", 7, "bf16", "N", "N", 8192, 4096, 14336, 1.0, 0.0, "n1", "n002",
                  description="transformer MLP down X[8192,14336]*W[14336,4096]"),
+        # one GPU's share of the four layer GEMMs split over 8 GPUs (QKV and MLP
+        # up by output columns, output projection and MLP down by K)
+        Workload("bf16_qkv_tp8", 8, "bf16", "N", "N", 8192, 1536, 4096, 1.0, 0.0, "n1", "n002",
+                 description="QKV projection, one of 8 column shards: 8192x1536x4096"),
+        Workload("bf16_outproj_tp8", 9, "bf16", "N", "N", 8192, 4096, 512, 1.0, 0.0, "n1", "n002",
+                 description="output projection, one of 8 K shards: 8192x4096x512"),
+        Workload("bf16_mlp_up_tp8", 10, "bf16", "N", "N", 8192, 1792, 4096, 1.0, 0.0, "n1", "n002",
+                 description="MLP up, one of 8 column shards: 8192x1792x4096"),
+        Workload("bf16_mlp_down_tp8", 11, "bf16", "N", "N", 8192, 4096, 1792, 1.0, 0.0, "n1", "n002",
+                 description="MLP down, one of 8 K shards: 8192x4096x1792"),
+        # few output tiles, long K: the shape split-K / stream-K is for
+        Workload("bf16_small_mn_long_k", 12, "bf16", "N", "N", 1024, 1024, 32768, 1.0, 0.0, "n1",
+                 "n1", description="few output tiles, long K: 1024x1024x32768"),
     ]
 }
 
