@@ -457,10 +457,27 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
     hipError_t e;
+    // bf16 NN with whole tiles: run as D^T = B^T A^T, which puts the
+    // mn-contiguous operand first (measured on 8192^3, same box: TT layout
+    // 1282 vs NN 1235 TFLOP/s); the transposed-output epilogue writes D.
+    const bool nn_t = sk == 0 && h->forced_variant < 0 && vr.nn_t_fn && aligned && a_kc &&
+                      !b_kc && dma_offsets_fit(vr, false, true, K, ldb, lda, es);
     if (sk > 0) {
         a.sk_flags = static_cast<unsigned*>(h->ws);
         a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
         e = vr.sk_fn[a_kc][b_kc](a, sk, stream);
+    } else if (nn_t) {
+        GemmArgs t = a;
+        t.A = B;
+        t.B = A;
+        t.lda = ldb;
+        t.ldb = lda;
+        t.M = (int)N;
+        t.N = (int)M;
+        t.tiles_m = (int)ceil_div(N, vr.bm);
+        t.tiles_n = (int)ceil_div(M, vr.bn);
+        t.group_m = std::min(t.tiles_m, 4);
+        e = vr.nn_t_fn(t, (int)grid, stream);
     } else {
         e = vr.fn[aligned][a_kc][b_kc](a, (int)grid, stream);
     }

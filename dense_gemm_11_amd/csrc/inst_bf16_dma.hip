@@ -1,5 +1,6 @@
 // bf16 matrix-core variants with direct-to-LDS loads and an S-stage LDS ring:
-// the ones the selector uses, each with a stream-K instantiation.
+// the ones the selector uses, each with a stream-K instantiation and a
+// transposed-output instantiation for NN problems.
 #include "mfma_dma_gemm.hpp"
 #include "variants.hpp"
 
@@ -10,7 +11,8 @@ using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
 
 #define BF16_DMA_SK_VARIANT(NAME, CFG)                                                      \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES,       \
-     DG_FN_TABLE(dma_gemm_kernel, CFG), DG_SK_TABLE(dma_gemm_kernel, CFG)}
+     DG_FN_TABLE(dma_gemm_kernel, CFG), DG_SK_TABLE(dma_gemm_kernel, CFG),                \
+     DG_NN_T_FN(dma_gemm_kernel, CFG)}
 
 const Variant* bf16dma_variant_table(int* count)
 {

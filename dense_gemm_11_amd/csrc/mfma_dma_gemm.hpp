@@ -341,7 +341,12 @@ __device__ __forceinline__ void wait_vm_lgkm0()
 
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false>
+// OUT_T: the kernel computes E = op(A) op(B) for a caller whose D is E
+// transposed (D = op(B)^T op(A)^T with the operands passed swapped): the
+// MFMA operands go in unswapped, so each lane's accumulator group holds four
+// consecutive rows of E at one column, i.e. four adjacent columns of one row
+// of D, and the epilogue still writes 16-byte vectors.
+template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false, bool OUT_T = false>
 __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
@@ -472,7 +477,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 #pragma unroll
             for (int i = 0; i < MF; ++i)
 #pragma unroll
-                for (int j = 0; j < NF; ++j) mfma_step<Cfg::KIND>(fb[cb][j], fa[cb][i], acc[i][j]);
+                for (int j = 0; j < NF; ++j) {
+                    if constexpr (OUT_T) mfma_step<Cfg::KIND>(fa[cb][i], fb[cb][j], acc[i][j]);
+                    else mfma_step<Cfg::KIND>(fb[cb][j], fa[cb][i], acc[i][j]);
+                }
         }
     };
     // Steady-state step with a pinned instruction order: every MFMA of a
@@ -530,7 +538,10 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
             constexpr int nops = NREAD + (mid ? NDMA : 0);
             static_for<NMFMA>([&](auto e_c) __attribute__((always_inline)) {
                 constexpr int e = decltype(e_c)::value;
-                mfma_step<Cfg::KIND>(fb[cb][e % NF], fa[cb][e / NF], acc[e / NF][e % NF]);
+                if constexpr (OUT_T)
+                    mfma_step<Cfg::KIND>(fa[cb][e / NF], fb[cb][e % NF], acc[e / NF][e % NF]);
+                else
+                    mfma_step<Cfg::KIND>(fb[cb][e % NF], fa[cb][e / NF], acc[e / NF][e % NF]);
                 __builtin_amdgcn_sched_barrier(0);
                 // front-load: fragment reads go out over the first half of the
                 // MFMAs (two per MFMA), DMA copies over the rest
@@ -609,13 +620,20 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     const int m0 = tm * BM, n0 = tn * BN;
     const float alpha = p.alpha, beta = p.beta;
     constexpr int VG = Cfg::ACC / 4;
-    auto col_of = [&](int j, int vg) __attribute__((always_inline)) {
-        return n0 + wave_n0 + j * FM + (FM == 32 ? 8 * vg + 4 * (lane >> 5) : 4 * (lane >> 4));
+    // D is M x N, or N x M when the output is transposed
+    const int d_rows = OUT_T ? p.N : p.M, d_cols = OUT_T ? p.M : p.N;
+    // D row of fragment (i, j) for this lane, and the first of the lane's
+    // four adjacent D columns of group vg
+    const int in_frag = FM == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
+    auto d_row = [&](int i, int j) __attribute__((always_inline)) {
+        return OUT_T ? n0 + wave_n0 + j * FM + lane % FM : m0 + wave_m0 + i * FM + lane % FM;
+    };
+    auto d_col = [&](int i, int j, int vg) __attribute__((always_inline)) {
+        return OUT_T ? m0 + wave_m0 + i * FM + 8 * vg + in_frag
+                     : n0 + wave_n0 + j * FM + 8 * vg + in_frag;
     };
     static_for<MF>([&](auto i_c) __attribute__((always_inline)) {
         constexpr int i = decltype(i_c)::value;
-        const int row = m0 + wave_m0 + i * FM + lane % FM;
-        const bool row_ok = row < p.M;
         f32x4 sum[NF][VG];
 #pragma unroll
         for (int j = 0; j < NF; ++j)
@@ -625,20 +643,23 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                                    acc[i][j][4 * vg + 3]};
         f32x4 cv[NF][VG];
         if (beta != 0.0f) {
-            const float* crow = p.C + (int64_t)(row_ok ? row : 0) * p.ldc;
 #pragma unroll
-            for (int j = 0; j < NF; ++j)
+            for (int j = 0; j < NF; ++j) {
+                const int row = d_row(i, j);
+                const bool row_ok = row < d_rows;
+                const float* crow = p.C + (int64_t)(row_ok ? row : 0) * p.ldc;
 #pragma unroll
                 for (int vg = 0; vg < VG; ++vg) {
-                    const int col = col_of(j, vg);
-                    if (row_ok && p.c_vec && col + 4 <= p.N) {
+                    const int col = d_col(i, j, vg);
+                    if (row_ok && p.c_vec && col + 4 <= d_cols) {
                         cv[j][vg] = *reinterpret_cast<const f32x4*>(crow + col);
                     } else {
 #pragma unroll
                         for (int s = 0; s < 4; ++s)
-                            cv[j][vg][s] = (row_ok && col + s < p.N) ? crow[col + s] : 0.0f;
+                            cv[j][vg][s] = (row_ok && col + s < d_cols) ? crow[col + s] : 0.0f;
                     }
                 }
+            }
         }
         if constexpr (SK) {
             for (int64_t c = c0; c < c1; ++c) {
@@ -657,23 +678,25 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                     for (int vg = 0; vg < VG; ++vg) sum[j][vg] += v[j][vg];
             }
         }
-        if (!row_ok) return;
-        float* drow = p.D + (int64_t)row * p.ldd;
 #pragma unroll
-        for (int j = 0; j < NF; ++j)
+        for (int j = 0; j < NF; ++j) {
+            const int row = d_row(i, j);
+            if (row >= d_rows) continue;
+            float* drow = p.D + (int64_t)row * p.ldd;
 #pragma unroll
             for (int vg = 0; vg < VG; ++vg) {
-                const int col = col_of(j, vg);
+                const int col = d_col(i, j, vg);
                 f32x4 out = alpha * sum[j][vg];
                 if (beta != 0.0f) out += beta * cv[j][vg];
-                if (p.d_vec && col + 4 <= p.N) {
+                if (p.d_vec && col + 4 <= d_cols) {
                     *reinterpret_cast<f32x4*>(drow + col) = out;
                 } else {
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        if (col + s < p.N) drow[col + s] = out[s];
+                        if (col + s < d_cols) drow[col + s] = out[s];
                 }
             }
+        }
     });
     };  // epilogue
 

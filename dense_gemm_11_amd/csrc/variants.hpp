@@ -19,6 +19,9 @@ struct Variant {
     LaunchFn fn[2][2][2];  // [wide access][A k-contiguous][B k-contiguous]
     LaunchFn sk_fn[2][2];  // stream-K instantiations (wide access only), or null
     OccFn sk_occ;          // occupancy of the stream-K kernel, or null
+    // NN problems as D^T = B^T A^T: the kernel with A mn-contiguous, B
+    // k-contiguous and a transposed-output epilogue (wide access), or null
+    LaunchFn nn_t_fn;
 };
 
 // Launch through hipLaunchKernel so the launch status is returned directly.
@@ -75,3 +78,6 @@ const Variant* f32dma_sweep_variant_table(int* count);
      {dg::launch_kernel<KERNEL<CFG, true, false, true, true>, CFG::THREADS>,        \
       dg::launch_kernel<KERNEL<CFG, true, true, true, true>, CFG::THREADS>}},       \
         &dg::occupancy<KERNEL<CFG, true, false, true, true>, CFG::THREADS>
+
+// The transposed-output instantiation serving NN problems.
+#define DG_NN_T_FN(KERNEL, CFG) dg::launch_kernel<KERNEL<CFG, false, true, true, false, true>, CFG::THREADS>
