@@ -35,6 +35,9 @@ METRIC = ("GEMM TFLOPS (2MNK/s) FP32 4096³ & BF16→FP32 8192³; "
           "% of MI355X dense peak")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+# fp32 vector ALU without packed FP32 instructions (which this library does not
+# emit): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP per FMA x 2.4 GHz
+VALU_FP32_UNPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 HBM_GBS = 8000.0
 STEP_WORKLOADS = ("fp32_4096", "bf16_8192")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -358,8 +361,12 @@ def main(argv=None):
     # split), and a few-tile long-K shape that the stream-K path takes
     extras = {}
     if not args.no_extras:
-        extras["fp32_4096_vector_fma"] = time_extra(g, h, "fp32_4096", "f32_vfma_128x128x8_t8x8",
-                                                    reps=10, warmup=3)
+        vf = time_extra(g, h, "fp32_4096", "f32_vfma_128x128x8_t8x8", reps=10, warmup=3)
+        vf["roofline"] = {"bound": "alu", "peak": round(VALU_FP32_UNPACKED_TFLOPS, 1),
+                          "unit": "TFLOP/s",
+                          "frac": round(vf["tflops"] / VALU_FP32_UNPACKED_TFLOPS, 4),
+                          "note": "plain v_fma_f32 rate; 157.3 assumes packed FP32 FMA"}
+        extras["fp32_4096_vector_fma"] = vf
         extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
                                                        warmup=5)
         for group, names in (("transformer_layer", ("bf16_qkv", "bf16_outproj", "bf16_mlp_up",
