@@ -43,8 +43,9 @@ STEP_WORKLOADS = ("fp32_4096", "bf16_8192")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def compulsory_bytes(w: workloads.Workload) -> int:
-    """Read A and B once, read C once if beta != 0, write D once.
+def compulsory_bytes(w: workloads.Workload, out_bytes: int = 4) -> int:
+    """Read A and B once, read C once if beta != 0, write D once (C and D of
+    out_bytes per element).
 
     The one-pass traffic of "Understanding Roofline and Tiling through Matrix
     Multiplication", section 8.5 (12 N^2 bytes for square fp32), generalized to
@@ -52,8 +53,8 @@ def compulsory_bytes(w: workloads.Workload) -> int:
     section 2, ideal traffic).
     """
     ea = 4 if w.dtype == "f32" else 2
-    c = 4 * w.M * w.N if w.beta != 0.0 else 0
-    return ea * (w.M * w.K + w.K * w.N) + c + 4 * w.M * w.N
+    c = out_bytes * w.M * w.N if w.beta != 0.0 else 0
+    return ea * (w.M * w.K + w.K * w.N) + c + out_bytes * w.M * w.N
 
 
 def kernel_source_digest() -> str:
@@ -135,19 +136,23 @@ class Part:
         return float(np.mean([a.elapsed_time(b) for a, b in self.events]))
 
 
-def roofline_tflops(w: workloads.Workload) -> float:
+def roofline_tflops(w: workloads.Workload, out_bytes: int = 4) -> float:
     """min(compute peak, HBM bandwidth x compulsory intensity), in TFLOP/s
     ("GEMM on NVIDIA GPUs", section 2, roofline bound)."""
-    return min(PEAK_TFLOPS[w.dtype], HBM_GBS * 1e9 * w.flops / compulsory_bytes(w) / 1e12)
+    return min(PEAK_TFLOPS[w.dtype],
+               HBM_GBS * 1e9 * w.flops / compulsory_bytes(w, out_bytes) / 1e12)
 
 
-def time_extra(g, h, name: str, variant_name, reps: int, warmup: int):
-    """Time one workload outside the step (own buffers, HIP events)."""
+def time_extra(g, h, name: str, variant_name, reps: int, warmup: int,
+               out_dtype=torch.float32):
+    """Time one workload outside the step (own buffers, HIP events).
+
+    out_dtype=torch.bfloat16 runs a bf16 workload with bf16 C and D."""
     w = workloads.WORKLOADS[name]
     A, B, C = workloads.make_inputs(w)
     A, B = A.cuda(), B.cuda()
-    C = None if C is None else C.cuda()
-    D = torch.empty(w.M, w.N, dtype=torch.float32, device="cuda")
+    C = None if C is None else C.to("cuda", out_dtype)
+    D = torch.empty(w.M, w.N, dtype=out_dtype, device="cuda")
     vid = -1
     if variant_name is not None:
         vid = [i for i, n, _, _ in g.variants() if n == variant_name][0]
@@ -155,8 +160,15 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int):
     try:
         run = lambda: g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
                                     alpha=w.alpha, beta=w.beta)
-        for _ in range(warmup):
+        # at least `warmup` calls and ~50 ms of them: clocks that dropped
+        # while the GPU idled take tens of milliseconds to come back
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t0 < 0.05:
             run()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -171,13 +183,14 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int):
         g.gemm_set_variant(h, -1)
     ms = e0.elapsed_time(e1) / reps
     tf = w.flops / (ms * 1e-3) / 1e12
-    roof = roofline_tflops(w)
+    roof = roofline_tflops(w, 2 if out_dtype == torch.bfloat16 else 4)
     del A, B, C, D
     return {"kernel_ms": round(ms, 4), "tflops": round(tf, 2), "variant": used,
             "stream_k_workgroups": sk,
             "peak_tflops": PEAK_TFLOPS[w.dtype], "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
             "roofline_tflops": round(roof, 1), "frac_of_roofline": round(tf / roof, 4),
-            "workload": w.description}
+            "workload": (w.description.replace("FP32 accumulate/output", "FP32 accumulate, BF16 C/D")
+                         if out_dtype == torch.bfloat16 else w.description)}
 
 
 def oracle_sample_rate(part: Part, cores: int, budget_s: float):
@@ -357,6 +370,7 @@ def main(argv=None):
 
     # the remaining hot-path rows, timed outside the step: the fp32 vector-FMA
     # mainloop at 4096^3, the full alpha/beta epilogue with ragged edges, the
+    # bf16-output epilogue at 8192^3, the
     # transformer-layer sweep (and one GPU's share of it under an 8-way
     # split), and a few-tile long-K shape that the stream-K path takes
     extras = {}
@@ -369,6 +383,8 @@ def main(argv=None):
         extras["fp32_4096_vector_fma"] = vf
         extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
                                                        warmup=5)
+        extras["bf16_8192_bf16_output"] = time_extra(g, h, "bf16_8192", None, reps=10, warmup=3,
+                                                     out_dtype=torch.bfloat16)
         for group, names in (("transformer_layer", ("bf16_qkv", "bf16_outproj", "bf16_mlp_up",
                                                     "bf16_mlp_down")),
                              ("transformer_layer_tp8_shard", ("bf16_qkv_tp8", "bf16_outproj_tp8",

@@ -27,6 +27,7 @@ GEMM_OP_N = 0
 GEMM_OP_T = 1
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16_F32 = 1
+GEMM_DTYPE_BF16_BF16 = 2
 GEMM_OK = 0
 GEMM_ERR_INVALID_VALUE = 1
 GEMM_ERR_NOT_SUPPORTED = 2
@@ -209,7 +210,9 @@ def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
     """gemm_run on torch tensors (row-major 2-D views with unit column stride).
 
     A: op(A) is M x K (A stored M x K for "N", K x M for "T"); B likewise;
-    C, D: M x N float32.  A and B are float32 (fp32 GEMM) or bfloat16.
+    C, D: M x N.  A and B are float32 (fp32 GEMM) or bfloat16; with bfloat16
+    operands, C and D are float32 (GEMM_DTYPE_BF16_F32) or both bfloat16
+    (GEMM_DTYPE_BF16_BF16).
     """
     import torch
 
@@ -221,11 +224,12 @@ def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
     if A.dtype == torch.float32 and B.dtype == torch.float32:
         dtype = GEMM_DTYPE_F32
     elif A.dtype == torch.bfloat16 and B.dtype == torch.bfloat16:
-        dtype = GEMM_DTYPE_BF16_F32
+        dtype = GEMM_DTYPE_BF16_BF16 if D.dtype == torch.bfloat16 else GEMM_DTYPE_BF16_F32
     else:
         raise TypeError("A and B must both be float32 or both bfloat16")
-    if D.dtype != torch.float32 or (C is not None and C.dtype != torch.float32):
-        raise TypeError("C and D must be float32")
+    out = torch.bfloat16 if dtype == GEMM_DTYPE_BF16_BF16 else torch.float32
+    if D.dtype != out or (C is not None and C.dtype != out):
+        raise TypeError("C and D must be float32, or both bfloat16 with bfloat16 operands")
     M, K = (A.shape[0], A.shape[1]) if transA == "N" else (A.shape[1], A.shape[0])
     Kb, N = (B.shape[0], B.shape[1]) if transB == "N" else (B.shape[1], B.shape[0])
     if Kb != K or tuple(D.shape) != (M, N) or (C is not None and tuple(C.shape) != (M, N)):

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdense_gemm.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "inst_bf16.hip", "inst_bf16_dma.hip", "inst_bf16_dma_sweep.hip",
+SOURCES = ["api.hip", "inst_bf16.hip", "inst_bf16_dma.hip", "inst_bf16_dma_out.hip",
+           "inst_bf16_dma_sweep.hip",
            "inst_f32_mfma.hip", "inst_f32_dma.hip", "inst_f32_dma_sweep.hip", "inst_f32_fma.hip"]
 
 

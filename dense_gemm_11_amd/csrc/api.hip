@@ -23,13 +23,17 @@ struct gemm_handle_s {
 namespace dg {
 
 // D = beta * C (or 0 when beta == 0): the whole result when K == 0 or alpha == 0.
+template <typename OutT>
 __global__ __launch_bounds__(256) void scale_c_kernel(GemmArgs p)
 {
     const int64_t total = (int64_t)p.M * p.N;
+    const OutT* C = reinterpret_cast<const OutT*>(p.C);
+    OutT* D = reinterpret_cast<OutT*>(p.D);
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * 256) {
         const int64_t row = e / p.N, col = e % p.N;
-        p.D[row * p.ldd + col] = (p.beta != 0.0f) ? p.beta * p.C[row * p.ldc + col] : 0.0f;
+        D[row * p.ldd + col] =
+            from_f32<OutT>((p.beta != 0.0f) ? p.beta * to_f32(C[row * p.ldc + col]) : 0.0f);
     }
 }
 
@@ -343,23 +347,27 @@ gemm_status_t gemm_set_stream_k(gemm_handle_t h, int mode)
 int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, int64_t M,
                         int64_t N, int64_t K)
 {
-    if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32) ||
+    if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32 && dtype != GEMM_DTYPE_BF16_BF16) ||
         (transA != GEMM_OP_N && transA != GEMM_OP_T) || (transB != GEMM_OP_N && transB != GEMM_OP_T))
         return -1;
-    return dg::select_variant(dtype, M, N, K, true);
+    return dg::select_variant(dtype == GEMM_DTYPE_F32 ? GEMM_DTYPE_F32 : GEMM_DTYPE_BF16_F32, M, N,
+                              K, true);
 }
 
 gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M, int64_t N,
                        int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
-                       float beta, const float* C, int64_t ldc, float* D, int64_t ldd,
+                       float beta, const void* C, int64_t ldc, void* D, int64_t ldd,
                        gemm_dtype_t dtype, hipStream_t stream)
 {
     using namespace dg;
     if (!h) return GEMM_ERR_INVALID_VALUE;
     if ((transA != GEMM_OP_N && transA != GEMM_OP_T) || (transB != GEMM_OP_N && transB != GEMM_OP_T))
         return GEMM_ERR_INVALID_VALUE;
-    if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32) return GEMM_ERR_INVALID_VALUE;
+    if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32 && dtype != GEMM_DTYPE_BF16_BF16)
+        return GEMM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+    const bool out_bf16 = dtype == GEMM_DTYPE_BF16_BF16;
+    const int64_t es_out = out_bf16 ? 2 : 4;  // bytes per element of C and D
     const int64_t one = 1;
     const int64_t min_lda = transA == GEMM_OP_N ? std::max(one, K) : std::max(one, M);
     const int64_t min_ldb = transB == GEMM_OP_N ? std::max(one, N) : std::max(one, K);
@@ -377,7 +385,7 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
         ldd > INT_MAX || (beta != 0.0f && ldc > INT_MAX))
         return GEMM_ERR_NOT_SUPPORTED;
     if (beta != 0.0f) {
-        const int64_t span_c = ((M - 1) * ldc + N) * 4, span_d = ((M - 1) * ldd + N) * 4;
+        const int64_t span_c = ((M - 1) * ldc + N) * es_out, span_d = ((M - 1) * ldd + N) * es_out;
         if (static_cast<const void*>(C) == static_cast<const void*>(D)) {
             if (ldc != ldd) return GEMM_ERR_INVALID_VALUE;
         } else if (ranges_overlap(C, span_c, D, span_d)) {
@@ -388,8 +396,8 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     GemmArgs a;
     a.A = A;
     a.B = B;
-    a.C = beta != 0.0f ? C : nullptr;
-    a.D = D;
+    a.C = beta != 0.0f ? static_cast<const float*>(C) : nullptr;  // element type per dtype
+    a.D = static_cast<float*>(D);
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = beta != 0.0f ? ldc : 0;
@@ -401,43 +409,52 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     a.beta = beta;
     // 16-byte accesses need only element alignment: the memory system serves
     // unaligned vector loads and stores whole
-    a.c_vec = beta != 0.0f && aligned_to(C, 4);
-    a.d_vec = aligned_to(D, 4);
+    a.c_vec = beta != 0.0f && aligned_to(C, es_out);
+    a.d_vec = aligned_to(D, es_out);
     a.sk_partials = nullptr;
     a.sk_flags = nullptr;
 
     if (!reads_ab) {
         const int64_t blocks = std::min<int64_t>(ceil_div(M * N, 256), 65536);
         void* args[] = {&a};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&scale_c_kernel),
-                                       dim3((unsigned)blocks), dim3(256), args, 0, stream);
+        const void* k = out_bf16 ? reinterpret_cast<const void*>(&scale_c_kernel<bf16_t>)
+                                 : reinterpret_cast<const void*>(&scale_c_kernel<float>);
+        hipError_t e = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), args, 0, stream);
         return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     }
 
     const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    // operand precision: the variants are keyed by it (bf16 operands serve
+    // both bf16 dtypes)
+    const int op_dtype = dtype == GEMM_DTYPE_F32 ? GEMM_DTYPE_F32 : GEMM_DTYPE_BF16_F32;
     const bool a_kc = transA == GEMM_OP_N, b_kc = transB == GEMM_OP_T;
     // wide (16-byte) operand access needs element-aligned A and B only
     const bool wide = aligned_to(A, es) && aligned_to(B, es);
     int id = h->forced_variant;
     if (id < 0) {
-        const Variant& big = table()[select_variant(dtype, M, N, K, true)];
-        id = select_variant(dtype, M, N, K, wide && dma_offsets_fit(big, a_kc, b_kc, K, lda, ldb, es));
+        const Variant& big = table()[select_variant(op_dtype, M, N, K, true)];
+        id = select_variant(op_dtype, M, N, K,
+                            wide && dma_offsets_fit(big, a_kc, b_kc, K, lda, ldb, es));
     }
     const Variant& v = table()[id];
-    if (v.dtype != (int)dtype) return GEMM_ERR_NOT_SUPPORTED;
+    if (v.dtype != op_dtype) return GEMM_ERR_NOT_SUPPORTED;
+    // bf16 C/D: only the selected direct-to-LDS variants carry that epilogue,
+    // for element-aligned operands whose panel offsets fit in 32 bits
+    if (out_bf16 && !v.bo_nn_t_fn) return GEMM_ERR_NOT_SUPPORTED;
     // a direct-to-LDS kernel whose offsets would overflow stages every step
     // through registers instead (its ALIGNED == false instantiation)
     const bool aligned =
         wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, a_kc, b_kc, K, lda, ldb, es));
     const double dp_us = data_parallel_us(v, M, N, K);
     double sk_us = 0.0;
-    int sk = (aligned && v.kind == KIND_MFMA_DMA)
+    int sk = (aligned && v.kind == KIND_MFMA_DMA && !out_bf16)
                  ? stream_k_grid(v, M, N, K, h->stream_k_mode, h->ws_bytes, dp_us, &sk_us)
                  : 0;
-    if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0) {
+    if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0 &&
+        !out_bf16) {
         // With a workspace, stream-K on the other tile size competes too; the
         // lowest estimate wins.
-        const int other = dma_variant(dtype, v.bm < 256);
+        const int other = dma_variant(op_dtype, v.bm < 256);
         if (other != id && dma_offsets_fit(table()[other], a_kc, b_kc, K, lda, ldb, es)) {
             double o_us = 0.0;
             const int sk_o = stream_k_grid(table()[other], M, N, K, h->stream_k_mode, h->ws_bytes,
@@ -462,6 +479,7 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     // 1282 vs NN 1235 TFLOP/s); the transposed-output epilogue writes D.
     const bool nn_t = sk == 0 && h->forced_variant < 0 && vr.nn_t_fn && aligned && a_kc &&
                       !b_kc && dma_offsets_fit(vr, false, true, K, ldb, lda, es);
+    if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
     if (sk > 0) {
         a.sk_flags = static_cast<unsigned*>(h->ws);
         a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
@@ -477,9 +495,9 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
         t.tiles_m = (int)ceil_div(N, vr.bm);
         t.tiles_n = (int)ceil_div(M, vr.bn);
         t.group_m = std::min(t.tiles_m, 4);
-        e = vr.nn_t_fn(t, (int)grid, stream);
+        e = (out_bf16 ? vr.bo_nn_t_fn : vr.nn_t_fn)(t, (int)grid, stream);
     } else {
-        e = vr.fn[aligned][a_kc][b_kc](a, (int)grid, stream);
+        e = (out_bf16 ? vr.bo_fn : vr.fn)[aligned][a_kc][b_kc](a, (int)grid, stream);
     }
     if (e != hipSuccess) return GEMM_ERR_HIP;
     h->last_variant = id;

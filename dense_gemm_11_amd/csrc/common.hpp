@@ -23,6 +23,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 // Everything a kernel needs for one GEMM call (passed by value as kernarg).
 struct GemmArgs {
@@ -92,6 +94,17 @@ template <>
 __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x)
 {
     return __uint_as_float(((uint32_t)x) << 16);
+}
+
+// fp32 -> element type of C/D (bf16: round to nearest even)
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
+{
+    return __builtin_bit_cast(bf16_t, (__bf16)x);
 }
 
 }  // namespace dg

@@ -9,10 +9,17 @@ namespace dg {
 using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
 using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
 
+#define bf16_out_table(BM)                                                                   \
+    {{{bf16_out_fns(BM).fn[0][0][0], bf16_out_fns(BM).fn[0][0][1]},                         \
+      {bf16_out_fns(BM).fn[0][1][0], bf16_out_fns(BM).fn[0][1][1]}},                        \
+     {{bf16_out_fns(BM).fn[1][0][0], bf16_out_fns(BM).fn[1][0][1]},                         \
+      {bf16_out_fns(BM).fn[1][1][0], bf16_out_fns(BM).fn[1][1][1]}}},                       \
+        bf16_out_fns(BM).nn_t
+
 #define BF16_DMA_SK_VARIANT(NAME, CFG)                                                      \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES,       \
      DG_FN_TABLE(dma_gemm_kernel, CFG), DG_SK_TABLE(dma_gemm_kernel, CFG),                \
-     DG_NN_T_FN(dma_gemm_kernel, CFG)}
+     DG_NN_T_FN(dma_gemm_kernel, CFG), bf16_out_table(CFG::BM)}
 
 const Variant* bf16dma_variant_table(int* count)
 {

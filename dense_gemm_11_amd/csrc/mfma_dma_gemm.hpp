@@ -346,7 +346,11 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // MFMA operands go in unswapped, so each lane's accumulator group holds four
 // consecutive rows of E at one column, i.e. four adjacent columns of one row
 // of D, and the epilogue still writes 16-byte vectors.
-template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false, bool OUT_T = false>
+//
+// OUT_BF16: C and D are bfloat16; alpha*acc + beta*C is formed in fp32 and
+// rounded once to bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false, bool OUT_T = false,
+          bool OUT_BF16 = false>
 __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
@@ -610,6 +614,21 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                                                  0x00020000);
     };
 
+    // C and D element type, and 4-element vector access to them
+    using OutT = std::conditional_t<OUT_BF16, bf16_t, float>;
+    auto load4 = [](const OutT* q) __attribute__((always_inline)) -> f32x4 {
+        if constexpr (OUT_BF16) {
+            const u16x4 h = *reinterpret_cast<const u16x4*>(q);
+            return f32x4{to_f32(h[0]), to_f32(h[1]), to_f32(h[2]), to_f32(h[3])};
+        } else {
+            return *reinterpret_cast<const f32x4*>(q);
+        }
+    };
+    auto store4 = [](OutT* q, f32x4 v) __attribute__((always_inline)) {
+        if constexpr (OUT_BF16) *reinterpret_cast<bf16x4*>(q) = __builtin_convertvector(v, bf16x4);
+        else *reinterpret_cast<f32x4*>(q) = v;
+    };
+
     // ---- epilogue: lane holds 4 adjacent columns of one row per accumulator
     // group.  One fragment row at a time: every load the row needs (beta*C,
     // and a stream-K finisher's contributors' partial sums, added in
@@ -647,16 +666,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
             for (int j = 0; j < NF; ++j) {
                 const int row = d_row(i, j);
                 const bool row_ok = row < d_rows;
-                const float* crow = p.C + (int64_t)(row_ok ? row : 0) * p.ldc;
+                const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)(row_ok ? row : 0) * p.ldc;
 #pragma unroll
                 for (int vg = 0; vg < VG; ++vg) {
                     const int col = d_col(i, j, vg);
                     if (row_ok && p.c_vec && col + 4 <= d_cols) {
-                        cv[j][vg] = *reinterpret_cast<const f32x4*>(crow + col);
+                        cv[j][vg] = load4(crow + col);
                     } else {
 #pragma unroll
                         for (int s = 0; s < 4; ++s)
-                            cv[j][vg][s] = (row_ok && col + s < d_cols) ? crow[col + s] : 0.0f;
+                            cv[j][vg][s] = (row_ok && col + s < d_cols) ? to_f32(crow[col + s]) : 0.0f;
                     }
                 }
             }
@@ -682,18 +701,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         for (int j = 0; j < NF; ++j) {
             const int row = d_row(i, j);
             if (row >= d_rows) continue;
-            float* drow = p.D + (int64_t)row * p.ldd;
+            OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
 #pragma unroll
             for (int vg = 0; vg < VG; ++vg) {
                 const int col = d_col(i, j, vg);
                 f32x4 out = alpha * sum[j][vg];
                 if (beta != 0.0f) out += beta * cv[j][vg];
                 if (p.d_vec && col + 4 <= d_cols) {
-                    *reinterpret_cast<f32x4*>(drow + col) = out;
+                    store4(drow + col, out);
                 } else {
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        if (col + s < d_cols) drow[col + s] = out[s];
+                        if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
                 }
             }
         }

@@ -22,6 +22,9 @@ struct Variant {
     // NN problems as D^T = B^T A^T: the kernel with A mn-contiguous, B
     // k-contiguous and a transposed-output epilogue (wide access), or null
     LaunchFn nn_t_fn;
+    // bf16 C and D (GEMM_DTYPE_BF16_BF16): the same three launch kinds, or null
+    LaunchFn bo_fn[2][2][2];
+    LaunchFn bo_nn_t_fn;
 };
 
 // Launch through hipLaunchKernel so the launch status is returned directly.
@@ -43,6 +46,14 @@ int occupancy()
         return 0;
     return n;
 }
+
+// bf16-output launch functions of the selected bf16 direct-to-LDS variant
+// with BM x BM tiles (BM = 256 or 128).
+struct Bf16OutFns {
+    LaunchFn fn[2][2][2];
+    LaunchFn nn_t;
+};
+const Bf16OutFns& bf16_out_fns(int bm);
 
 // Table fragments, one per instantiation file (host functions returning a
 // static array, so the device compile never sees host function pointers).
@@ -81,3 +92,16 @@ const Variant* f32dma_sweep_variant_table(int* count);
 
 // The transposed-output instantiation serving NN problems.
 #define DG_NN_T_FN(KERNEL, CFG) dg::launch_kernel<KERNEL<CFG, false, true, true, false, true>, CFG::THREADS>
+
+// bf16-output instantiations: [wide access][A k-contiguous][B k-contiguous],
+// then the transposed-output one for NN.
+#define DG_BO_TABLE(KERNEL, CFG)                                                                     \
+    {{{dg::launch_kernel<KERNEL<CFG, false, false, false, false, false, true>, CFG::THREADS>,     \
+       dg::launch_kernel<KERNEL<CFG, false, true, false, false, false, true>, CFG::THREADS>},     \
+      {dg::launch_kernel<KERNEL<CFG, true, false, false, false, false, true>, CFG::THREADS>,      \
+       dg::launch_kernel<KERNEL<CFG, true, true, false, false, false, true>, CFG::THREADS>}},     \
+     {{dg::launch_kernel<KERNEL<CFG, false, false, true, false, false, true>, CFG::THREADS>,      \
+       dg::launch_kernel<KERNEL<CFG, false, true, true, false, false, true>, CFG::THREADS>},      \
+      {dg::launch_kernel<KERNEL<CFG, true, false, true, false, false, true>, CFG::THREADS>,       \
+       dg::launch_kernel<KERNEL<CFG, true, true, true, false, false, true>, CFG::THREADS>}}},     \
+        dg::launch_kernel<KERNEL<CFG, false, true, true, false, true, true>, CFG::THREADS>

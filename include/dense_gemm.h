@@ -12,8 +12,15 @@
  * (alpha/beta work excluded, as in that section).
  *
  * Precisions (input / accumulate / output, the triple named in its section 5):
- *   GEMM_DTYPE_F32      : A, B fp32 / fp32 / C, D fp32
- *   GEMM_DTYPE_BF16_F32 : A, B bfloat16 (raw 16-bit patterns) / fp32 / C, D fp32
+ *   GEMM_DTYPE_F32       : A, B fp32 / fp32 / C, D fp32
+ *   GEMM_DTYPE_BF16_F32  : A, B bfloat16 (raw 16-bit patterns) / fp32 / C, D fp32
+ *   GEMM_DTYPE_BF16_BF16 : A, B bfloat16 / fp32 / C, D bfloat16 — the section's
+ *                          example triple; alpha*acc + beta*C is formed in fp32
+ *                          and rounded once to bfloat16 (nearest even).  Needs
+ *                          element-aligned operands whose panels the
+ *                          direct-to-LDS kernels can address (every leading
+ *                          dimension below 2^31 / 256 elements is), else
+ *                          GEMM_ERR_NOT_SUPPORTED; never runs as stream-K.
  * The order in which the K products are summed is not specified; results are
  * bitwise reproducible run to run for the same call and kernel variant.
  *
@@ -71,8 +78,9 @@ typedef struct gemm_handle_s* gemm_handle_t;
 typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
 
 typedef enum {
-    GEMM_DTYPE_F32 = 0,      /* A, B fp32; C, D fp32; fp32 accumulate */
-    GEMM_DTYPE_BF16_F32 = 1  /* A, B bf16; C, D fp32; fp32 accumulate */
+    GEMM_DTYPE_F32 = 0,       /* A, B fp32; C, D fp32; fp32 accumulate */
+    GEMM_DTYPE_BF16_F32 = 1,  /* A, B bf16; C, D fp32; fp32 accumulate */
+    GEMM_DTYPE_BF16_BF16 = 2  /* A, B bf16; C, D bf16; fp32 accumulate */
 } gemm_dtype_t;
 
 typedef enum {
@@ -92,12 +100,13 @@ gemm_status_t gemm_destroy(gemm_handle_t h);
 
 /* D = alpha*op(A)*op(B) + beta*C, enqueued on `stream`.  See the header
  * comment for layouts, degenerate cases and errors.  A and B point to float
- * (GEMM_DTYPE_F32) or to 16-bit bfloat16 patterns (GEMM_DTYPE_BF16_F32). */
+ * (GEMM_DTYPE_F32) or to 16-bit bfloat16 patterns (both bf16 dtypes); C and D
+ * point to float, or to bfloat16 patterns for GEMM_DTYPE_BF16_BF16. */
 gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB,
                        int64_t M, int64_t N, int64_t K, float alpha,
                        const void* A, int64_t lda, const void* B, int64_t ldb,
-                       float beta, const float* C, int64_t ldc,
-                       float* D, int64_t ldd, gemm_dtype_t dtype, hipStream_t stream);
+                       float beta, const void* C, int64_t ldc,
+                       void* D, int64_t ldd, gemm_dtype_t dtype, hipStream_t stream);
 
 /* Static, human-readable text for a status code ("unknown status" otherwise). */
 const char* gemm_status_string(gemm_status_t s);

@@ -153,5 +153,31 @@ def max_relative_error(D, val, den) -> float:
     return float(e.max()) if e.size else 0.0
 
 
+# bf16 output (A, B bf16; C, D bf16; fp32 accumulation): D is the fp32 result r
+# rounded once to bfloat16, nearest even.  With |r - d| <= e = 1e-5 * den (the
+# fp32 accumulation allowance, as for fp32 GEMMs) and |D - r| <= 2^-8 |r| (half
+# a bf16 ulp), |D - d| <= 2^-8 |d| + (1 + 2^-8) e.
+BF16_OUTPUT_ROUNDING = 2.0 ** -8
+BF16_OUTPUT_ACCUMULATION = 1e-5
+
+
+def bf16_output_errors(D: np.ndarray, val: np.ndarray, den: np.ndarray) -> np.ndarray:
+    """Per-element |D - d| / (2^-8 |d| + (1 + 2^-8) 1e-5 den); passing means
+    <= 1.  A zero bound demands exact equality; non-finite D fails (inf)."""
+    D = np.asarray(D, dtype=np.float64)
+    diff = np.abs(D - val)
+    bound = (BF16_OUTPUT_ROUNDING * np.abs(val)
+             + (1.0 + BF16_OUTPUT_ROUNDING) * BF16_OUTPUT_ACCUMULATION * den)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err = np.where(bound > 0, diff / np.where(bound > 0, bound, 1.0),
+                       np.where(diff == 0, 0.0, np.inf))
+    return np.where(np.isfinite(D), err, np.inf)
+
+
+def max_bf16_output_error(D, val, den) -> float:
+    e = bf16_output_errors(D, val, den)
+    return float(e.max()) if e.size else 0.0
+
+
 def max_threads() -> int:
     return int(_get().oracle_max_threads())

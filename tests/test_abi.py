@@ -62,7 +62,8 @@ def run(h, **kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(transA=2), dict(transB=-1), dict(dtype=2), dict(M=-1), dict(N=-3), dict(K=-1),
+    dict(transA=2), dict(transB=-1), dict(dtype=3), dict(dtype=-1), dict(M=-1), dict(N=-3),
+    dict(K=-1),
     dict(lda=5), dict(transA=1, lda=3), dict(ldb=4), dict(transB=1, ldb=5), dict(ldd=4),
     dict(beta=1.0, C=FAKE, ldc=4), dict(D=None), dict(beta=0.5, C=None), dict(A=None),
     dict(B=None), dict(beta=1.0, C=FAKE, ldc=6, D=FAKE, ldd=5),          # C == D, ldc != ldd
@@ -165,3 +166,13 @@ def test_stream_k_workspace_size_covers_the_flag_area_and_one_slot_per_workgroup
     # 4096 flags, then at least one 256x256 fp32 slot per compute unit
     assert n >= 4096 * 4 + 256 * 256 * 4
     assert (n - 4096 * 4) % (128 * 128 * 4) == 0
+
+
+def test_bf16_output_dtype_validates_with_2_byte_elements(h):
+    # C and D overlap checks count 2-byte elements for GEMM_DTYPE_BF16_BF16:
+    # D 4 bytes after C overlaps (4 < 5*2); D 100 bytes after C does not
+    kw = dict(dtype=g.GEMM_DTYPE_BF16_BF16, beta=1.0, C=FAKE, ldc=5, ldd=5, M=4, N=5)
+    assert run(h, D=FAKE + 4, **kw) == g.GEMM_ERR_INVALID_VALUE
+    assert run(h, dtype=g.GEMM_DTYPE_BF16_BF16, M=0) == g.GEMM_OK
+    assert g.gemm_select_variant(g.GEMM_DTYPE_BF16_BF16, 0, 0, 8192, 8192, 8192) == \
+        g.gemm_select_variant(g.GEMM_DTYPE_BF16_F32, 0, 0, 8192, 8192, 8192)

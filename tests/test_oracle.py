@@ -172,6 +172,29 @@ def test_relative_error_metric():
     assert oracle.TOLERANCE == {"f32": 1e-5, "bf16": 1e-2}
 
 
+def test_bf16_output_metric():
+    """Rounding an exact result once to bf16 (nearest even, as torch rounds)
+    passes; a result one bf16 ulp off, or rounded toward zero where that moves
+    it by more than half an ulp, fails; zero bounds demand equality."""
+    import torch
+    rng = np.random.default_rng(7)
+    val = rng.standard_normal(20000) * 10.0 ** rng.integers(-3, 4, 20000)
+    den = np.abs(val) * 0.0           # no accumulation allowance: rounding only
+    rne = torch.from_numpy(val).to(torch.float32).to(torch.bfloat16).double().numpy()
+    assert oracle.max_bf16_output_error(rne, val, den) <= 1.0
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(rne))) - 7)
+    assert oracle.max_bf16_output_error(rne + ulp, val, den) > 1.0
+    # truncation (round toward zero) is off by more than half an ulp somewhere
+    bits = torch.from_numpy(val).to(torch.float32).view(torch.int32)
+    trunc = (bits & ~0xFFFF).view(torch.float32).double().numpy()
+    assert oracle.max_bf16_output_error(trunc, val, den) > 1.0
+    e = oracle.bf16_output_errors(np.array([0.0, 1e-30, np.nan]), np.zeros(3), np.zeros(3))
+    assert e[0] == 0.0 and np.isinf(e[1]) and np.isinf(e[2])
+    # the accumulation allowance: 1e-5 of the denominator on top of rounding
+    assert oracle.max_bf16_output_error(np.array([1e-5]), np.array([0.0]), np.array([1.0])) < 1.0
+    assert oracle.max_bf16_output_error(np.array([2e-5]), np.array([0.0]), np.array([1.0])) > 1.0
+
+
 # -- planted mistakes: each must be caught by at least one pin ------------------
 
 MUTANTS = {
