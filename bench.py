@@ -35,9 +35,12 @@ METRIC = ("GEMM TFLOPS (2MNK/s) FP32 4096³ & BF16→FP32 8192³; "
           "% of MI355X dense peak")
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
-# fp32 vector ALU without packed FP32 instructions (which this library does not
-# emit): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP per FMA x 2.4 GHz
-VALU_FP32_UNPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# fp32 vector ALU: 256 CUs x 256 FLOP per clock x 2.4 GHz = the published
+# 157.3 TFLOP/s.  gfx950 reaches it without packed FP32 instructions (which
+# this library does not emit): the two-operand v_fmac_f32 encoding issues at
+# 2 FMAs per lane per clock (measured 222-226 FLOP/clock/CU), the
+# three-operand v_fma_f32 at 1.
+VALU_FP32_TFLOPS = 256 * 256 * 2.4e9 / 1e12
 HBM_GBS = 8000.0
 STEP_WORKLOADS = ("fp32_4096", "bf16_8192")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -132,8 +135,41 @@ class Part:
             e1.record()
             self.events.append((e0, e1))
 
+    def times_ms(self):
+        return np.array([a.elapsed_time(b) for a, b in self.events])
+
     def kernel_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.events]))
+        return float(np.mean(self.times_ms()))
+
+    def hot_cache_ms(self, stream_handle, reps: int = 20):
+        """Mean launch time on one buffer set (operands stay in L2/MALL as far
+        as they fit): the secondary, hot-cache number."""
+        A, B, C, D = self.sets[0]
+        w = self.w
+        run = lambda: self.g.run_tensors(self.h, A, B, D, C=C, transA=w.transA,
+                                         transB=w.transB, alpha=w.alpha, beta=w.beta,
+                                         stream=stream_handle)
+        for _ in range(3):
+            run()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+
+MALL_BYTES = 256 << 20
+
+
+def sets_needed(w: workloads.Workload) -> int:
+    """Buffer sets whose total exceeds twice the 256 MiB MALL, so a launch
+    finds none of its operands left in the cache by the previous one."""
+    ea = 4 if w.dtype == "f32" else 2
+    one = ea * (w.M * w.K + w.K * w.N) + 4 * w.M * w.N * (2 if w.beta != 0.0 else 1)
+    return 2 * MALL_BYTES // one + 1
 
 
 def roofline_tflops(w: workloads.Workload, out_bytes: int = 4) -> float:
@@ -217,7 +253,35 @@ def oracle_sample_rate(part: Part, cores: int, budget_s: float):
         t = run(n)
     n = int(min(n * budget_s / max(t, 1e-6), 16_000_000))
     t = run(n)
-    return {"outputs": n, "seconds": t, "tflops": 2.0 * w.K * n / t / 1e12}
+    per = t / n
+    rec = {"outputs": n, "seconds": t, "tflops": 2.0 * w.K * n / t / 1e12,
+           "us_per_output": per * 1e6, "extrapolated_full_gemm_s": per * w.M * w.N}
+    # the same with one thread, on a smaller sample (about a second)
+    n1 = max(64, min(n, int(1.0 / max(per * cores, 1e-9))))
+    ii = rng.integers(0, w.M, size=n1)
+    jj = rng.integers(0, w.N, size=n1)
+    t0 = time.perf_counter()
+    oracle.gemm_points(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A_np, A.shape[1], B_np,
+                       B.shape[1], w.beta, C_np, w.N, ii, jj, nthreads=1)
+    t1 = time.perf_counter() - t0
+    rec["one_thread"] = {"outputs": n1, "seconds": t1, "tflops": 2.0 * w.K * n1 / t1 / 1e12}
+    return rec
+
+
+def oracle_full_small(cores: int):
+    """Whole-output oracle wall time on the 256^3 fp32 workload."""
+    import oracle
+    w = workloads.WORKLOADS["fp32_256"]
+    A, B, C = workloads.make_inputs(w)
+    A_np, B_np = workloads.as_numpy_operand(A), workloads.as_numpy_operand(B)
+    out = {}
+    for nt in (cores, 1):
+        t0 = time.perf_counter()
+        oracle.gemm_full(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A_np, A.shape[1], B_np,
+                         B.shape[1], w.beta, None, w.N, nthreads=nt)
+        t = time.perf_counter() - t0
+        out[f"threads_{nt}"] = {"seconds": t, "gflops": w.flops / t / 1e9}
+    return out
 
 
 PMC_COMMANDS = {
@@ -280,7 +344,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sets", type=int, default=2, help="buffer sets per workload")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="buffer sets per workload (0: enough to exceed twice the MALL)")
     ap.add_argument("--cpu-budget", type=float, default=8.0,
                     help="seconds of oracle work per workload for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -309,7 +374,8 @@ def main(argv=None):
     # a stream-K workspace (the automatic policy keeps the two step workloads
     # on whole tiles; it splits the few-tile, long-K extra row)
     workspace = g.attach_workspace(h)
-    parts = [Part(g, h, n, args.sets) for n in STEP_WORKLOADS]
+    parts = [Part(g, h, n, args.sets or sets_needed(workloads.WORKLOADS[n]))
+             for n in STEP_WORKLOADS]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -344,9 +410,16 @@ def main(argv=None):
     for p in parts:
         kms = p.kernel_ms()
         tf = p.w.flops / (kms * 1e-3) / 1e12
+        p10, p50, p90 = np.percentile(p.times_ms(), [10, 50, 90])
         report_parts[p.name] = {"kernel_ms": round(kms, 4), "tflops": round(tf, 2),
                                 "frac_of_peak": round(tf / PEAK_TFLOPS[p.w.dtype], 4),
-                                "peak_tflops": PEAK_TFLOPS[p.w.dtype]}
+                                "peak_tflops": PEAK_TFLOPS[p.w.dtype],
+                                "launch_ms_p10_p50_p90": [round(float(x), 4)
+                                                          for x in (p10, p50, p90)],
+                                "buffer_sets": len(p.sets)}
+    for p in parts:
+        hot = p.hot_cache_ms(sh)
+        report_parts[p.name]["hot_cache_kernel_ms"] = round(hot, 4)
     # which kernel each part used
     for p in parts:
         A, B, C, D = p.sets[0]
@@ -376,11 +449,11 @@ def main(argv=None):
     extras = {}
     if not args.no_extras:
         vf = time_extra(g, h, "fp32_4096", "f32_vfma_128x128x8_t8x8", reps=10, warmup=3)
-        vf["roofline"] = {"bound": "alu", "peak": round(VALU_FP32_UNPACKED_TFLOPS, 1),
-                          "unit": "TFLOP/s",
-                          "frac": round(vf["tflops"] / VALU_FP32_UNPACKED_TFLOPS, 4),
-                          "note": "plain v_fma_f32 rate; 157.3 assumes packed FP32 FMA"}
+        vf["roofline"] = {"bound": "alu", "peak": round(VALU_FP32_TFLOPS, 1),
+                          "unit": "TFLOP/s", "frac": round(vf["tflops"] / VALU_FP32_TFLOPS, 4),
+                          "note": "vector FP32 FMA rate, 2 v_fmac_f32 per lane per clock"}
         extras["fp32_4096_vector_fma"] = vf
+        extras["fp32_256"] = time_extra(g, h, "fp32_256", None, reps=50, warmup=10)
         extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
                                                        warmup=5)
         extras["bf16_8192_bf16_output"] = time_extra(g, h, "bf16_8192", None, reps=10, warmup=3,
@@ -413,7 +486,7 @@ def main(argv=None):
         cpu = {"value": fl / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                "sample": "; ".join(f"{k}: {v['outputs']} random outputs, full K, "
                                     f"{v['seconds']:.1f} s" for k, v in samples.items()),
-               "per_workload_tflops": {k: v["tflops"] for k, v in samples.items()}}
+               "per_workload": samples, "fp32_256_full_output": oracle_full_small(cores)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -421,7 +494,8 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp32 + bf16-in/fp32-acc", "data": "synthetic",
         "config": {"workload": "fp32 GEMM 4096^3 + bf16->fp32 GEMM 8192^3 (NN, alpha=1, beta=0)",
-                   "parallelism": "single GPU", "buffer_sets": args.sets},
+                   "parallelism": "single GPU",
+                   "buffer_sets": {p.name: len(p.sets) for p in parts}},
         "parts": report_parts, "extra_rows": extras, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -15,8 +15,10 @@
 // the 16 threads of a row read consecutive 16-byte LDS words.  Two LDS stages
 // with register staging overlap the next step's global loads with the FMAs.
 //
-// Peak note: without packed FP32 instructions (not used by this library),
-// gfx950's vector FP32 rate is half the device FP32 peak.
+// Peak note: the FMAs compile to the two-operand v_fmac_f32 encoding, which
+// gfx950 issues at two per lane per clock (the device FP32 peak) without
+// packed FP32 instructions (not used by this library); the three-operand
+// v_fma_f32 form issues at half that rate.
 #pragma once
 
 #include "common.hpp"
