@@ -180,22 +180,28 @@ def roofline_tflops(w: workloads.Workload, out_bytes: int = 4) -> float:
 
 
 def time_extra(g, h, name: str, variant_name, reps: int, warmup: int,
-               out_dtype=torch.float32):
+               out_dtype=torch.float32, activation=0):
     """Time one workload outside the step (own buffers, HIP events).
 
-    out_dtype=torch.bfloat16 runs a bf16 workload with bf16 C and D."""
+    out_dtype=torch.bfloat16 runs a bf16 workload with bf16 C and D; a nonzero
+    activation (GEMM_ACT_*) runs the fused epilogue with a N(0, 0.02) bias."""
     w = workloads.WORKLOADS[name]
     A, B, C = workloads.make_inputs(w)
     A, B = A.cuda(), B.cuda()
     C = None if C is None else C.to("cuda", out_dtype)
     D = torch.empty(w.M, w.N, dtype=out_dtype, device="cuda")
+    bias = None
+    if activation:
+        bias = workloads.draw_matrix((w.N,), "n002", w.seeds["sample"] + 1, "f32").to(
+            "cuda", out_dtype)
     vid = -1
     if variant_name is not None:
         vid = [i for i, n, _, _ in g.variants() if n == variant_name][0]
     g.gemm_set_variant(h, vid)
     try:
         run = lambda: g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
-                                    alpha=w.alpha, beta=w.beta)
+                                    alpha=w.alpha, beta=w.beta, bias=bias,
+                                    activation=activation)
         # at least `warmup` calls and ~50 ms of them: clocks that dropped
         # while the GPU idled take tens of milliseconds to come back
         t0 = time.perf_counter()
@@ -443,7 +449,7 @@ def main(argv=None):
 
     # the remaining hot-path rows, timed outside the step: the fp32 vector-FMA
     # mainloop at 4096^3, the full alpha/beta epilogue with ragged edges, the
-    # bf16-output epilogue at 8192^3, the
+    # bf16-output epilogue at 8192^3, the fused bias+GELU epilogue, the
     # transformer-layer sweep (and one GPU's share of it under an 8-way
     # split), and a few-tile long-K shape that the stream-K path takes
     extras = {}
@@ -458,6 +464,15 @@ def main(argv=None):
                                                        warmup=5)
         extras["bf16_8192_bf16_output"] = time_extra(g, h, "bf16_8192", None, reps=10, warmup=3,
                                                      out_dtype=torch.bfloat16)
+        # the fused epilogue on the MLP-up shape: bias + GELU, bf16 output,
+        # beside the same GEMM without them
+        fused = time_extra(g, h, "bf16_mlp_up", None, reps=10, warmup=3,
+                           out_dtype=torch.bfloat16, activation=g.GEMM_ACT_GELU)
+        plain = time_extra(g, h, "bf16_mlp_up", None, reps=10, warmup=3,
+                           out_dtype=torch.bfloat16)
+        fused["plain_kernel_ms"] = plain["kernel_ms"]
+        fused["epilogue"] = "bias (N(0,0.02), bf16) + GELU (erf form), bf16 C/D"
+        extras["bf16_mlp_up_bias_gelu"] = fused
         for group, names in (("transformer_layer", ("bf16_qkv", "bf16_outproj", "bf16_mlp_up",
                                                     "bf16_mlp_down")),
                              ("transformer_layer_tp8_shard", ("bf16_qkv_tp8", "bf16_outproj_tp8",

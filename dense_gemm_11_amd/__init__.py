@@ -33,13 +33,24 @@ GEMM_ERR_INVALID_VALUE = 1
 GEMM_ERR_NOT_SUPPORTED = 2
 GEMM_ERR_HIP = 3
 GEMM_ERR_ALLOC = 4
+GEMM_ACT_NONE = 0
+GEMM_ACT_RELU = 1
+GEMM_ACT_GELU = 2
 
 # Every function declared in include/dense_gemm.h.
 EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
            "gemm_variant_count", "gemm_variant_name", "gemm_variant_dtype",
            "gemm_variant_tile", "gemm_set_variant", "gemm_last_variant",
            "gemm_select_variant", "gemm_stream_k_workspace_bytes", "gemm_set_workspace",
-           "gemm_set_stream_k", "gemm_last_stream_k")
+           "gemm_set_stream_k", "gemm_last_stream_k", "gemm_run_epilogue")
+
+
+class GemmEpilogue(ctypes.Structure):
+    """gemm_epilogue_t: bias pointer (0/None for none), activation, clamp flag
+    and bounds."""
+    _fields_ = [("bias", ctypes.c_void_p), ("activation", ctypes.c_int),
+                ("clamp", ctypes.c_int), ("clamp_lo", ctypes.c_float),
+                ("clamp_hi", ctypes.c_float)]
 
 
 class GemmError(RuntimeError):
@@ -80,6 +91,9 @@ def _load():
     lib.gemm_run.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                              vp, i64, i32, vp]
     lib.gemm_run.restype = i32
+    lib.gemm_run_epilogue.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32,
+                                      vp, i64, vp, i64, i32, ctypes.POINTER(GemmEpilogue), vp]
+    lib.gemm_run_epilogue.restype = i32
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_variant_count.argtypes = []
@@ -128,6 +142,15 @@ def gemm_run(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D,
     """Raw call: pointers and the stream are integers (0/None for NULL)."""
     return lib.gemm_run(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                         D, ldd, dtype, stream)
+
+
+def gemm_run_epilogue(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd,
+                      dtype, epilogue, stream) -> int:
+    """Raw call: pointers and the stream are integers (0/None for NULL);
+    epilogue is a GemmEpilogue or None."""
+    ep = None if epilogue is None else ctypes.byref(epilogue)
+    return lib.gemm_run_epilogue(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                 ldc, D, ldd, dtype, ep, stream)
 
 
 def gemm_status_string(s: int) -> str:
@@ -206,13 +229,15 @@ def variants():
 
 
 def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
-                stream=None, check=True) -> int:
+                stream=None, check=True, bias=None, activation=GEMM_ACT_NONE,
+                clamp=None) -> int:
     """gemm_run on torch tensors (row-major 2-D views with unit column stride).
 
     A: op(A) is M x K (A stored M x K for "N", K x M for "T"); B likewise;
     C, D: M x N.  A and B are float32 (fp32 GEMM) or bfloat16; with bfloat16
     operands, C and D are float32 (GEMM_DTYPE_BF16_F32) or both bfloat16
-    (GEMM_DTYPE_BF16_BF16).
+    (GEMM_DTYPE_BF16_BF16).  bias (a length-N tensor of D's dtype),
+    activation (GEMM_ACT_*) and clamp ((lo, hi)) select gemm_run_epilogue.
     """
     import torch
 
@@ -234,13 +259,23 @@ def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
     Kb, N = (B.shape[0], B.shape[1]) if transB == "N" else (B.shape[1], B.shape[0])
     if Kb != K or tuple(D.shape) != (M, N) or (C is not None and tuple(C.shape) != (M, N)):
         raise ValueError("inconsistent GEMM shapes")
+    if bias is not None and (bias.dtype != out or bias.dim() != 1 or bias.shape[0] != N
+                             or (N > 1 and bias.stride(0) != 1)):
+        raise ValueError("bias must be a contiguous length-N tensor of D's dtype")
     if stream is None:
         stream = torch.cuda.current_stream(D.device).cuda_stream
-    s = gemm_run(h, GEMM_OP_N if transA == "N" else GEMM_OP_T,
-                 GEMM_OP_N if transB == "N" else GEMM_OP_T, M, N, K, float(alpha),
-                 A.data_ptr(), ld(A), B.data_ptr(), ld(B), float(beta),
-                 None if C is None else C.data_ptr(), ld(C) if C is not None else N,
-                 D.data_ptr(), ld(D), dtype, stream)
+    args = (h, GEMM_OP_N if transA == "N" else GEMM_OP_T,
+            GEMM_OP_N if transB == "N" else GEMM_OP_T, M, N, K, float(alpha),
+            A.data_ptr(), ld(A), B.data_ptr(), ld(B), float(beta),
+            None if C is None else C.data_ptr(), ld(C) if C is not None else N,
+            D.data_ptr(), ld(D), dtype)
+    if bias is None and activation == GEMM_ACT_NONE and clamp is None:
+        s = gemm_run(*args, stream)
+    else:
+        lo, hi = (0.0, 0.0) if clamp is None else clamp
+        ep = GemmEpilogue(None if bias is None else bias.data_ptr(), int(activation),
+                          int(clamp is not None), float(lo), float(hi))
+        s = gemm_run_epilogue(*args, ep, stream)
     if check and s != GEMM_OK:
         raise GemmError(s)
     return s

@@ -22,7 +22,9 @@ struct gemm_handle_s {
 
 namespace dg {
 
-// D = beta * C (or 0 when beta == 0): the whole result when K == 0 or alpha == 0.
+// D = beta * C (or 0 when beta == 0), then the fused epilogue (bias,
+// activation, clamp; nothing for a plain call): the whole result when K == 0
+// or alpha == 0.
 template <typename OutT>
 __global__ __launch_bounds__(256) void scale_c_kernel(GemmArgs p)
 {
@@ -32,8 +34,8 @@ __global__ __launch_bounds__(256) void scale_c_kernel(GemmArgs p)
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * 256) {
         const int64_t row = e / p.N, col = e % p.N;
-        D[row * p.ldd + col] =
-            from_f32<OutT>((p.beta != 0.0f) ? p.beta * to_f32(C[row * p.ldc + col]) : 0.0f);
+        const float v = (p.beta != 0.0f) ? p.beta * to_f32(C[row * p.ldc + col]) : 0.0f;
+        D[row * p.ldd + col] = from_f32<OutT>(epilogue_op<OutT>(p, v, (int)col));
     }
 }
 
@@ -354,10 +356,11 @@ int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, 
                               K, true);
 }
 
-gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M, int64_t N,
-                       int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
-                       float beta, const void* C, int64_t ldc, void* D, int64_t ldd,
-                       gemm_dtype_t dtype, hipStream_t stream)
+static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M,
+                              int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                              const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
+                              void* D, int64_t ldd, gemm_dtype_t dtype, const gemm_epilogue_t* ep,
+                              hipStream_t stream)
 {
     using namespace dg;
     if (!h) return GEMM_ERR_INVALID_VALUE;
@@ -366,6 +369,14 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     if (dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32 && dtype != GEMM_DTYPE_BF16_BF16)
         return GEMM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+    if (ep) {
+        if (ep->activation != GEMM_ACT_NONE && ep->activation != GEMM_ACT_RELU &&
+            ep->activation != GEMM_ACT_GELU)
+            return GEMM_ERR_INVALID_VALUE;
+        if (ep->clamp && !(ep->clamp_lo <= ep->clamp_hi)) return GEMM_ERR_INVALID_VALUE;  // NaN too
+    }
+    // a fused epilogue with something to do (bias, activation or clamp)
+    const bool epi = ep && (ep->bias || ep->activation != GEMM_ACT_NONE || ep->clamp);
     const bool out_bf16 = dtype == GEMM_DTYPE_BF16_BF16;
     const int64_t es_out = out_bf16 ? 2 : 4;  // bytes per element of C and D
     const int64_t one = 1;
@@ -384,13 +395,19 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX || lda > INT_MAX || ldb > INT_MAX ||
         ldd > INT_MAX || (beta != 0.0f && ldc > INT_MAX))
         return GEMM_ERR_NOT_SUPPORTED;
+    const int64_t span_d = ((M - 1) * ldd + N) * es_out;
     if (beta != 0.0f) {
-        const int64_t span_c = ((M - 1) * ldc + N) * es_out, span_d = ((M - 1) * ldd + N) * es_out;
+        const int64_t span_c = ((M - 1) * ldc + N) * es_out;
         if (static_cast<const void*>(C) == static_cast<const void*>(D)) {
             if (ldc != ldd) return GEMM_ERR_INVALID_VALUE;
         } else if (ranges_overlap(C, span_c, D, span_d)) {
             return GEMM_ERR_INVALID_VALUE;
         }
+    }
+    if (epi && ep->bias) {
+        // the bias is read while D is written: it must lie outside D
+        if (ranges_overlap(ep->bias, N * es_out, D, span_d)) return GEMM_ERR_INVALID_VALUE;
+        if (!aligned_to(ep->bias, es_out)) return GEMM_ERR_NOT_SUPPORTED;
     }
 
     GemmArgs a;
@@ -413,6 +430,11 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     a.d_vec = aligned_to(D, es_out);
     a.sk_partials = nullptr;
     a.sk_flags = nullptr;
+    a.bias = epi ? ep->bias : nullptr;
+    a.act = epi ? (int)ep->activation : EPI_ACT_NONE;
+    a.clamp = epi && ep->clamp;
+    a.clamp_lo = a.clamp ? ep->clamp_lo : 0.0f;
+    a.clamp_hi = a.clamp ? ep->clamp_hi : 0.0f;
 
     if (!reads_ab) {
         const int64_t blocks = std::min<int64_t>(ceil_div(M * N, 256), 65536);
@@ -447,11 +469,11 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
         wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, a_kc, b_kc, K, lda, ldb, es));
     const double dp_us = data_parallel_us(v, M, N, K);
     double sk_us = 0.0;
-    int sk = (aligned && v.kind == KIND_MFMA_DMA && !out_bf16)
+    int sk = (aligned && v.kind == KIND_MFMA_DMA && !out_bf16 && !epi)
                  ? stream_k_grid(v, M, N, K, h->stream_k_mode, h->ws_bytes, dp_us, &sk_us)
                  : 0;
     if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0 &&
-        !out_bf16) {
+        !out_bf16 && !epi) {
         // With a workspace, stream-K on the other tile size competes too; the
         // lowest estimate wins.
         const int other = dma_variant(op_dtype, v.bm < 256);
@@ -480,6 +502,16 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     const bool nn_t = sk == 0 && h->forced_variant < 0 && vr.nn_t_fn && aligned && a_kc &&
                       !b_kc && dma_offsets_fit(vr, false, true, K, ldb, lda, es);
     if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
+    // fused epilogue: only the selected direct-to-LDS variants, whole tiles
+    // and wide access, carry it
+    const EpiFns* ef = nullptr;
+    if (epi) {
+        if (!aligned || id != dma_variant(op_dtype, vr.bm == 256)) return GEMM_ERR_NOT_SUPPORTED;
+        ef = op_dtype == GEMM_DTYPE_F32 ? epi_fns_f32(vr.bm)
+             : out_bf16                 ? epi_fns_bf16_out(vr.bm)
+                                        : epi_fns_bf16(vr.bm);
+        if (!ef) return GEMM_ERR_NOT_SUPPORTED;
+    }
     if (sk > 0) {
         a.sk_flags = static_cast<unsigned*>(h->ws);
         a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
@@ -495,7 +527,9 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
         t.tiles_m = (int)ceil_div(N, vr.bm);
         t.tiles_n = (int)ceil_div(M, vr.bn);
         t.group_m = std::min(t.tiles_m, 4);
-        e = (out_bf16 ? vr.bo_nn_t_fn : vr.nn_t_fn)(t, (int)grid, stream);
+        e = (ef ? ef->nn_t : out_bf16 ? vr.bo_nn_t_fn : vr.nn_t_fn)(t, (int)grid, stream);
+    } else if (ef) {
+        e = ef->fn[a_kc][b_kc](a, (int)grid, stream);
     } else {
         e = (out_bf16 ? vr.bo_fn : vr.fn)[aligned][a_kc][b_kc](a, (int)grid, stream);
     }
@@ -503,6 +537,25 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
     h->last_variant = id;
     h->last_stream_k = sk;
     return GEMM_OK;
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M, int64_t N,
+                       int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, const void* C, int64_t ldc, void* D, int64_t ldd,
+                       gemm_dtype_t dtype, hipStream_t stream)
+{
+    return run_gemm(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, dtype,
+                    nullptr, stream);
+}
+
+gemm_status_t gemm_run_epilogue(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M,
+                                int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, float beta, const void* C,
+                                int64_t ldc, void* D, int64_t ldd, gemm_dtype_t dtype,
+                                const gemm_epilogue_t* epilogue, hipStream_t stream)
+{
+    return run_gemm(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, dtype,
+                    epilogue, stream);
 }
 
 }  // extern "C"

@@ -42,7 +42,16 @@ struct GemmArgs {
     // stream-K only: one BM*BN partial-sum slot and one flag per workgroup
     float* sk_partials;
     unsigned* sk_flags;
+    // fused epilogue, applied after alpha*acc + beta*C in this order: bias
+    // (one value per D column, element type of D; null = none), activation
+    // (EPI_ACT_*), clamp to [clamp_lo, clamp_hi] when clamp != 0
+    const void* bias;
+    int act;
+    int clamp;
+    float clamp_lo, clamp_hi;
 };
+
+enum : int { EPI_ACT_NONE = 0, EPI_ACT_RELU = 1, EPI_ACT_GELU = 2 };
 
 // Tile (tm, tn) of logical tile id w: tiles are walked in groups of group_m
 // tile-rows, column by column within a group, so that workgroups running at
@@ -105,6 +114,25 @@ template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
 {
     return __builtin_bit_cast(bf16_t, (__bf16)x);
+}
+
+// Activation of the fused epilogue: ReLU max(x, 0), or GELU in its erf form
+// x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)); act is uniform across a launch.
+__device__ __forceinline__ float activate(float x, int act)
+{
+    if (act == EPI_ACT_RELU) return x > 0.0f ? x : 0.0f;
+    if (act == EPI_ACT_GELU) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    return x;
+}
+
+// bias + activation + clamp on one value (after alpha*acc + beta*C).
+template <typename OutT>
+__device__ __forceinline__ float epilogue_op(const GemmArgs& p, float v, int col)
+{
+    if (p.bias) v += to_f32(static_cast<const OutT*>(p.bias)[col]);
+    v = activate(v, p.act);
+    if (p.clamp) v = fminf(fmaxf(v, p.clamp_lo), p.clamp_hi);
+    return v;
 }
 
 }  // namespace dg

@@ -1,0 +1,18 @@
+// Fused-epilogue (bias, activation, clamp) instantiations of the selected
+// bf16 direct-to-LDS variants with fp32 C and D.
+#include "mfma_dma_gemm.hpp"
+#include "variants.hpp"
+
+namespace dg {
+
+using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
+using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+
+const EpiFns* epi_fns_bf16(int bm)
+{
+    static const EpiFns big = DG_EPI_TABLE(dma_gemm_kernel, Dma256s3L, false);
+    static const EpiFns mid = DG_EPI_TABLE(dma_gemm_kernel, Dma128s3L, false);
+    return bm == 256 ? &big : bm == 128 ? &mid : nullptr;
+}
+
+}  // namespace dg

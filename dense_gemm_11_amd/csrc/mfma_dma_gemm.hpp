@@ -349,8 +349,13 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 //
 // OUT_BF16: C and D are bfloat16; alpha*acc + beta*C is formed in fp32 and
 // rounded once to bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+//
+// EPI: the fused epilogue of "GEMM on NVIDIA GPUs" (section 4, epilogue):
+// after alpha*acc + beta*C, add the bias of the D column, apply the
+// activation and the clamp, then convert and store -- all in registers, so
+// no second kernel reads D back.
 template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false, bool OUT_T = false,
-          bool OUT_BF16 = false>
+          bool OUT_BF16 = false, bool EPI = false>
 __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
@@ -707,6 +712,11 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                 const int col = d_col(i, j, vg);
                 f32x4 out = alpha * sum[j][vg];
                 if (beta != 0.0f) out += beta * cv[j][vg];
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        if (col + s < d_cols) out[s] = epilogue_op<OutT>(p, out[s], col + s);
+                }
                 if (p.d_vec && col + 4 <= d_cols) {
                     store4(drow + col, out);
                 } else {

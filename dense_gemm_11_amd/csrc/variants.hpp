@@ -27,6 +27,19 @@ struct Variant {
     LaunchFn bo_nn_t_fn;
 };
 
+// Fused-epilogue (bias, activation, clamp) instantiations of one selected
+// direct-to-LDS variant, wide access only: [A k-contiguous][B k-contiguous],
+// then the transposed-output one serving NN.
+struct EpiFns {
+    LaunchFn fn[2][2];
+    LaunchFn nn_t;
+};
+// For operand dtype 0 (fp32) or 1 (bf16), tile size bm (256 or 128) and
+// output type (bf16 C/D or fp32); null when there is none.
+const EpiFns* epi_fns_f32(int bm);
+const EpiFns* epi_fns_bf16(int bm);
+const EpiFns* epi_fns_bf16_out(int bm);
+
 // Launch through hipLaunchKernel so the launch status is returned directly.
 template <auto KERNEL, int THREADS>
 hipError_t launch_kernel(const GemmArgs& a, int grid, hipStream_t s)
@@ -94,14 +107,20 @@ const Variant* f32dma_sweep_variant_table(int* count);
 #define DG_NN_T_FN(KERNEL, CFG) dg::launch_kernel<KERNEL<CFG, false, true, true, false, true>, CFG::THREADS>
 
 // bf16-output instantiations: [wide access][A k-contiguous][B k-contiguous],
-// then the transposed-output one for NN.
+// then the transposed-output one for NN.  Only wide access is instantiated
+// (the entry point requires it for bf16 output); the narrow entries are null.
 #define DG_BO_TABLE(KERNEL, CFG)                                                                     \
-    {{{dg::launch_kernel<KERNEL<CFG, false, false, false, false, false, true>, CFG::THREADS>,     \
-       dg::launch_kernel<KERNEL<CFG, false, true, false, false, false, true>, CFG::THREADS>},     \
-      {dg::launch_kernel<KERNEL<CFG, true, false, false, false, false, true>, CFG::THREADS>,      \
-       dg::launch_kernel<KERNEL<CFG, true, true, false, false, false, true>, CFG::THREADS>}},     \
+    {{{nullptr, nullptr}, {nullptr, nullptr}},                                                     \
      {{dg::launch_kernel<KERNEL<CFG, false, false, true, false, false, true>, CFG::THREADS>,      \
        dg::launch_kernel<KERNEL<CFG, false, true, true, false, false, true>, CFG::THREADS>},      \
       {dg::launch_kernel<KERNEL<CFG, true, false, true, false, false, true>, CFG::THREADS>,       \
        dg::launch_kernel<KERNEL<CFG, true, true, true, false, false, true>, CFG::THREADS>}}},     \
         dg::launch_kernel<KERNEL<CFG, false, true, true, false, true, true>, CFG::THREADS>
+
+// Fused-epilogue instantiations for output type OUTBF (false: fp32 C/D).
+#define DG_EPI_TABLE(KERNEL, CFG, OUTBF)                                                          \
+    {{{dg::launch_kernel<KERNEL<CFG, false, false, true, false, false, OUTBF, true>, CFG::THREADS>, \
+       dg::launch_kernel<KERNEL<CFG, false, true, true, false, false, OUTBF, true>, CFG::THREADS>},  \
+      {dg::launch_kernel<KERNEL<CFG, true, false, true, false, false, OUTBF, true>, CFG::THREADS>,  \
+       dg::launch_kernel<KERNEL<CFG, true, true, true, false, false, OUTBF, true>, CFG::THREADS>}},  \
+     dg::launch_kernel<KERNEL<CFG, false, true, true, false, true, OUTBF, true>, CFG::THREADS>}

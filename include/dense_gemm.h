@@ -108,6 +108,52 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB,
                        float beta, const void* C, int64_t ldc,
                        void* D, int64_t ldd, gemm_dtype_t dtype, hipStream_t stream);
 
+/* ---- fused epilogue ------------------------------------------------------
+ * "GEMM on NVIDIA GPUs: from a naive kernel to a tiled pipeline" (section 4,
+ * epilogue) lists alpha, beta, bias, activation, clamp and the dtype
+ * conversion as work the store step can do in place, saving the round trip
+ * of a second kernel through D.  gemm_run_epilogue computes, per element,
+ *     D_ij = convert(clamp(act(alpha*op(A)op(B)_ij + beta*C_ij + bias_j)))
+ * in that order, every step in fp32, with one conversion to D's type at the
+ * end (nearest even for bf16).
+ *   bias       : device pointer to N elements of D's element type (float, or
+ *                bfloat16 for GEMM_DTYPE_BF16_BF16), bias[j] added to column
+ *                j of every row; NULL for none.  Caller-owned; it must not
+ *                overlap D (GEMM_ERR_INVALID_VALUE) and must be element
+ *                aligned (GEMM_ERR_NOT_SUPPORTED otherwise).
+ *   activation : GEMM_ACT_NONE; GEMM_ACT_RELU max(x, 0); GEMM_ACT_GELU
+ *                x*Phi(x) = x/2 * (1 + erf(x/sqrt(2))) (the erf form).  Any
+ *                other value: GEMM_ERR_INVALID_VALUE.
+ *   clamp      : nonzero clamps to [clamp_lo, clamp_hi]; clamp_lo > clamp_hi
+ *                or a NaN bound: GEMM_ERR_INVALID_VALUE.
+ * A NULL epilogue (or one with no bias, no activation and no clamp) is
+ * gemm_run.  Everything else -- layouts, degenerate cases (K == 0 or
+ * alpha == 0 gives clamp(act(beta*C + bias))), errors -- is as for gemm_run.
+ * The fused epilogue runs in the whole-tile direct-to-LDS kernels the
+ * selector uses for element-aligned operands (never as stream-K); where
+ * gemm_run would take another kernel (operands not element-aligned, panel
+ * offsets beyond 32 bits, a forced sweep variant) it returns
+ * GEMM_ERR_NOT_SUPPORTED.                                                   */
+typedef enum {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1,
+    GEMM_ACT_GELU = 2
+} gemm_activation_t;
+
+typedef struct {
+    const void* bias;
+    gemm_activation_t activation;
+    int clamp;
+    float clamp_lo, clamp_hi;
+} gemm_epilogue_t;
+
+gemm_status_t gemm_run_epilogue(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB,
+                                int64_t M, int64_t N, int64_t K, float alpha,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                float beta, const void* C, int64_t ldc,
+                                void* D, int64_t ldd, gemm_dtype_t dtype,
+                                const gemm_epilogue_t* epilogue, hipStream_t stream);
+
 /* Static, human-readable text for a status code ("unknown status" otherwise). */
 const char* gemm_status_string(gemm_status_t s);
 

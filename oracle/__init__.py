@@ -18,10 +18,15 @@ General Matrix Multiplication on NVIDIA Ada Lovelace via CUTLASS and WMMA"
 naive kernel to a tiled pipeline" (section 5, precision; section 6,
 measurement) asks for a reference and tolerance matched to the dtypes rather
 than bitwise equality.
+
+``epilogue`` applies the fused bias / activation / clamp steps to the
+oracle's values in float64 and widens the error denominator by the bias and
+the activation's largest slope.
 """
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from typing import Optional, Sequence
@@ -177,6 +182,56 @@ def bf16_output_errors(D: np.ndarray, val: np.ndarray, den: np.ndarray) -> np.nd
 def max_bf16_output_error(D, val, den) -> float:
     e = bf16_output_errors(D, val, den)
     return float(e.max()) if e.size else 0.0
+
+
+# Fused epilogue ("GEMM on NVIDIA GPUs", section 4, epilogue): after
+# alpha*acc + beta*C come the bias, the activation and the clamp, in the order
+# that section lists them, each on the exact value here.
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+# Largest |d/dx| of GELU(x) = x Phi(x): the slope Phi(x) + x phi(x) has its
+# maximum where phi(x) (2 - x^2) = 0, x = sqrt(2): Phi(sqrt 2) + e^-1 / sqrt(pi).
+GELU_MAX_SLOPE = 0.5 * (1.0 + math.erf(1.0)) + math.exp(-1.0) / math.sqrt(math.pi)
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """x Phi(x) with Phi the standard normal CDF, Phi(x) = (1 + erf(x/sqrt 2)) / 2."""
+    x = np.asarray(x, dtype=np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def activate(x: np.ndarray, act: int) -> np.ndarray:
+    if act == ACT_RELU:
+        return np.maximum(x, 0.0)
+    if act == ACT_GELU:
+        return gelu(x)
+    if act == ACT_NONE:
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown activation {act}")
+
+
+def epilogue(val: np.ndarray, den: np.ndarray, cols: np.ndarray, bias=None, act: int = ACT_NONE,
+             clamp=None):
+    """Reference value and error scale after the fused epilogue.
+
+    val, den: the oracle's alpha*s + beta*C and its denominator at outputs
+    whose columns are `cols`; bias: float64-convertible array of N values
+    (bias[j] added to column j).  Returns (d, scale) with
+    d = clamp(act(val + bias[cols])) and scale = slope * (den + |bias[cols]|),
+    slope the activation's largest |derivative| (1, or GELU_MAX_SLOPE), so an
+    fp32 pre-activation within tol * (den + |bias|) of the exact one lands
+    within tol * scale after the activation and the clamp (both Lipschitz)."""
+    val = np.asarray(val, dtype=np.float64)
+    den = np.asarray(den, dtype=np.float64)
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float64)[np.asarray(cols)]
+        val = val + b
+        den = den + np.abs(b)
+    d = activate(val, act)
+    if clamp is not None:
+        d = np.clip(d, clamp[0], clamp[1])
+    slope = GELU_MAX_SLOPE if act == ACT_GELU else 1.0
+    return d, slope * den
 
 
 def max_threads() -> int:

@@ -176,3 +176,33 @@ def test_bf16_output_dtype_validates_with_2_byte_elements(h):
     assert run(h, dtype=g.GEMM_DTYPE_BF16_BF16, M=0) == g.GEMM_OK
     assert g.gemm_select_variant(g.GEMM_DTYPE_BF16_BF16, 0, 0, 8192, 8192, 8192) == \
         g.gemm_select_variant(g.GEMM_DTYPE_BF16_F32, 0, 0, 8192, 8192, 8192)
+
+
+def run_epi(h, ep, **kw):
+    a = dict(transA=0, transB=0, M=4, N=5, K=6, alpha=1.0, A=FAKE, lda=6, B=FAKE, ldb=5,
+             beta=0.0, C=None, ldc=5, D=FAKE, ldd=5, dtype=0, stream=None)
+    a.update(kw)
+    return g.gemm_run_epilogue(h, a["transA"], a["transB"], a["M"], a["N"], a["K"], a["alpha"],
+                               a["A"], a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"],
+                               a["D"], a["ldd"], a["dtype"], ep, a["stream"])
+
+
+def test_epilogue_arguments_validated(h):
+    far = FAKE + (1 << 20)
+    E = g.GemmEpilogue
+    for ep in (E(None, 3, 0, 0.0, 0.0), E(None, -1, 0, 0.0, 0.0),
+               E(None, g.GEMM_ACT_RELU, 1, 1.0, 0.0),              # lo > hi
+               E(None, g.GEMM_ACT_NONE, 1, float("nan"), 1.0),      # NaN bound
+               E(None, g.GEMM_ACT_NONE, 1, 0.0, float("nan")),
+               E(FAKE + 8, g.GEMM_ACT_NONE, 0, 0.0, 0.0)):          # bias inside D
+        assert run_epi(h, ep) == g.GEMM_ERR_INVALID_VALUE, (ep.activation, ep.clamp, ep.bias)
+    # a bias that is not element aligned is not supported (checked before any launch)
+    assert run_epi(h, E(far + 2, g.GEMM_ACT_NONE, 0, 0.0, 0.0)) == g.GEMM_ERR_NOT_SUPPORTED
+    # bias of bf16 D: 2-byte elements; far + 2 is aligned, D's 4 x 5 bf16 span is 40 bytes
+    assert run_epi(h, E(FAKE + 38, g.GEMM_ACT_NONE, 0, 0.0, 0.0),
+                   dtype=g.GEMM_DTYPE_BF16_BF16) == g.GEMM_ERR_INVALID_VALUE
+    # the usual argument checks still come first, and an empty output is a no-op
+    assert run_epi(h, None, M=-1) == g.GEMM_ERR_INVALID_VALUE
+    assert run_epi(h, E(None, g.GEMM_ACT_GELU, 0, 0.0, 0.0), M=0, A=None, B=None,
+                   D=None) == g.GEMM_OK
+    assert run_epi(None, E(None, g.GEMM_ACT_GELU, 0, 0.0, 0.0)) == g.GEMM_ERR_INVALID_VALUE

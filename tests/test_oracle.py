@@ -248,3 +248,75 @@ def test_unmodified_oracle_passes_pins_in_child(mutant_dir):
     proc = subprocess.run([sys.executable, "-m", "tests.oracle_pins", so], cwd=root,
                           capture_output=True, text=True, timeout=300)
     assert proc.returncode == 0, proc.stdout + proc.stderr
+
+
+# -- fused epilogue: bias, activation, clamp -----------------------------------
+
+def test_gelu_at_tabulated_normal_cdf_values():
+    """GELU(x) = x Phi(x): at x = +-1, +-2 it equals x times the standard
+    normal CDF values found in any table (Phi(1) = 0.841344746068543,
+    Phi(2) = 0.977249868051821)."""
+    phi1, phi2 = 0.8413447460685429, 0.9772498680518208
+    x = np.array([1.0, -1.0, 2.0, -2.0, 0.0])
+    want = np.array([phi1, -(1.0 - phi1), 2.0 * phi2, -2.0 * (1.0 - phi2), 0.0])
+    assert np.allclose(oracle.gelu(x), want, rtol=1e-15, atol=1e-16)
+
+
+def test_gelu_odd_part_is_identity():
+    """x Phi(x) - (-x) Phi(-x) = x (Phi(x) + Phi(-x)) = x."""
+    x = np.random.default_rng(3).standard_normal(1000) * 4.0
+    assert np.allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=1e-13, atol=1e-15)
+
+
+def test_gelu_max_slope():
+    """The error scale's slope bound is the true maximum of |d/dx x Phi(x)|:
+    no finite difference exceeds it, and one at x = sqrt(2) reaches it."""
+    x = np.linspace(-8.0, 8.0, 160001)
+    h = 1e-6
+    slope = (oracle.gelu(x + h) - oracle.gelu(x - h)) / (2 * h)
+    assert np.abs(slope).max() <= oracle.GELU_MAX_SLOPE + 1e-8
+    s2 = (oracle.gelu(np.sqrt(2.0) + h) - oracle.gelu(np.sqrt(2.0) - h)) / (2 * h)
+    assert abs(s2 - oracle.GELU_MAX_SLOPE) < 1e-8
+
+
+def test_epilogue_closed_form_all_ones():
+    """A = B = 1 (M x K, K x N): alpha*K + beta*C_ij + bias_j, then the
+    activation and the clamp, computed by hand on small integers; a bias
+    indexed by row, a bias added after the activation, or the clamp taken
+    before the activation each give a different answer."""
+    M, N, K = 5, 7, 6
+    alpha, beta = -1.0, 2.0
+    A = np.ones((M, K), dtype=np.float32)
+    B = np.ones((K, N), dtype=np.float32)
+    C = np.arange(M * N, dtype=np.float32).reshape(M, N) % 5 - 2.0
+    bias = np.arange(N, dtype=np.float64) * 3.0 - 4.0
+    val, den = oracle.gemm_full("N", "N", M, N, K, alpha, A, K, B, N, beta, C, N)
+    cols = np.broadcast_to(np.arange(N), (M, N))
+    pre = alpha * K + beta * C.astype(np.float64) + bias[None, :]
+    d, scale = oracle.epilogue(val, den, cols, bias, oracle.ACT_RELU, clamp=(0.0, 9.0))
+    want = np.clip(np.maximum(pre, 0.0), 0.0, 9.0)
+    assert np.array_equal(d, want)
+    assert np.array_equal(scale, K + np.abs(beta * C) + np.abs(bias)[None, :])
+    rows = np.broadcast_to(np.arange(M)[:, None], (M, N))
+    wrong_row, _ = oracle.epilogue(val, den, rows, bias, oracle.ACT_RELU, clamp=(0.0, 9.0))
+    assert not np.array_equal(wrong_row, want)
+    late_bias = np.clip(np.maximum(alpha * K + beta * C, 0.0) + bias[None, :], 0.0, 9.0)
+    assert not np.array_equal(late_bias, want)
+    g, _ = oracle.epilogue(val, den, cols, bias, oracle.ACT_GELU, clamp=(-0.1, 5.0))
+    assert np.array_equal(g, np.clip(oracle.gelu(pre), -0.1, 5.0))
+    assert not np.array_equal(g, oracle.gelu(np.clip(pre, -0.1, 5.0)))
+
+
+def test_epilogue_gelu_scale_and_identity_paths():
+    """No bias and no activation leave the value and denominator unchanged;
+    GELU scales the denominator by its slope bound."""
+    rng = np.random.default_rng(5)
+    val = rng.standard_normal(50)
+    den = np.abs(rng.standard_normal(50)) + 1.0
+    cols = np.arange(50)
+    d, sc = oracle.epilogue(val, den, cols)
+    assert np.array_equal(d, val) and np.array_equal(sc, den)
+    d, sc = oracle.epilogue(val, den, cols, act=oracle.ACT_GELU)
+    assert np.allclose(d, oracle.gelu(val)) and np.allclose(sc, den * oracle.GELU_MAX_SLOPE)
+    d, sc = oracle.epilogue(val, den, cols, clamp=(-0.5, 0.25))
+    assert d.min() >= -0.5 and d.max() <= 0.25 and np.array_equal(sc, den)
