@@ -634,96 +634,123 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         else *reinterpret_cast<f32x4*>(q) = v;
     };
 
-    // ---- epilogue: lane holds 4 adjacent columns of one row per accumulator
-    // group.  One fragment row at a time: every load the row needs (beta*C,
-    // and a stream-K finisher's contributors' partial sums, added in
-    // workgroup order) is issued before any of its stores, so the row waits
-    // for memory once instead of once per 16-byte group.  c0..c1 are the
-    // contributing workgroups (none when c0 == c1).
+    // ---- epilogue.  A lane's accumulator group holds 4 adjacent columns of
+    // one D row, so direct stores would write each row 32 bytes per
+    // instruction (every 128-byte line in four pieces, from four
+    // instructions).  Instead each batch of FM D rows (fragment row i, or
+    // fragment column j when the output is transposed) goes through LDS
+    // (the stage arrays are free once the mainloop is done): the lanes write
+    // their groups into a per-wave [FM][DC] fp32 block, 16-byte chunks
+    // XOR-swizzled by row so neither the column-wise writes nor the row-wise
+    // reads conflict, then read it back so that consecutive lanes hold
+    // consecutive 16-byte pieces of one row.  beta*C loads and D stores then
+    // cover whole rows of the wave's block per instruction ("GEMM on NVIDIA
+    // GPUs", section 4: the epilogue stores the accumulator in the output
+    // layout).  Stream-K partial sums (contributors c0..c1, none when
+    // c0 == c1) are added in registers, in workgroup order, before staging.
     auto epilogue = [&](int tm, int tn, int64_t c0, int64_t c1) __attribute__((always_inline)) {
     const int m0 = tm * BM, n0 = tn * BN;
     const float alpha = p.alpha, beta = p.beta;
     constexpr int VG = Cfg::ACC / 4;
     // D is M x N, or N x M when the output is transposed
     const int d_rows = OUT_T ? p.N : p.M, d_cols = OUT_T ? p.M : p.N;
-    // D row of fragment (i, j) for this lane, and the first of the lane's
-    // four adjacent D columns of group vg
     const int in_frag = FM == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
-    auto d_row = [&](int i, int j) __attribute__((always_inline)) {
-        return OUT_T ? n0 + wave_n0 + j * FM + lane % FM : m0 + wave_m0 + i * FM + lane % FM;
+    constexpr int NO = OUT_T ? NF : MF, NQ = OUT_T ? MF : NF;
+    constexpr int DC = NQ * FM;        // D columns of the wave's block
+    constexpr int CH = DC / 4;         // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CH;       // staged rows per read instruction
+    constexpr int NT = FM / RPI;       // read instructions per batch
+    constexpr int REGION = FM * DC * 4;
+    constexpr int WPS = Cfg::STAGE_BYTES / REGION;  // wave blocks per stage array
+    static_assert(CH >= 16 && CH <= 64 && 64 % CH == 0, "staging shape");
+    // the blocks use the first one or two stage arrays (naming only those
+    // keeps the others out of the kernel when S does not need them)
+    static_assert(WPS >= 1 && (Cfg::WAVES + WPS - 1) / WPS <= 2 && S >= 2, "staging space");
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    char* const region = (wv < WPS ? st0 : st1) + (wv % WPS) * REGION;
+    auto slot = [&](int r, int chunk) __attribute__((always_inline)) -> f32x4* {
+        return reinterpret_cast<f32x4*>(region + r * (DC * 4) + ((chunk ^ (r & 15)) * 16));
     };
-    auto d_col = [&](int i, int j, int vg) __attribute__((always_inline)) {
-        return OUT_T ? m0 + wave_m0 + i * FM + 8 * vg + in_frag
-                     : n0 + wave_n0 + j * FM + 8 * vg + in_frag;
-    };
-    static_for<MF>([&](auto i_c) __attribute__((always_inline)) {
-        constexpr int i = decltype(i_c)::value;
-        f32x4 sum[NF][VG];
+    // first D row and column of the wave's block; the lane's 4 D columns
+    const int wr0 = OUT_T ? n0 + wave_n0 : m0 + wave_m0;
+    const int col = (OUT_T ? m0 + wave_m0 : n0 + wave_n0) + 4 * (lane % CH);
+    const bool col_vec = p.d_vec && col + 4 <= d_cols;
+    __syncthreads();  // every wave is done reading operands from the stage arrays
+    static_for<NO>([&](auto o_c) __attribute__((always_inline)) {
+        constexpr int o = decltype(o_c)::value;
+        f32x4 sum[NQ][VG];
 #pragma unroll
-        for (int j = 0; j < NF; ++j)
+        for (int q = 0; q < NQ; ++q) {
+            const int i = OUT_T ? q : o, j = OUT_T ? o : q;
 #pragma unroll
             for (int vg = 0; vg < VG; ++vg)
-                sum[j][vg] = f32x4{acc[i][j][4 * vg], acc[i][j][4 * vg + 1], acc[i][j][4 * vg + 2],
+                sum[q][vg] = f32x4{acc[i][j][4 * vg], acc[i][j][4 * vg + 1], acc[i][j][4 * vg + 2],
                                    acc[i][j][4 * vg + 3]};
-        f32x4 cv[NF][VG];
-        if (beta != 0.0f) {
-#pragma unroll
-            for (int j = 0; j < NF; ++j) {
-                const int row = d_row(i, j);
-                const bool row_ok = row < d_rows;
-                const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)(row_ok ? row : 0) * p.ldc;
-#pragma unroll
-                for (int vg = 0; vg < VG; ++vg) {
-                    const int col = d_col(i, j, vg);
-                    if (row_ok && p.c_vec && col + 4 <= d_cols) {
-                        cv[j][vg] = load4(crow + col);
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            cv[j][vg][s] = (row_ok && col + s < d_cols) ? to_f32(crow[col + s]) : 0.0f;
-                    }
-                }
-            }
         }
         if constexpr (SK) {
             for (int64_t c = c0; c < c1; ++c) {
                 const auto rsrc = part_rsrc(c);
-                f32x4 v[NF][VG];
+                f32x4 v[NQ][VG];
 #pragma unroll
-                for (int j = 0; j < NF; ++j)
+                for (int q = 0; q < NQ; ++q)
 #pragma unroll
                     for (int vg = 0; vg < VG; ++vg)
-                        v[j][vg] = __builtin_bit_cast(
+                        v[q][vg] = __builtin_bit_cast(
                             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       rsrc, part_index(i, j, vg) * 16, 0, CPOL_SC1));
+                                       rsrc,
+                                       part_index(OUT_T ? q : o, OUT_T ? o : q, vg) * 16, 0,
+                                       CPOL_SC1));
 #pragma unroll
-                for (int j = 0; j < NF; ++j)
+                for (int q = 0; q < NQ; ++q)
 #pragma unroll
-                    for (int vg = 0; vg < VG; ++vg) sum[j][vg] += v[j][vg];
+                    for (int vg = 0; vg < VG; ++vg) sum[q][vg] += v[q][vg];
             }
         }
+        // stage: the lane's row lane % FM, columns q*FM + 8*vg + in_frag
 #pragma unroll
-        for (int j = 0; j < NF; ++j) {
-            const int row = d_row(i, j);
-            if (row >= d_rows) continue;
-            OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int vg = 0; vg < VG; ++vg) {
-                const int col = d_col(i, j, vg);
-                f32x4 out = alpha * sum[j][vg];
-                if (beta != 0.0f) out += beta * cv[j][vg];
-                if constexpr (EPI) {
+            for (int vg = 0; vg < VG; ++vg)
+                *slot(lane % FM, (q * FM + 8 * vg + in_frag) / 4) = sum[q][vg];
+        // read back row-wise: lane holds chunk lane % CH of rows t*RPI + lane / CH
+        f32x4 val[NT];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        if (col + s < d_cols) out[s] = epilogue_op<OutT>(p, out[s], col + s);
-                }
-                if (p.d_vec && col + 4 <= d_cols) {
-                    store4(drow + col, out);
+        for (int t = 0; t < NT; ++t) val[t] = *slot(t * RPI + lane / CH, lane % CH);
+        const int row0 = wr0 + o * FM + lane / CH;
+        f32x4 cv[NT];
+        if (beta != 0.0f) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int row = row0 + t * RPI;
+                const bool row_ok = row < d_rows;
+                const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)(row_ok ? row : 0) * p.ldc;
+                if (row_ok && p.c_vec && col + 4 <= d_cols) {
+                    cv[t] = load4(crow + col);
                 } else {
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
+                        cv[t][s] = (row_ok && col + s < d_cols) ? to_f32(crow[col + s]) : 0.0f;
                 }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int row = row0 + t * RPI;
+            if (row >= d_rows) continue;
+            OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
+            f32x4 out = alpha * val[t];
+            if (beta != 0.0f) out += beta * cv[t];
+            if constexpr (EPI) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    if (col + s < d_cols) out[s] = epilogue_op<OutT>(p, out[s], col + s);
+            }
+            if (col_vec) {
+                store4(drow + col, out);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
             }
         }
     });
