@@ -345,6 +345,48 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def trace_summary(trace_csv: str, stats_csv: str, warmup: int, steps: int) -> int:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this
+    benchmark: rocprofv3's own per-kernel statistics, and for each step kernel
+    the mean over the timed steps' dispatches alone (the step runs every
+    workload once per step, so a step kernel's dispatches warmup .. warmup +
+    steps - 1 are the timed ones; later dispatches are the variant report and
+    the hot-cache rows)."""
+    import csv
+
+    with open(stats_csv) as f:
+        stats = list(csv.DictReader(f))
+    with open(trace_csv) as f:
+        trace = [r for r in csv.DictReader(f) if r.get("Kind") == "KERNEL_DISPATCH"]
+    per = {}
+    for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel (rocprofv3 --stats) | calls | average us | min us | max us | share % |")
+    print("|---|---|---|---|---|---|")
+    for r in stats[:12]:
+        print(f"| `{r['Name'][:150]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+              f"{float(r['Percentage']):.2f} |")
+    print()
+    print("| step workload | kernel | timed dispatches | mean us | median us |")
+    print("|---|---|---|---|---|")
+    for name in STEP_WORKLOADS:
+        w = workloads.WORKLOADS[name]
+        # the step kernel: the one with exactly warmup + steps + 1 + 23 dispatches
+        # whose name carries the workload's operand type
+        ktype = "DmaConfig<0," if w.dtype == "f32" else "DmaConfig<2,"
+        cands = [k for k, v in per.items() if ktype in k and len(v) >= warmup + steps]
+        cands.sort(key=lambda k: -sum(per[k]))
+        if not cands:
+            continue
+        k = cands[0]
+        timed = per[k][warmup:warmup + steps]
+        print(f"| {name} | `{k[:150]}` | {len(timed)} | {np.mean(timed):.1f} | "
+              f"{np.median(timed):.1f} |")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,7 +405,13 @@ def main(argv=None):
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
                          "a --copy-probe run into the HBM-traffic record, then exit")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
+                    help="summarize a rocprofv3 --kernel-trace --stats run of this benchmark "
+                         "(its kernel_trace.csv and kernel_stats.csv; pass that run's --steps "
+                         "and --warmup), then exit")
     args = ap.parse_args(argv)
+    if args.trace_summary:
+        return trace_summary(*args.trace_summary, args.warmup, args.steps)
     if args.ingest_pmc:
         return ingest_pmc(*args.ingest_pmc)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

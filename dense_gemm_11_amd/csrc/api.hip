@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void scale_c_kernel(GemmArgs p)
          e += (int64_t)gridDim.x * 256) {
         const int64_t row = e / p.N, col = e % p.N;
         const float v = (p.beta != 0.0f) ? p.beta * to_f32(C[row * p.ldc + col]) : 0.0f;
-        D[row * p.ldd + col] = from_f32<OutT>(epilogue_op<OutT>(p, v, (int)col));
+        D[row * p.ldd + col] = from_f32<OutT>(epilogue_op(p, v, bias_of<OutT>(p, (int)col)));
     }
 }
 

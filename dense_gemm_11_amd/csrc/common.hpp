@@ -116,22 +116,78 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
     return __builtin_bit_cast(bf16_t, (__bf16)x);
 }
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^(-x^2),
+// t = 1 / (1 + p x) for x >= 0, odd in x, |error| <= 1.5e-7.  Branch-free,
+// so the lanes of a wave never diverge over it.
+__device__ __forceinline__ float erf_approx(float x)
+{
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+    const float poly =
+        t * (0.254829592f +
+             t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.44269504088896341f);  // e^(-x^2)
+    return copysignf(1.0f - poly * e, x);
+}
+
 // Activation of the fused epilogue: ReLU max(x, 0), or GELU in its erf form
 // x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)); act is uniform across a launch.
 __device__ __forceinline__ float activate(float x, int act)
 {
     if (act == EPI_ACT_RELU) return x > 0.0f ? x : 0.0f;
-    if (act == EPI_ACT_GELU) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    if (act == EPI_ACT_GELU) return 0.5f * x * (1.0f + erf_approx(x * 0.70710678118654752f));
     return x;
 }
 
-// bias + activation + clamp on one value (after alpha*acc + beta*C).
+// Bias of D column col (0 without a bias); col must be inside D.
 template <typename OutT>
-__device__ __forceinline__ float epilogue_op(const GemmArgs& p, float v, int col)
+__device__ __forceinline__ float bias_of(const GemmArgs& p, int col)
 {
-    if (p.bias) v += to_f32(static_cast<const OutT*>(p.bias)[col]);
-    v = activate(v, p.act);
+    return p.bias ? to_f32(static_cast<const OutT*>(p.bias)[col]) : 0.0f;
+}
+
+// bias + activation + clamp on one value (after alpha*acc + beta*C).
+__device__ __forceinline__ float epilogue_op(const GemmArgs& p, float v, float bias)
+{
+    v = activate(v + bias, p.act);
     if (p.clamp) v = fminf(fmaxf(v, p.clamp_lo), p.clamp_hi);
+    return v;
+}
+
+// The same on four values with the activation and the clamp fixed at
+// compile time (no branches at all).
+template <int ACT, bool CLAMP>
+__device__ __forceinline__ f32x4 epilogue_fixed4(const GemmArgs& p, f32x4 v, const float (&bias)[4])
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float x = v[s] + bias[s];
+        if constexpr (ACT == EPI_ACT_RELU) x = x > 0.0f ? x : 0.0f;
+        if constexpr (ACT == EPI_ACT_GELU) x = 0.5f * x * (1.0f + erf_approx(x * 0.70710678118654752f));
+        if constexpr (CLAMP) x = fminf(fmaxf(x, p.clamp_lo), p.clamp_hi);
+        v[s] = x;
+    }
+    return v;
+}
+
+// The same on four values: one uniform branch per step for the group.
+__device__ __forceinline__ f32x4 epilogue_op4(const GemmArgs& p, f32x4 v, const float (&bias)[4])
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) v[s] += bias[s];
+    if (p.act == EPI_ACT_RELU) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] = v[s] > 0.0f ? v[s] : 0.0f;
+    } else if (p.act == EPI_ACT_GELU) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            v[s] = 0.5f * v[s] * (1.0f + erf_approx(v[s] * 0.70710678118654752f));
+    }
+    if (p.clamp) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[s] = fminf(fmaxf(v[s], p.clamp_lo), p.clamp_hi);
+    }
     return v;
 }
 

@@ -675,6 +675,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     const int wr0 = OUT_T ? n0 + wave_n0 : m0 + wave_m0;
     const int col = (OUT_T ? m0 + wave_m0 : n0 + wave_n0) + 4 * (lane % CH);
     const bool col_vec = p.d_vec && col + 4 <= d_cols;
+    // whole tile inside D with 16-byte rows: no per-row or per-element checks
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && p.d_vec &&
+                          (beta == 0.0f || p.c_vec);
+    // the lane's columns are the same in every batch: their bias is read once
+    float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            if (col + s < d_cols) bias4[s] = bias_of<OutT>(p, col + s);
+    }
     __syncthreads();  // every wave is done reading operands from the stage arrays
     static_for<NO>([&](auto o_c) __attribute__((always_inline)) {
         constexpr int o = decltype(o_c)::value;
@@ -712,45 +722,69 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 #pragma unroll
             for (int vg = 0; vg < VG; ++vg)
                 *slot(lane % FM, (q * FM + 8 * vg + in_frag) / 4) = sum[q][vg];
-        // read back row-wise: lane holds chunk lane % CH of rows t*RPI + lane / CH
-        f32x4 val[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) val[t] = *slot(t * RPI + lane / CH, lane % CH);
+        // read back row-wise: lane holds chunk lane % CH of rows t*RPI + lane / CH.
+        // Runtime loops keep this code small: the epilogue runs once per tile
+        // from instruction memory, and every copy of an unrolled body is
+        // fetched again for each tile.
         const int row0 = wr0 + o * FM + lane / CH;
-        f32x4 cv[NT];
-        if (beta != 0.0f) {
-#pragma unroll
+        // interior tiles: the activation and the clamp are compile-time
+        // choices of the loop, so its body has no branches
+        auto interior_rows = [&](auto act_c, auto clamp_c) __attribute__((always_inline)) {
+#pragma unroll 4
+            for (int t = 0; t < NT; ++t) {
+                const int64_t row = row0 + t * RPI;
+                f32x4 out = alpha * *slot(t * RPI + lane / CH, lane % CH);
+                if (beta != 0.0f)
+                    out += beta * load4(reinterpret_cast<const OutT*>(p.C) + row * p.ldc + col);
+                if constexpr (EPI)
+                    out = epilogue_fixed4<decltype(act_c)::value, decltype(clamp_c)::value>(p, out,
+                                                                                          bias4);
+                store4(reinterpret_cast<OutT*>(p.D) + row * p.ldd + col, out);
+            }
+        };
+        using A0 = std::integral_constant<int, EPI_ACT_NONE>;
+        using A1 = std::integral_constant<int, EPI_ACT_RELU>;
+        using A2 = std::integral_constant<int, EPI_ACT_GELU>;
+        using C0 = std::false_type;
+        using C1 = std::true_type;
+        if (interior) {
+            if constexpr (EPI) {
+                if (p.act == EPI_ACT_RELU) {
+                    if (p.clamp) interior_rows(A1{}, C1{}); else interior_rows(A1{}, C0{});
+                } else if (p.act == EPI_ACT_GELU) {
+                    if (p.clamp) interior_rows(A2{}, C1{}); else interior_rows(A2{}, C0{});
+                } else {
+                    if (p.clamp) interior_rows(A0{}, C1{}); else interior_rows(A0{}, C0{});
+                }
+            } else {
+                interior_rows(A0{}, C0{});
+            }
+        } else {
+#pragma unroll 1
             for (int t = 0; t < NT; ++t) {
                 const int row = row0 + t * RPI;
-                const bool row_ok = row < d_rows;
-                const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)(row_ok ? row : 0) * p.ldc;
-                if (row_ok && p.c_vec && col + 4 <= d_cols) {
-                    cv[t] = load4(crow + col);
+                if (row >= d_rows) continue;
+                f32x4 out = alpha * *slot(t * RPI + lane / CH, lane % CH);
+                if (beta != 0.0f) {
+                    const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)row * p.ldc;
+                    f32x4 cv;
+                    if (p.c_vec && col + 4 <= d_cols) {
+                        cv = load4(crow + col);
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) cv[s] = col + s < d_cols ? to_f32(crow[col + s]) : 0.0f;
+                    }
+                    out += beta * cv;
+                }
+                if constexpr (EPI) out = epilogue_op4(p, out, bias4);
+                OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
+                if (col_vec) {
+                    store4(drow + col, out);
                 } else {
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        cv[t][s] = (row_ok && col + s < d_cols) ? to_f32(crow[col + s]) : 0.0f;
+                        if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
                 }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int row = row0 + t * RPI;
-            if (row >= d_rows) continue;
-            OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
-            f32x4 out = alpha * val[t];
-            if (beta != 0.0f) out += beta * cv[t];
-            if constexpr (EPI) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    if (col + s < d_cols) out[s] = epilogue_op<OutT>(p, out[s], col + s);
-            }
-            if (col_vec) {
-                store4(drow + col, out);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
             }
         }
     });
