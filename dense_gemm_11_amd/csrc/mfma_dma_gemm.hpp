@@ -663,11 +663,15 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     constexpr int REGION = FM * DC * 4;
     constexpr int WPS = Cfg::STAGE_BYTES / REGION;  // wave blocks per stage array
     static_assert(CH >= 16 && CH <= 64 && 64 % CH == 0, "staging shape");
-    // the blocks use the first one or two stage arrays (naming only those
-    // keeps the others out of the kernel when S does not need them)
-    static_assert(WPS >= 1 && (Cfg::WAVES + WPS - 1) / WPS <= 2 && S >= 2, "staging space");
+    // the blocks use the first NSA stage arrays (naming only those keeps the
+    // others out of the kernel when S does not need them)
+    constexpr int NSA = WPS >= 1 ? (Cfg::WAVES + WPS - 1) / WPS : 99;
+    static_assert(NSA <= S && NSA <= 3, "staging space");
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    char* const region = (wv < WPS ? st0 : st1) + (wv % WPS) * REGION;
+    char* base = st0;
+    if constexpr (NSA > 1) base = wv / WPS == 1 ? st1 : base;
+    if constexpr (NSA > 2) base = wv / WPS == 2 ? st2 : base;
+    char* const region = base + (wv % WPS) * REGION;
     auto slot = [&](int r, int chunk) __attribute__((always_inline)) -> f32x4* {
         return reinterpret_cast<f32x4*>(region + r * (DC * 4) + ((chunk ^ (r & 15)) * 16));
     };
