@@ -345,6 +345,86 @@ def ingest_pmc(fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
+def fit_pipeline_model(rows):
+    """Fit the pipeline-depth model of "High-Performance FP16 GEMM on NVIDIA
+    Ada Lovelace via CUTLASS and WMMA" (methodology: efficiency S/(S + kappa),
+    extended by an occupancy cap gamma(S)) to measured rows.
+
+    Each row: family (dtype, tile, BK), d = K-steps of lookahead (the depth
+    that hides copy latency: S with a late barrier, S-1 with a half-way one),
+    occ = resident workgroups per compute unit, tflops.  Model:
+        T = T_inf(family) * d / (d + kappa) * gamma,
+        gamma = (occ / occ_max(family)) ** eta   (1 at the family's best occupancy).
+    kappa is shared by a dtype's families, fitted with gamma = 1 on the rows
+    at their family's best occupancy (T_inf by least squares for each kappa
+    on a grid); eta from the remaining rows.  Returns per-dtype parameters
+    and per-row predictions of both the simple and the extended model."""
+    out = {}
+    for dt in sorted({r["dtype"] for r in rows}):
+        rs = [r for r in rows if r["dtype"] == dt]
+        fams = sorted({r["family"] for r in rs})
+        occ_max = {f: max(r["occ"] for r in rs if r["family"] == f) for f in fams}
+        full = [r for r in rs if r["occ"] == occ_max[r["family"]]]
+
+        def tinf_for(kappa):
+            t = {}
+            for f in fams:
+                xs = [r["d"] / (r["d"] + kappa) for r in full if r["family"] == f]
+                ys = [r["tflops"] for r in full if r["family"] == f]
+                t[f] = float(np.dot(xs, ys) / np.dot(xs, xs)) if xs else float("nan")
+            return t
+
+        best = None
+        for kappa in np.linspace(0.0, 4.0, 401):
+            t = tinf_for(kappa)
+            err = sum((r["tflops"] - t[r["family"]] * r["d"] / (r["d"] + kappa)) ** 2
+                      for r in full)
+            if best is None or err < best[0]:
+                best = (err, float(kappa), t)
+        _, kappa, tinf = best
+        capped = [r for r in rs if r["occ"] < occ_max[r["family"]]]
+        eta = 0.0
+        if capped:
+            # least squares on log(T / simple) = eta * log(occ / occ_max)
+            xs = [np.log(r["occ"] / occ_max[r["family"]]) for r in capped]
+            ys = [np.log(r["tflops"] / (tinf[r["family"]] * r["d"] / (r["d"] + kappa)))
+                  for r in capped]
+            eta = float(np.dot(xs, ys) / np.dot(xs, xs))
+        preds = []
+        for r in rs:
+            simple = tinf[r["family"]] * r["d"] / (r["d"] + kappa)
+            ext = simple * (r["occ"] / occ_max[r["family"]]) ** eta
+            preds.append({"variant": r["variant"], "d": r["d"], "occ": r["occ"],
+                          "measured": round(r["tflops"], 1), "simple": round(simple, 1),
+                          "simple_err": round(simple / r["tflops"] - 1.0, 4),
+                          "extended": round(ext, 1),
+                          "extended_err": round(ext / r["tflops"] - 1.0, 4)})
+        out[dt] = {"kappa": round(kappa, 3), "eta": round(eta, 3),
+                   "t_inf": {f: round(v, 1) for f, v in tinf.items()},
+                   "occ_max": occ_max, "rows": preds}
+    return out
+
+
+def pipeline_sweep(g, h, reps: int = 10) -> dict:
+    """Time every direct-to-LDS variant (forced) on the NN step shapes: bf16
+    8192^3 and fp32 4096^3, one buffer set, after >= 50 ms of warm-up each."""
+    rows = []
+    for i, name, dt, tile in g.variants():
+        if "_dma" not in name:
+            continue
+        wname = "bf16_8192" if dt == g.GEMM_DTYPE_BF16_F32 else "fp32_4096"
+        stages, ahead = g.gemm_variant_pipeline(i)
+        occ = g.gemm_variant_occupancy(i)
+        r = time_extra(g, h, wname, name, reps=reps, warmup=3)
+        rows.append({"variant": name, "dtype": "bf16" if dt == g.GEMM_DTYPE_BF16_F32 else "f32",
+                     "family": f"{'bf16' if dt else 'f32'}_{tile[0]}x{tile[1]}x{tile[2]}",
+                     "stages": stages, "d": ahead, "occ": occ, "kernel_ms": r["kernel_ms"],
+                     "tflops": r["tflops"], "workload": wname})
+        print(f"[sweep] {name} S={stages} ahead={ahead} occ={occ} {r['kernel_ms']} ms "
+              f"{r['tflops']} TFLOP/s", file=sys.stderr, flush=True)
+    return {"rows": rows, "model": fit_pipeline_model(rows)}
+
+
 def trace_summary(trace_csv: str, stats_csv: str, warmup: int, steps: int) -> int:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of this
     benchmark: rocprofv3's own per-kernel statistics, and for each step kernel
@@ -405,6 +485,9 @@ def main(argv=None):
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
                          "a --copy-probe run into the HBM-traffic record, then exit")
+    ap.add_argument("--pipeline-sweep", action="store_true",
+                    help="time every direct-to-LDS variant on the NN step shapes, fit the "
+                         "pipeline-depth model, print one JSON object, then exit")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
                     help="summarize a rocprofv3 --kernel-trace --stats run of this benchmark "
                          "(its kernel_trace.csv and kernel_stats.csv; pass that run's --steps "
@@ -425,6 +508,10 @@ def main(argv=None):
     import dense_gemm_11_amd as g
     torch.cuda.set_device(0)
     h = g.gemm_create()
+    if args.pipeline_sweep:
+        print(json.dumps(pipeline_sweep(g, h)), flush=True)
+        g.gemm_destroy(h)
+        return 0
     # a stream-K workspace (the automatic policy keeps the two step workloads
     # on whole tiles; it splits the few-tile, long-K extra row)
     workspace = g.attach_workspace(h)

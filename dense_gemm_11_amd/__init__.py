@@ -42,7 +42,8 @@ EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
            "gemm_variant_count", "gemm_variant_name", "gemm_variant_dtype",
            "gemm_variant_tile", "gemm_set_variant", "gemm_last_variant",
            "gemm_select_variant", "gemm_stream_k_workspace_bytes", "gemm_set_workspace",
-           "gemm_set_stream_k", "gemm_last_stream_k", "gemm_run_epilogue")
+           "gemm_set_stream_k", "gemm_last_stream_k", "gemm_run_epilogue",
+           "gemm_variant_pipeline", "gemm_variant_occupancy")
 
 
 class GemmEpilogue(ctypes.Structure):
@@ -105,6 +106,10 @@ def _load():
     lib.gemm_variant_tile.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                       ctypes.POINTER(i32)]
     lib.gemm_variant_tile.restype = i32
+    lib.gemm_variant_pipeline.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.gemm_variant_pipeline.restype = i32
+    lib.gemm_variant_occupancy.argtypes = [i32]
+    lib.gemm_variant_occupancy.restype = i32
     lib.gemm_set_variant.argtypes = [vp, i32]
     lib.gemm_set_variant.restype = i32
     lib.gemm_last_variant.argtypes = [vp]
@@ -176,6 +181,19 @@ def gemm_variant_tile(i: int):
     if s != GEMM_OK:
         raise GemmError(s, "gemm_variant_tile")
     return bm.value, bn.value, bk.value
+
+
+def gemm_variant_pipeline(i: int):
+    """(stages, ahead) of variant i."""
+    st, ah = ctypes.c_int(), ctypes.c_int()
+    s = lib.gemm_variant_pipeline(i, ctypes.byref(st), ctypes.byref(ah))
+    if s != GEMM_OK:
+        raise GemmError(s, "gemm_variant_pipeline")
+    return st.value, ah.value
+
+
+def gemm_variant_occupancy(i: int) -> int:
+    return lib.gemm_variant_occupancy(i)
 
 
 def gemm_set_variant(h, i: int) -> int:

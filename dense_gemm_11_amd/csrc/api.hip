@@ -139,28 +139,41 @@ int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
 
 // Time of one K-step of a tile of variant v for a workgroup alone on a
 // compute unit, in microseconds: measured on MI355X for 256x256x32 steps
-// (bf16 0.85 us, fp32 7.3 us; 8192^3 and 4096^3 runs) and scaled by the
-// step's FLOPs for other tiles (128x128x32 bf16 measured 0.245 us).
+// (bf16 0.85 us with 3 steps of lookahead, fp32 7.3 us with 2; 8192^3 and
+// 4096^3 runs), scaled by the step's FLOPs for other tiles (128x128x32 bf16
+// measured 0.245 us) and by the pipeline efficiency d/(d + kappa) of the
+// variant's lookahead d relative to the measured one ("High-Performance FP16
+// GEMM on NVIDIA Ada Lovelace", methodology: efficiency S/(S + kappa)).
+// kappa was fitted to the sweep of every direct-to-LDS variant on MI355X:
+// 1.27 steps for bf16; 0 for fp32, whose long steps hide the copies at any
+// depth.  (The occupancy part of that model is data_parallel_us's share.)
 double step_us(const Variant& v)
 {
-    const double base = v.dtype == GEMM_DTYPE_BF16_F32 ? 0.85 : 7.3;
-    return base * ((double)v.bm * v.bn * v.bk) / (256.0 * 256.0 * 32.0);
+    const bool bf16 = v.dtype == GEMM_DTYPE_BF16_F32;
+    const double base = bf16 ? 0.85 : 7.3;
+    const double kappa = bf16 ? 1.27 : 0.0, d_ref = bf16 ? 3.0 : 2.0;
+    const double d = std::max(1, v.ahead);
+    const double eff = (d / (d + kappa)) / (d_ref / (d_ref + kappa));
+    return base * ((double)v.bm * v.bn * v.bk) / (256.0 * 256.0 * 32.0) / eff;
 }
 
-int variant_occupancy(const Variant& v)
+// Workgroups per compute unit of v's stream-K kernel (sk = true) or of its
+// data-parallel kernel, from the HIP occupancy query (cached per variant).
+int variant_occupancy(const Variant& v, bool sk = true)
 {
-    static int cache[64] = {0};
+    static int cache[2][64] = {};
     const int vid = (int)(&v - table().data());
-    if (!v.sk_occ || vid < 0 || vid >= 64) return v.bm * v.bn >= 256 * 256 ? 1 : 2;
-    if (cache[vid] == 0) cache[vid] = std::max(1, v.sk_occ());
-    return cache[vid];
+    const OccFn f = sk ? v.sk_occ : v.occ;
+    if (!f || vid < 0 || vid >= 64) return v.bm * v.bn >= 256 * 256 ? 1 : 2;
+    if (cache[sk][vid] == 0) cache[sk][vid] = std::max(1, f());
+    return cache[sk][vid];
 }
 
 // Estimated time of the data-parallel launch: waves of concurrently resident
 // tiles, each K-step slowed by the workgroups sharing its compute unit.
 double data_parallel_us(const Variant& v, int64_t M, int64_t N, int64_t K)
 {
-    const int64_t cus = device_cus(), occ = variant_occupancy(v);
+    const int64_t cus = device_cus(), occ = variant_occupancy(v, false);
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
     const int64_t waves = ceil_div(tiles, cus * occ);
     const double share = std::min<double>((double)occ, std::max(1.0, (double)tiles / cus));
@@ -293,6 +306,22 @@ gemm_status_t gemm_variant_tile(int id, int* bm, int* bn, int* bk)
     if (bn) *bn = v.bn;
     if (bk) *bk = v.bk;
     return GEMM_OK;
+}
+
+gemm_status_t gemm_variant_pipeline(int id, int* stages, int* ahead)
+{
+    if (id < 0 || id >= gemm_variant_count()) return GEMM_ERR_INVALID_VALUE;
+    const dg::Variant& v = dg::table()[id];
+    if (stages) *stages = v.stages;
+    if (ahead) *ahead = v.ahead;
+    return GEMM_OK;
+}
+
+int gemm_variant_occupancy(int id)
+{
+    if (id < 0 || id >= gemm_variant_count()) return -1;
+    const int n = dg::table()[id].occ();
+    return n > 0 ? n : -1;
 }
 
 gemm_status_t gemm_set_variant(gemm_handle_t h, int id)

@@ -9,7 +9,7 @@ using Bf16Big32 = MfmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 2>;
 using Bf16Mid = MfmaConfig<MFMA_BF16_16x16x32, 128, 128, 64, 2, 2>;
 
 #define BF16_VARIANT(NAME, CFG) \
-    {NAME, 1, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(mfma_gemm_kernel, CFG)}
+    {NAME, 1, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, 2, 1, DG_FN_TABLE(mfma_gemm_kernel, CFG)}
 
 const Variant* bf16_variant_table(int* count)
 {

@@ -18,6 +18,7 @@ using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
 
 #define BF16_DMA_SK_VARIANT(NAME, CFG)                                                      \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES,       \
+     CFG::S, CFG::AHEAD,                                                                  \
      DG_FN_TABLE(dma_gemm_kernel, CFG), DG_SK_TABLE(dma_gemm_kernel, CFG),                \
      DG_NN_T_FN(dma_gemm_kernel, CFG), bf16_out_table(CFG::BM)}
 

@@ -10,6 +10,7 @@ using F32Dma128s3L = DmaConfig<MFMA_F32_32x32x2, 128, 128, 16, 2, 2, 3, true>;
 
 #define F32_DMA_SK_VARIANT(NAME, CFG)                                                       \
     {NAME, 0, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES,       \
+     CFG::S, CFG::AHEAD,                                                                  \
      DG_FN_TABLE(dma_gemm_kernel, CFG), DG_SK_TABLE(dma_gemm_kernel, CFG)}
 
 const Variant* f32dma_variant_table(int* count)

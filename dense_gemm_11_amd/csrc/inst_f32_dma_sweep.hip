@@ -10,7 +10,8 @@ using F32Dma256s3L = DmaConfig<MFMA_F32_32x32x2, 256, 256, 16, 2, 2, 3, true>;
 using F32Dma256s4L = DmaConfig<MFMA_F32_32x32x2, 256, 256, 16, 2, 2, 4, true>;
 
 #define F32_DMA_VARIANT(NAME, CFG) \
-    {NAME, 0, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(dma_gemm_kernel, CFG)}
+    {NAME, 0, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, CFG::S, CFG::AHEAD, \
+     DG_FN_TABLE(dma_gemm_kernel, CFG)}
 
 const Variant* f32dma_sweep_variant_table(int* count)
 {

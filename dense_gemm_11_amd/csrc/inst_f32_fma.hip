@@ -7,7 +7,7 @@ namespace dg {
 using FmaBig = FmaConfig<128, 128, 8>;
 
 #define F32V_VARIANT(NAME, CFG) \
-    {NAME, 0, KIND_VECTOR_FMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(fma_gemm_kernel, CFG)}
+    {NAME, 0, KIND_VECTOR_FMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, 2, 1, DG_FN_TABLE(fma_gemm_kernel, CFG)}
 
 const Variant* f32fma_variant_table(int* count)
 {

@@ -8,7 +8,7 @@ using F32Big = MfmaConfig<MFMA_F32_32x32x2, 256, 256, 32, 2, 2>;
 using F32Mid = MfmaConfig<MFMA_F32_32x32x2, 128, 128, 32, 2, 2>;
 
 #define F32M_VARIANT(NAME, CFG) \
-    {NAME, 0, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, DG_FN_TABLE(mfma_gemm_kernel, CFG)}
+    {NAME, 0, KIND_MFMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, 2, 1, DG_FN_TABLE(mfma_gemm_kernel, CFG)}
 
 const Variant* f32mfma_variant_table(int* count)
 {

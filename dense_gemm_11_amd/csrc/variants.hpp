@@ -16,7 +16,10 @@ struct Variant {
     int dtype;   // 0 = fp32 operands, 1 = bf16 operands
     int kind;    // VariantKind
     int bm, bn, bk, threads, lds_bytes;
+    int stages;  // LDS stages in the ring
+    int ahead;   // K-steps between a step's copy into LDS and its use
     LaunchFn fn[2][2][2];  // [wide access][A k-contiguous][B k-contiguous]
+    OccFn occ;             // occupancy of the NN wide-access kernel
     LaunchFn sk_fn[2][2];  // stream-K instantiations (wide access only), or null
     OccFn sk_occ;          // occupancy of the stream-K kernel, or null
     // NN problems as D^T = B^T A^T: the kernel with A mn-contiguous, B
@@ -80,7 +83,7 @@ const Variant* f32dma_sweep_variant_table(int* count);
 
 }  // namespace dg
 
-// Fill Variant::fn for a kernel template K<Cfg, A_KC, B_KC, ALIGNED>.
+// Fill Variant::fn and Variant::occ for a kernel template K<Cfg, A_KC, B_KC, ALIGNED>.
 #define DG_FN_TABLE(KERNEL, CFG)                                                        \
     {                                                                                   \
         {{dg::launch_kernel<KERNEL<CFG, false, false, false>, CFG::THREADS>,            \
@@ -93,7 +96,7 @@ const Variant* f32dma_sweep_variant_table(int* count);
             {dg::launch_kernel<KERNEL<CFG, true, false, true>, CFG::THREADS>,           \
              dg::launch_kernel<KERNEL<CFG, true, true, true>, CFG::THREADS>}            \
         }                                                                               \
-    }
+    }, &dg::occupancy<KERNEL<CFG, true, false, true>, CFG::THREADS>
 
 // Stream-K entries for a direct-to-LDS kernel template K<Cfg, A_KC, B_KC, ALIGNED, SK>.
 #define DG_SK_TABLE(KERNEL, CFG)                                                    \

@@ -176,6 +176,19 @@ int gemm_variant_dtype(int id);
 /* Tile shape of variant `id` into bm/bn/bk (any may be NULL). */
 gemm_status_t gemm_variant_tile(int id, int* bm, int* bn, int* bk);
 
+/* Software pipeline of variant `id`: LDS stages in its ring (*stages) and
+ * K-steps between a step's copy into LDS and its first use (*ahead; S for a
+ * barrier late in the step, S-1 for one half way).  Any may be NULL.
+ * GEMM_ERR_INVALID_VALUE for an unknown id. */
+gemm_status_t gemm_variant_pipeline(int id, int* stages, int* ahead);
+
+/* Workgroups of variant `id` (its NN kernel with 16-byte access) that fit on
+ * one compute unit of the current device, from the HIP occupancy query: the
+ * occupancy the pipeline depth trades against ("High-Performance FP16 GEMM
+ * on NVIDIA Ada Lovelace", key results).  -1 for an unknown id or when the
+ * device cannot be queried. */
+int gemm_variant_occupancy(int id);
+
 /* Force variant `id` for later gemm_run calls on h; -1 restores automatic
  * selection.  GEMM_ERR_INVALID_VALUE for an unknown id or NULL handle. */
 gemm_status_t gemm_set_variant(gemm_handle_t h, int id);

@@ -206,3 +206,39 @@ def test_epilogue_arguments_validated(h):
     assert run_epi(h, E(None, g.GEMM_ACT_GELU, 0, 0.0, 0.0), M=0, A=None, B=None,
                    D=None) == g.GEMM_OK
     assert run_epi(None, E(None, g.GEMM_ACT_GELU, 0, 0.0, 0.0)) == g.GEMM_ERR_INVALID_VALUE
+
+
+def test_variant_pipeline_query():
+    """Every variant reports its ring depth and lookahead; the direct-to-LDS
+    names carry the stage count (s<S>) and a late barrier looks S steps ahead,
+    a half-way one S - 1."""
+    for i, name, _, _ in g.variants():
+        stages, ahead = g.gemm_variant_pipeline(i)
+        assert 1 <= ahead <= stages <= 5
+        if "_dma" in name:
+            tag = name.split("_s")[-1]
+            assert int(tag.split("_")[0]) == stages
+            assert ahead == (stages if name.endswith("_late") else stages - 1)
+    with pytest.raises(g.GemmError):
+        g.gemm_variant_pipeline(g.gemm_variant_count())
+    assert g.gemm_variant_occupancy(-1) == -1
+
+
+def test_pipeline_model_fit_recovers_parameters():
+    """The bench's fit of T = T_inf * d/(d + kappa) * (occ/occ_max)^eta
+    recovers the parameters of synthetic measurements, and the simple model
+    (eta = 0) overestimates the occupancy-capped point by the cap."""
+    import bench
+    rows = []
+    for fam, tinf, occ_max in (("bf16_a", 1500.0, 1), ("bf16_b", 1200.0, 2)):
+        for d in (2, 3, 4):
+            rows.append(dict(variant=f"{fam}{d}", dtype="bf16", family=fam, d=d, occ=occ_max,
+                             tflops=tinf * d / (d + 0.8)))
+    rows.append(dict(variant="capped", dtype="bf16", family="bf16_b", d=3, occ=1,
+                     tflops=1200.0 * 3 / 3.8 * 0.5 ** 0.4))
+    m = bench.fit_pipeline_model(rows)["bf16"]
+    assert abs(m["kappa"] - 0.8) < 0.011 and abs(m["eta"] - 0.4) < 0.01
+    assert abs(m["t_inf"]["bf16_a"] - 1500.0) < 1.0
+    capped = [r for r in m["rows"] if r["variant"] == "capped"][0]
+    assert abs(capped["extended_err"]) < 0.01
+    assert abs(capped["simple_err"] - (0.5 ** -0.4 - 1.0)) < 0.01
