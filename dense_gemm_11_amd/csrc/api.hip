@@ -186,40 +186,48 @@ double data_parallel_us(const Variant& v, int64_t M, int64_t N, int64_t K)
 // section 5): every workgroup that ends inside a tile writes a BM x BN fp32
 // partial that the tile's finisher reads back (device-scope traffic, taken
 // at 3 TB/s), and a finisher reduces its contributors one after another (one
-// memory round trip, ~1.5 us, per fragment row and contributor).  The grid
-// is chosen among 2, 4, 8, ... workgroups per tile (at least one per tile,
-// since the kernel gives a workgroup at most one tile's iterations, and at
-// most the device's workgroup slots); mode 1 takes the best of these
-// regardless, automatic mode only when it beats the data-parallel estimate
-// `dp_us` by a fifth.
+// memory round trip, ~1.5 us, per fragment row and contributor).  Candidate
+// grids: every resident workgroup slot when there are fewer slots than two
+// per tile (each workgroup then spans more than a tile; the kernel takes at
+// most two tiles' worth, so never fewer than half the tiles), and 2, 4, 8,
+// ... workgroups per tile up to the slots.  Workgroups sharing a compute
+// unit share its matrix cores.  Mode 1 takes the best candidate regardless,
+// automatic mode only when it beats the data-parallel estimate `dp_us` by a
+// fifth.
 int stream_k_grid(const Variant& v, int64_t M, int64_t N, int64_t K, int mode, size_t ws_bytes,
                   double dp_us, double* est_us = nullptr)
 {
     if (mode == 0 || !v.sk_occ || ws_bytes == 0) return 0;
-    const int64_t slots = std::min<int64_t>((int64_t)device_cus() * variant_occupancy(v), SK_MAX_WG);
+    const int64_t cus = device_cus();
+    const int64_t slots = std::min<int64_t>(cus * variant_occupancy(v), SK_MAX_WG);
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, v.bn);
     const int64_t nk = ceil_div(K, v.bk);
     const int64_t W = tiles * nk;
     const double tile_bytes = (double)v.bm * v.bn * sizeof(float);
     const int mf = v.bm / 2 / 32;  // fragment rows per wave (2x2 waves, 32-row fragments)
+    int64_t cand[24];
+    int nc = 0;
+    if (slots < 2 * tiles) cand[nc++] = std::max(slots, ceil_div(tiles, 2));
+    for (int64_t g = 2 * tiles; g <= slots && nc < 24; g *= 2) cand[nc++] = g;
     int64_t best_g = 0;
     double best_us = 0.0;
-    for (int64_t g = 2 * tiles;; g *= 2) {
-        const int64_t gg = std::min<int64_t>(std::min(g, slots), W / 4);
-        if (gg < tiles || gg < 2) break;
+    for (int i = 0; i < nc; ++i) {
+        const int64_t gg = std::min<int64_t>(cand[i], W / 4);
+        // each workgroup's range within two tiles' worth of iterations
+        if (gg < 2 || gg > SK_MAX_WG || ceil_div(W, gg) > 2 * nk) continue;
         const size_t need = SK_FLAG_BYTES + (size_t)gg * v.bm * v.bn * sizeof(float);
-        if (need <= ws_bytes) {
-            const int64_t per = ceil_div(W, gg);
-            const int64_t splits = ceil_div(nk, W / gg);  // workgroups meeting one tile
-            const double contrib = (double)std::max<int64_t>(gg - tiles, 0);
-            const double us = per * step_us(v) + 2.0 * contrib * tile_bytes / 3e12 * 1e6 +
-                              (double)(splits - 1) * mf * 1.5 + 5.0;
-            if (best_g == 0 || us < best_us) {
-                best_g = gg;
-                best_us = us;
-            }
+        if (need > ws_bytes) continue;
+        const int64_t per = ceil_div(W, gg);
+        // workgroups meeting one tile, and partial sums written and read back
+        const int64_t splits = gg >= tiles ? ceil_div(nk, W / gg) : 2;
+        const double contrib = (double)(gg >= tiles ? gg - tiles : gg - 1);
+        const double share = std::max(1.0, (double)std::min(gg, slots) / cus);
+        const double us = per * step_us(v) * share + 2.0 * contrib * tile_bytes / 3e12 * 1e6 +
+                          (double)(splits - 1) * mf * 1.5 + 5.0;
+        if (best_g == 0 || us < best_us) {
+            best_g = gg;
+            best_us = us;
         }
-        if (gg != g) break;  // capped: larger grids give the same one
     }
     if (best_g == 0) return 0;
     if (mode < 0 && !(best_us < 0.8 * dp_us)) return 0;

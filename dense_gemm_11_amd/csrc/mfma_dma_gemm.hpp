@@ -801,19 +801,23 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
         epilogue(tm, tn, 0, 0);
     } else {
         // Stream-K ("GEMM on NVIDIA GPUs", section 5: split-K partial sums
-        // P^(s) = sum over a K range, reduced afterwards).  The grid's G >=
-        // tiles workgroups split the W = tiles * nk_all (tile, K-step)
-        // iterations evenly: workgroup g takes [g*W/G, (g+1)*W/G), at most one
-        // tile's worth, so it meets at most two tiles: the end of one and the
-        // start of the next.  A tile is finished by the workgroup that reaches
-        // its last K-step; every other workgroup touching the tile ends its
-        // range inside it, stores its partial sums to its own workspace slot
-        // and raises its flag.  A workgroup does that contributing segment
-        // first, so no contribution waits behind another tile's fix-up.  The
-        // finisher waits for the lower-numbered contributors, adds their
-        // partials in workgroup (= K) order, so the result is reproducible,
-        // and runs the epilogue.  Contributions are published before any wait,
-        // so the waits cannot deadlock; they are bounded as well.
+        // P^(s) = sum over a K range, reduced afterwards).  The grid's G
+        // workgroups split the W = tiles * nk_all (tile, K-step) iterations
+        // evenly: workgroup g takes [g*W/G, (g+1)*W/G).  Its range is the
+        // tail of a first tile, a whole tile, and the head of a last tile.  A
+        // tile is finished by the workgroup that reaches its last K-step;
+        // every other workgroup touching the tile ends its range inside it,
+        // stores its partial sums to its own workspace slot and raises its
+        // flag (a workgroup contributes to at most one tile: the one its
+        // range ends in).  A workgroup does that contributing segment first
+        // and its whole tiles next, so no contribution waits behind another
+        // tile's fix-up; the finishing segment comes last.  The finisher
+        // waits for the lower-numbered contributors, adds their partials in
+        // workgroup (= K) order, so the result is reproducible, and runs the
+        // epilogue.  Contributions are published before any wait, and a
+        // finisher only waits for lower-numbered workgroups, which were
+        // dispatched before it, so the waits cannot deadlock; they are
+        // bounded as well.
         const int64_t W = (int64_t)p.tiles_m * p.tiles_n * nk_all;
         const int64_t G = gridDim.x, g = blockIdx.x;
         const int64_t w_end = (g + 1) * W / G;
@@ -867,9 +871,19 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
         };
+        // The host keeps every range within two tiles' worth of iterations
+        // (G >= W / (2 nk)), so a range is at most a first tile's tail (or
+        // the whole first tile), one whole tile, and a last tile's head:
+        // three straight-line segments (a loop over them keeps far more
+        // registers live).
         const int64_t w0 = g * W / G;
-        const int64_t t0_end = (w0 / nk_all + 1) * nk_all;
-        if (w_end > t0_end) segment(t0_end);  // start of the next tile (contributes)
+        if (w0 >= w_end) return;
+        const int64_t t_first = w0 / nk_all, t_last = (w_end - 1) / nk_all;
+        // the range ends inside a later tile: its head is the contribution
+        const bool head = t_last > t_first && w_end < (t_last + 1) * nk_all;
+        const bool mid = t_last - t_first - (head ? 1 : 0) >= 1;  // one whole tile after the first
+        if (head) segment(t_last * nk_all);
+        if (mid) segment((t_first + 1) * nk_all);
         segment(w0);
     }
 }

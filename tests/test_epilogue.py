@@ -174,3 +174,20 @@ def test_epilogue_identity_matches_plain_call_bitwise(g, handle):
         zero = torch.zeros(N, dtype=out)
         relu = run(g, handle, "N", "T", 1.0, 0.0, A, B, None, zero, ACTS["relu"], None, out, M, N)
         assert torch.equal(relu, torch.clamp_min(plain, 0.0))
+
+
+def test_epilogue_at_the_benchmarked_mlp_up_shape(g, handle):
+    """The fused bias + GELU row exactly as bench.py times it: the MLP-up
+    workload (8192 x 14336 x 4096, X N(0,1), W N(0,0.02)) with bf16 C/D, a
+    N(0, 0.02) bf16 bias; sampled outputs incl. first/last rows and columns."""
+    w = workloads.WORKLOADS["bf16_mlp_up"]
+    announce("epilogue mlp_up", w.M, w.N, w.K)
+    A, B, _ = workloads.make_inputs(w)
+    bias = workloads.draw_matrix((w.N,), "n002", w.seeds["sample"] + 1, "f32").to(torch.bfloat16)
+    D = run(g, handle, w.transA, w.transB, w.alpha, w.beta, A, B, None, bias, ACTS["gelu"], None,
+            torch.bfloat16, w.M, w.N)
+    rows, cols = workloads.sample_indices(w.M, w.N, w.seeds["sample"])
+    err, tol = check("bf16_bf16", w.transA, w.transB, w.M, w.N, w.K, w.alpha, w.beta, A, B, None,
+                     bias, ACTS["gelu"], None, D, rows=rows, cols=cols)
+    print(f"[result] mlp_up bias+gelu bf16 max_err={err:.3e}", flush=True)
+    assert err <= tol

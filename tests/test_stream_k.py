@@ -141,3 +141,34 @@ def test_automatic_policy_keeps_whole_tiles_where_they_are_faster(handle):
     err, tol = oracle_check(w.dtype, w.transA, w.transB, w.M, w.N, w.K, w.alpha, w.beta,
                             A, B, C, D, rows=rows, cols=cols)
     assert err <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stream_k_with_fewer_workgroups_than_tiles(handle, dtype):
+    """More tiles than resident workgroup slots: each workgroup's range spans
+    a tile's tail, whole tiles and the next tile's head (short K), or a tail
+    and a head (long K)."""
+    import dense_gemm_11_amd as g
+    assert g.gemm_set_stream_k(handle, 1) == g.GEMM_OK
+    try:
+        for n, (ta, tb, M, N, K) in enumerate([("N", "N", 3000, 2900, 72),
+                                               ("T", "N", 2900, 3000, 1000),
+                                               ("N", "T", 3001, 2999, 40)]):
+            alpha, beta = ((0.5, 1.5), (1.0, 0.0), (-1.0, 1.0))[n]
+            announce("stream-k many tiles", dtype, ta, tb, M, N, K)
+            A, B, C = make_case(dtype, ta, tb, M, N, K, seed=4300 + n, with_c=beta != 0)
+            D, _, _ = gpu_gemm(handle, dtype, ta, tb, M, N, K, alpha, beta, A, B, C)
+            sk = g.gemm_last_stream_k(handle)
+            vid = g.gemm_last_variant(handle)
+            bm, bn, _ = g.gemm_variant_tile(vid)
+            tiles = -(-M // bm) * -(-N // bn)
+            assert 1 < sk < tiles, (sk, tiles)
+            if K <= 100:
+                err, tol = oracle_check(dtype, ta, tb, M, N, K, alpha, beta, A, B, C, D)
+            else:
+                rows, cols = workloads.sample_indices(M, N, 4300 + n)
+                err, tol = oracle_check(dtype, ta, tb, M, N, K, alpha, beta, A, B, C, D,
+                                        rows=rows, cols=cols)
+            assert err <= tol, (dtype, M, N, K, sk, err)
+    finally:
+        g.gemm_set_stream_k(handle, -1)
