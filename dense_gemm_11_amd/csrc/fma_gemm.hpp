@@ -172,7 +172,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
                 for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) {
+        // The next stage's LDS stores come after this stage's FMAs, with no
+        // branch around them: a conditional store lets the compiler sink the
+        // FMAs below it, which puts the wait for the global loads (and every
+        // LDS read of the stage, all hoisted) in front of the arithmetic.
+        // After the last stage the stores write stale registers into the
+        // unused buffer, which is never read.
+        __builtin_amdgcn_sched_barrier(0);
+        {
             float* nxt = smem + (cur ^ 1) * Cfg::STAGE_FLOATS;
             la.store(nxt, SA, tid);
             lb.store(nxt + BK * SA, SB, tid);
