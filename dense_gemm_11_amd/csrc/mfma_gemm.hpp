@@ -368,7 +368,12 @@ __global__ __launch_bounds__(Cfg::THREADS) void mfma_gemm_kernel(GemmArgs p)
                 for (int j = 0; j < NF; ++j) mfma_step<Cfg::KIND>(af[i], bfr[j], acc[i][j]);
         }
 
-        if (more) {
+        // Unconditional, behind a scheduling barrier: a conditional store lets
+        // the compiler sink the MFMAs below it and wait for the global loads
+        // first.  After the last stage the stores write stale registers into
+        // the idle buffer, which is never read.
+        __builtin_amdgcn_sched_barrier(0);
+        {
             char* nxt = smem + (cur ^ 1) * Cfg::STAGE_BYTES;
             la.store(nxt, tid);
             lb.store(nxt + Cfg::A_BYTES, tid);
