@@ -134,3 +134,37 @@ def test_k_zero_and_alpha_zero_scale_c(g, handle, dtype):
     s = g.run_tensors(handle, A.cuda(), B.cuda(), D, alpha=0.0, beta=0.0)
     torch.cuda.synchronize()
     assert s == g.GEMM_OK and torch.equal(D.cpu(), torch.zeros(M, N))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_panels_beyond_32_bit_offsets_take_the_register_staged_kernels(g, handle, dtype):
+    """An operand panel whose byte span exceeds 2^32 (here: 256 rows of A with
+    a leading dimension of 9.5M fp32 or 20M bf16 elements) cannot be addressed by the
+    direct-to-LDS kernels' 32-bit offsets: the call runs the register-staged
+    MFMA kernels instead and still matches the oracle.  bf16 output and the
+    fused epilogue report GEMM_ERR_NOT_SUPPORTED for such panels."""
+    M, N, K = 256, 192, 96
+    lda = 9_500_000 if dtype == "f32" else 20_000_000   # 127 rows span > 4 GiB
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    A, B, C = make_case(dtype, "N", "N", M, N, K, seed=9, with_c=True)
+    announce("huge lda", dtype, lda)
+    buf = torch.zeros(M * lda, dtype=tdt, device="cuda")
+    Ad = buf.as_strided((M, K), (lda, 1))
+    Ad.copy_(A.to("cuda"))
+    Bd, _ = place(B)
+    Cd, _ = place(C)
+    D, _ = place(torch.full((M, N), float("nan")))
+    s = g.run_tensors(handle, Ad, Bd, D, C=Cd, alpha=1.0, beta=0.5, check=False)
+    torch.cuda.synchronize()
+    assert s == g.GEMM_OK, g.gemm_status_string(s)
+    assert "_dma" not in g.gemm_variant_name(g.gemm_last_variant(handle))
+    err, tol = oracle_check(dtype, "N", "N", M, N, K, 1.0, 0.5, A, B, C, D.cpu())
+    assert err <= tol
+    if dtype == "bf16":
+        Dh = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+        s = g.run_tensors(handle, Ad, Bd, Dh, check=False)
+        assert s == g.GEMM_ERR_NOT_SUPPORTED
+    s = g.run_tensors(handle, Ad, Bd, D, check=False, activation=g.GEMM_ACT_RELU)
+    assert s == g.GEMM_ERR_NOT_SUPPORTED
+    del buf
+    torch.cuda.empty_cache()
