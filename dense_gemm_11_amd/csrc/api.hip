@@ -221,9 +221,12 @@ int stream_k_grid(const Variant& v, int64_t M, int64_t N, int64_t K, int mode, s
         // workgroups meeting one tile, and partial sums written and read back
         const int64_t splits = gg >= tiles ? ceil_div(nk, W / gg) : 2;
         const double contrib = (double)(gg >= tiles ? gg - tiles : gg - 1);
+        // rounds of resident workgroups, each sharing its compute unit
+        const double rounds = (double)ceil_div(gg, slots);
         const double share = std::max(1.0, (double)std::min(gg, slots) / cus);
-        const double us = per * step_us(v) * share + 2.0 * contrib * tile_bytes / 3e12 * 1e6 +
-                          (double)(splits - 1) * mf * 1.5 + 5.0;
+        const double us = rounds * per * step_us(v) * share +
+                          2.0 * contrib * tile_bytes / 3e12 * 1e6 + (double)(splits - 1) * mf * 1.5 +
+                          5.0;
         if (best_g == 0 || us < best_us) {
             best_g = gg;
             best_us = us;
