@@ -237,6 +237,57 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int,
                          if out_dtype == torch.bfloat16 else w.description)}
 
 
+def amd_smi_sample():
+    """Socket power (W), mean graphics clock and memory clock (MHz) from
+    `amd-smi metric -p -c --json`, or None where the tool is not there."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if not exe:
+        return None
+    try:
+        out = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        data = json.loads(out.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    gpu = data["gpu_data"][0] if isinstance(data, dict) and "gpu_data" in data else data[0]
+
+    def val(x):
+        return x.get("value") if isinstance(x, dict) else None
+
+    clocks = gpu.get("clock", {})
+    gfx = [val(c.get("clk")) for k, c in clocks.items() if k.startswith("gfx_") and isinstance(c, dict)]
+    gfx = [g for g in gfx if isinstance(g, (int, float))]
+    mem = [val(c.get("clk")) for k, c in clocks.items() if k.startswith("mem") and isinstance(c, dict)]
+    mem = [m for m in mem if isinstance(m, (int, float))]
+    return {"socket_power_w": val(gpu.get("power", {}).get("socket_power")),
+            "gfx_clock_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
+            "mem_clock_mhz": mem[0] if mem else None}
+
+
+def telemetry_under_load(part, stream_handle, seconds: float = 1.5):
+    """Clocks and power while part's kernel runs back to back: one amd-smi
+    sample taken half way through ~`seconds` of launches, and one just
+    before (the bf16 matrix cores are power limited, so the clock under load
+    belongs with the timing)."""
+    import threading
+    result = {}
+    th = threading.Thread(target=lambda: (time.sleep(seconds / 2),
+                                          result.update(sample=amd_smi_sample())))
+    before = amd_smi_sample()
+    if before is None:
+        return None
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            part.launch(stream_handle)
+        torch.cuda.synchronize()
+    th.join()
+    return {"workload": part.name, "before": before, "under_load": result.get("sample")}
+
+
 def oracle_sample_rate(part: Part, cores: int, budget_s: float):
     """Time the CPU oracle on a sample of outputs of the part's workload."""
     import oracle
@@ -563,6 +614,9 @@ def main(argv=None):
     for p in parts:
         hot = p.hot_cache_ms(sh)
         report_parts[p.name]["hot_cache_kernel_ms"] = round(hot, 4)
+    telemetry = None
+    if not args.no_extras:
+        telemetry = [telemetry_under_load(p, sh) for p in parts]
     # which kernel each part used
     for p in parts:
         A, B, C, D = p.sets[0]
@@ -649,6 +703,7 @@ def main(argv=None):
                    "parallelism": "single GPU",
                    "buffer_sets": {p.name: len(p.sets) for p in parts}},
         "parts": report_parts, "extra_rows": extras, "roofline": roofline, "cpu_baseline": cpu,
+        "telemetry": telemetry,
     }
     print(json.dumps(out), flush=True)
     g.gemm_set_workspace(h, None, 0, None)
