@@ -509,15 +509,31 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
         wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, a_kc, b_kc, K, lda, ldb, es));
     const double dp_us = data_parallel_us(v, M, N, K);
     double sk_us = 0.0;
-    int sk = (aligned && v.kind == KIND_MFMA_DMA && !out_bf16 && !epi)
+    // stream-K launch functions of a variant for this call's output type and
+    // epilogue (null: the variant has none, so whole tiles)
+    auto sk_fns = [&](const Variant& x) -> const LaunchFn(*)[2] {
+        if (x.kind != KIND_MFMA_DMA || !x.sk_occ) return nullptr;
+        if (!out_bf16 && !epi) return x.sk_fn;
+        if (x.bm != 256 && x.bm != 128) return nullptr;
+        if (&x != &table()[dma_variant(op_dtype, x.bm == 256)]) return nullptr;
+        const SkFns* f = nullptr;
+        if (op_dtype == GEMM_DTYPE_F32) {
+            f = epi ? sk_fns_f32(x.bm) : nullptr;
+        } else {
+            const int kind = !epi ? 0 : out_bf16 ? 2 : 1;
+            f = x.bm == 256 ? sk_fns_bf16_256(kind) : sk_fns_bf16_128(kind);
+        }
+        return f ? f->fn : nullptr;
+    };
+    int sk = (aligned && sk_fns(v))
                  ? stream_k_grid(v, M, N, K, h->stream_k_mode, h->ws_bytes, dp_us, &sk_us)
                  : 0;
-    if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0 &&
-        !out_bf16 && !epi) {
+    if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0) {
         // With a workspace, stream-K on the other tile size competes too; the
         // lowest estimate wins.
         const int other = dma_variant(op_dtype, v.bm < 256);
-        if (other != id && dma_offsets_fit(table()[other], a_kc, b_kc, K, lda, ldb, es)) {
+        if (other != id && sk_fns(table()[other]) &&
+            dma_offsets_fit(table()[other], a_kc, b_kc, K, lda, ldb, es)) {
             double o_us = 0.0;
             const int sk_o = stream_k_grid(table()[other], M, N, K, h->stream_k_mode, h->ws_bytes,
                                            dp_us, &o_us);
@@ -555,7 +571,7 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     if (sk > 0) {
         a.sk_flags = static_cast<unsigned*>(h->ws);
         a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
-        e = vr.sk_fn[a_kc][b_kc](a, sk, stream);
+        e = sk_fns(vr)[a_kc][b_kc](a, sk, stream);
     } else if (nn_t) {
         GemmArgs t = a;
         t.A = B;

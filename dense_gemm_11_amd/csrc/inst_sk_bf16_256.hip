@@ -1,0 +1,19 @@
+// Stream-K instantiations of the selected bf16 direct-to-LDS variant with
+// 256x256 tiles for bf16 output and for the fused epilogue (fp32 or bf16
+// output); the partial sums handed between workgroups stay fp32.
+#include "mfma_dma_gemm.hpp"
+#include "variants.hpp"
+
+namespace dg {
+
+using SkCfg256 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
+
+const SkFns* sk_fns_bf16_256(int kind)
+{
+    static const SkFns t[3] = {DG_SK_OUT_TABLE(dma_gemm_kernel, SkCfg256, true, false),
+                               DG_SK_OUT_TABLE(dma_gemm_kernel, SkCfg256, false, true),
+                               DG_SK_OUT_TABLE(dma_gemm_kernel, SkCfg256, true, true)};
+    return kind >= 0 && kind < 3 ? &t[kind] : nullptr;
+}
+
+}  // namespace dg

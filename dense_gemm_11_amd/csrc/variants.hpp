@@ -43,6 +43,19 @@ const EpiFns* epi_fns_f32(int bm);
 const EpiFns* epi_fns_bf16(int bm);
 const EpiFns* epi_fns_bf16_out(int bm);
 
+// Stream-K instantiations with bf16 output or the fused epilogue (the
+// partial sums stay fp32): [A k-contiguous][B k-contiguous].
+struct SkFns {
+    LaunchFn fn[2][2];
+};
+// bf16 operands, 256x256 or 128x128 tiles: kind 0 = bf16 output, 1 = fused
+// epilogue with fp32 output, 2 = fused epilogue with bf16 output; null for
+// another kind.
+const SkFns* sk_fns_bf16_256(int kind);
+const SkFns* sk_fns_bf16_128(int kind);
+// fp32 operands, fused epilogue.
+const SkFns* sk_fns_f32(int bm);
+
 // Launch through hipLaunchKernel so the launch status is returned directly.
 template <auto KERNEL, int THREADS>
 hipError_t launch_kernel(const GemmArgs& a, int grid, hipStream_t s)
@@ -127,3 +140,10 @@ const Variant* f32dma_sweep_variant_table(int* count);
       {dg::launch_kernel<KERNEL<CFG, true, false, true, false, false, OUTBF, true>, CFG::THREADS>,  \
        dg::launch_kernel<KERNEL<CFG, true, true, true, false, false, OUTBF, true>, CFG::THREADS>}},  \
      dg::launch_kernel<KERNEL<CFG, false, true, true, false, true, OUTBF, true>, CFG::THREADS>}
+
+// Stream-K instantiations for output type OUTBF and fused epilogue EPI.
+#define DG_SK_OUT_TABLE(KERNEL, CFG, OUTBF, EPI)                                                    \
+    {{{dg::launch_kernel<KERNEL<CFG, false, false, true, true, false, OUTBF, EPI>, CFG::THREADS>,    \
+       dg::launch_kernel<KERNEL<CFG, false, true, true, true, false, OUTBF, EPI>, CFG::THREADS>},    \
+      {dg::launch_kernel<KERNEL<CFG, true, false, true, true, false, OUTBF, EPI>, CFG::THREADS>,     \
+       dg::launch_kernel<KERNEL<CFG, true, true, true, true, false, OUTBF, EPI>, CFG::THREADS>}}}

@@ -20,7 +20,8 @@
  *                          element-aligned operands whose panels the
  *                          direct-to-LDS kernels can address (every leading
  *                          dimension below 2^31 / 256 elements is), else
- *                          GEMM_ERR_NOT_SUPPORTED; never runs as stream-K.
+ *                          GEMM_ERR_NOT_SUPPORTED.  As stream-K, the partial
+ *                          sums handed between workgroups stay fp32.
  * The order in which the K products are summed is not specified; results are
  * bitwise reproducible run to run for the same call and kernel variant.
  *
@@ -130,7 +131,8 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB,
  * gemm_run.  Everything else -- layouts, degenerate cases (K == 0 or
  * alpha == 0 gives clamp(act(beta*C + bias))), errors -- is as for gemm_run.
  * The fused epilogue runs in the whole-tile direct-to-LDS kernels the
- * selector uses for element-aligned operands (never as stream-K); where
+ * selector uses for element-aligned operands (also as stream-K, the
+ * finishing workgroup applying it after the partial sums); where
  * gemm_run would take another kernel (operands not element-aligned, panel
  * offsets beyond 32 bits, a forced sweep variant) it returns
  * GEMM_ERR_NOT_SUPPORTED.                                                   */

@@ -149,3 +149,43 @@ def test_bf16_output_at_8192_cubed(handle):
     err = check("N", "N", w.M, w.N, w.K, 1.0, 0.0, A, B, None, D, rows=rows, cols=cols)
     print(f"[result] bf16-out 8192^3 max_err={err:.3e}", flush=True)
     assert err <= 1.0
+
+
+@pytest.fixture(scope="module")
+def sk_handle():
+    require_gpu()
+    import dense_gemm_11_amd as g
+    h = g.gemm_create()
+    ws = g.attach_workspace(h)
+    torch.cuda.synchronize()
+    yield h
+    g.gemm_set_workspace(h, None, 0, None)
+    g.gemm_destroy(h)
+    del ws
+
+
+def test_bf16_output_as_stream_k(sk_handle):
+    """bf16 output through the stream-K path: forced on ragged shapes (the
+    partial sums stay fp32, the finisher rounds once), and chosen by the
+    automatic policy on a few-tile long-K shape."""
+    import dense_gemm_11_amd as g
+    h = sk_handle
+    assert g.gemm_set_stream_k(h, 1) == g.GEMM_OK
+    try:
+        for n, (ta, tb, M, N, K) in enumerate([("N", "N", 300, 200, 1000), ("T", "N", 257, 513, 777),
+                                               ("N", "T", 64, 64, 1024), ("T", "T", 513, 129, 2051)]):
+            alpha, beta = ((1.0, 0.0), (0.5, 1.5), (-2.0, 1.0), (1.0, -0.25))[n]
+            announce("bf16-out stream-k", ta, tb, M, N, K)
+            A, B, C = case(ta, tb, M, N, K, 5300 + n, with_c=beta != 0)
+            D, _ = run_bf16_out(h, ta, tb, M, N, K, alpha, beta, A, B, C)
+            assert g.gemm_last_stream_k(h) > 1
+            assert check(ta, tb, M, N, K, alpha, beta, A, B, C, D) <= 1.0
+    finally:
+        g.gemm_set_stream_k(h, -1)
+    M, N, K = 1024, 1024, 32768
+    announce("bf16-out stream-k auto", M, N, K)
+    A, B, _ = case("N", "N", M, N, K, 5310, with_c=False)
+    D, _ = run_bf16_out(h, "N", "N", M, N, K, 1.0, 0.0, A, B, None)
+    assert g.gemm_last_stream_k(h) > 1
+    rows, cols = workloads.sample_indices(M, N, 5311)
+    assert check("N", "N", M, N, K, 1.0, 0.0, A, B, None, D, rows=rows, cols=cols) <= 1.0

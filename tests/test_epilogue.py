@@ -191,3 +191,46 @@ def test_epilogue_at_the_benchmarked_mlp_up_shape(g, handle):
                      bias, ACTS["gelu"], None, D, rows=rows, cols=cols)
     print(f"[result] mlp_up bias+gelu bf16 max_err={err:.3e}", flush=True)
     assert err <= tol
+
+
+@pytest.fixture(scope="module")
+def sk_handle(g):
+    h = g.gemm_create()
+    ws = g.attach_workspace(h)
+    torch.cuda.synchronize()
+    yield h
+    g.gemm_set_workspace(h, None, 0, None)
+    g.gemm_destroy(h)
+    del ws
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16_f32", "bf16_bf16"])
+def test_epilogue_as_stream_k(g, sk_handle, dtype):
+    """The fused epilogue through the stream-K path (the finisher applies it
+    after adding the partial sums): forced on ragged shapes, and chosen
+    automatically on a few-tile long-K shape."""
+    h = sk_handle
+    assert g.gemm_set_stream_k(h, 1) == g.GEMM_OK
+    try:
+        for n, (ta, tb, M, N, K) in enumerate([("N", "N", 300, 200, 1000), ("T", "N", 257, 513, 777),
+                                               ("N", "T", 513, 129, 2051)]):
+            with_bias, act, clamp = EPIS[(n + 1) % len(EPIS)]
+            alpha, beta = ((1.0, 0.0), (0.5, 1.5), (-1.0, 1.0))[n]
+            A, B, C, bias, out = make(dtype, ta, tb, M, N, K, 7500 + n, beta != 0.0)
+            bias = bias if with_bias else None
+            announce("epilogue stream-k", dtype, ta, tb, M, N, K, act, clamp)
+            D = run(g, h, ta, tb, alpha, beta, A, B, C, bias, ACTS[act], clamp, out, M, N)
+            assert g.gemm_last_stream_k(h) > 1
+            err, tol = check(dtype, ta, tb, M, N, K, alpha, beta, A, B, C, bias, ACTS[act], clamp, D)
+            assert err <= tol, (dtype, ta, tb, M, N, K, err)
+    finally:
+        g.gemm_set_stream_k(h, -1)
+    M, N, K = (1024, 1024, 32768) if dtype != "f32" else (1024, 1024, 16384)
+    announce("epilogue stream-k auto", dtype, M, N, K)
+    A, B, C, bias, out = make(dtype, "N", "N", M, N, K, 7510, False)
+    D = run(g, h, "N", "N", 1.0, 0.0, A, B, None, bias, ACTS["gelu"], None, out, M, N)
+    assert g.gemm_last_stream_k(h) > 1
+    rows, cols = workloads.sample_indices(M, N, 7511)
+    err, tol = check(dtype, "N", "N", M, N, K, 1.0, 0.0, A, B, None, bias, ACTS["gelu"], None, D,
+                     rows=rows, cols=cols)
+    assert err <= tol
