@@ -237,6 +237,40 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int,
                          if out_dtype == torch.bfloat16 else w.description)}
 
 
+def graph_replay_ms(g, h, name: str, launches: int = 50, replays: int = 5) -> float:
+    """Per-launch time with `launches` back-to-back calls captured in one HIP
+    graph (through torch.cuda.graph) and replayed: the kernels without the
+    host's per-call cost, which bounds a small GEMM called one at a time."""
+    w = workloads.WORKLOADS[name]
+    A, B, C = workloads.make_inputs(w)
+    A, B = A.cuda(), B.cuda()
+    C = None if C is None else C.cuda()
+    D = torch.empty(w.M, w.N, dtype=torch.float32, device="cuda")
+    run = lambda: g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
+                                alpha=w.alpha, beta=w.beta)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(launches):
+            run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return round(e0.elapsed_time(e1) / (replays * launches), 4)
+
+
 def amd_smi_sample():
     """Socket power (W), mean graphics clock and memory clock (MHz) from
     `amd-smi metric -p -c --json`, or None where the tool is not there."""
@@ -651,6 +685,7 @@ def main(argv=None):
                           "note": "vector FP32 FMA rate, 2 v_fmac_f32 per lane per clock"}
         extras["fp32_4096_vector_fma"] = vf
         extras["fp32_256"] = time_extra(g, h, "fp32_256", None, reps=50, warmup=10)
+        extras["fp32_256"]["graph_replay_kernel_ms"] = graph_replay_ms(g, h, "fp32_256")
         extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
                                                        warmup=5)
         extras["bf16_8192_bf16_output"] = time_extra(g, h, "bf16_8192", None, reps=10, warmup=3,
