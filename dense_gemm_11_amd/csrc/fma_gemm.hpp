@@ -9,11 +9,13 @@
 // and performs TM*TN fused multiply-adds (an outer product).
 //
 // LDS holds both tiles k-major ([k][m] and [k][n]) so that a thread's TM
-// consecutive A values and TN consecutive B values are each one or two
-// 16-byte reads; k-contiguous operands are transposed on the way in.  A
-// thread's outputs are split into 4x4 blocks spaced BM/2 and BN/2 apart, so
-// the 16 threads of a row read consecutive 16-byte LDS words.  Two LDS stages
-// with register staging overlap the next step's global loads with the FMAs.
+// A values and TN B values are 16-byte reads; k-contiguous operands are
+// transposed on the way in.  A thread's outputs are split into 4-row blocks
+// spaced BM/2 apart and 4-column blocks spaced BN/NB apart (TM = 8; TN = 8
+// or 16, NB = TN/4), so the 16 threads of a row read consecutive 16-byte LDS
+// words.  An 8x16 thread tile reads 24 values per 128 FMAs instead of 16 per
+// 64, a quarter less LDS traffic per FMA.  Two LDS stages with register
+// staging overlap the next step's global loads with the FMAs.
 //
 // Peak note: the FMAs compile to the two-operand v_fmac_f32 encoding, which
 // gfx950 issues at two per lane per clock (the device FP32 peak) without
@@ -31,11 +33,12 @@ struct FmaConfig {
     static constexpr int THREADS = 256;
     static constexpr int TY = 16, TX = 16;           // thread grid
     static constexpr int TM = BM / TY, TN = BN / TX;  // outputs per thread
+    static constexpr int NB = TN / 4;                 // 4-column blocks per thread along N
     static constexpr int PAD = 4;                     // floats of padding per LDS row
     static constexpr int SA = BM + PAD, SB = BN + PAD;
     static constexpr int STAGE_FLOATS = BK * SA + BK * SB;
     static constexpr int LDS_BYTES = 2 * STAGE_FLOATS * 4;
-    static_assert(TM == 8 && TN == 8, "two 4x4 blocks per direction");
+    static_assert(TM == 8 && (TN == 8 || TN == 16), "two 4-row blocks; two or four 4-column blocks");
     static_assert(BK % 4 == 0, "16-byte chunks along k");
 };
 
@@ -120,11 +123,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
     FmaLoader<Cfg, BM, A_KC, ALIGNED> la;
     FmaLoader<Cfg, BN, B_KC, ALIGNED> lb;
 
-    float acc[8][8];
+    constexpr int TN = Cfg::TN, NB = Cfg::NB;
+    float acc[8][TN];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
 
     const int nk = (p.K + BK - 1) / BK;
     const bool k_ragged = (p.K % BK) != 0;
@@ -154,22 +158,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
         // barrier keeps the compiler from hoisting every k's reads at once
         f32x4 a0 = *reinterpret_cast<const f32x4*>(As + ty * 4);
         f32x4 a1 = *reinterpret_cast<const f32x4*>(As + BM / 2 + ty * 4);
-        f32x4 b0 = *reinterpret_cast<const f32x4*>(Bs + tx * 4);
-        f32x4 b1 = *reinterpret_cast<const f32x4*>(Bs + BN / 2 + tx * 4);
+        f32x4 b[NB];
+#pragma unroll
+        for (int h = 0; h < NB; ++h) b[h] = *reinterpret_cast<const f32x4*>(Bs + h * (BN / NB) + tx * 4);
 #pragma unroll
         for (int k = 0; k < BK; ++k) {
             const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            float bv[TN];
+#pragma unroll
+            for (int h = 0; h < NB; ++h)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) bv[4 * h + s] = b[h][s];
             if (k + 1 < BK) {
                 a0 = *reinterpret_cast<const f32x4*>(As + (k + 1) * SA + ty * 4);
                 a1 = *reinterpret_cast<const f32x4*>(As + (k + 1) * SA + BM / 2 + ty * 4);
-                b0 = *reinterpret_cast<const f32x4*>(Bs + (k + 1) * SB + tx * 4);
-                b1 = *reinterpret_cast<const f32x4*>(Bs + (k + 1) * SB + BN / 2 + tx * 4);
+#pragma unroll
+                for (int h = 0; h < NB; ++h)
+                    b[h] = *reinterpret_cast<const f32x4*>(Bs + (k + 1) * SB + h * (BN / NB) + tx * 4);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+                for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // The next stage's LDS stores come after this stage's FMAs, with no
@@ -195,8 +205,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
         float* drow = p.D + (int64_t)row * p.ldd;
         const float* crow = p.C + (int64_t)row * p.ldc;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = n0 + h * (BN / 2) + tx * 4;
+        for (int h = 0; h < NB; ++h) {
+            const int col = n0 + h * (BN / NB) + tx * 4;
             float out[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) out[s] = alpha * acc[i][h * 4 + s];

@@ -5,6 +5,7 @@
 namespace dg {
 
 using FmaBig = FmaConfig<128, 128, 8>;
+using FmaWide = FmaConfig<128, 256, 8>;
 
 #define F32V_VARIANT(NAME, CFG) \
     {NAME, 0, KIND_VECTOR_FMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, 2, 1, DG_FN_TABLE(fma_gemm_kernel, CFG)}
@@ -13,6 +14,7 @@ const Variant* f32fma_variant_table(int* count)
 {
     static const Variant table[] = {
     F32V_VARIANT("f32_vfma_128x128x8_t8x8", FmaBig),
+    F32V_VARIANT("f32_vfma_128x256x8_t8x16", FmaWide),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -51,11 +51,12 @@ def test_workload_parity(handle, name):
     assert err <= tol
 
 
-def test_vector_fma_kernel_at_4096(handle):
-    """The fp32 vector-FMA kernel (reported beside the MFMA path) at the
-    4096^3 shape it is timed on, forced as the timing forces it."""
+@pytest.mark.parametrize("name", ["f32_vfma_128x256x8_t8x16", "f32_vfma_128x128x8_t8x8"])
+def test_vector_fma_kernel_at_4096(handle, name):
+    """The fp32 vector-FMA kernels (the first is reported beside the MFMA
+    path) at the 4096^3 shape they are timed on, forced as the timing forces
+    them."""
     import dense_gemm_11_amd as g
-    name = "f32_vfma_128x128x8_t8x8"
     vid = [i for i, n, _, _ in g.variants() if n == name][0]
     w = workloads.WORKLOADS["fp32_4096"]
     announce("vector-FMA", w.M, w.N, w.K)
