@@ -44,7 +44,7 @@ VALU_FP32_TFLOPS = 256 * 256 * 2.4e9 / 1e12
 HBM_GBS = 8000.0
 STEP_WORKLOADS = ("fp32_4096", "bf16_8192")
 # the vector-FMA (no matrix cores) fp32 kernel reported beside the step
-VECTOR_FMA_VARIANT = "f32_vfma_128x256x8_t8x16"
+VECTOR_FMA_VARIANT = "f32_vfma_128x256x16_t8x16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 

@@ -51,7 +51,8 @@ def test_workload_parity(handle, name):
     assert err <= tol
 
 
-@pytest.mark.parametrize("name", ["f32_vfma_128x256x8_t8x16", "f32_vfma_128x128x8_t8x8"])
+@pytest.mark.parametrize("name", ["f32_vfma_128x256x16_t8x16", "f32_vfma_128x256x8_t8x16",
+                                  "f32_vfma_128x128x8_t8x8"])
 def test_vector_fma_kernel_at_4096(handle, name):
     """The fp32 vector-FMA kernels (the first is reported beside the MFMA
     path) at the 4096^3 shape they are timed on, forced as the timing forces
