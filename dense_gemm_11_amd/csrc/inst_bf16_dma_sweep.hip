@@ -3,7 +3,9 @@
 // stages, late barrier with 4 stages, 2 stages of 64-deep steps.  128x128
 // tiles: late barrier with 2 or 4 stages of 32-deep steps, and 2 or 3 stages
 // of 64-deep steps, where the third stage (96 KiB of LDS) leaves room for one
-// workgroup per compute unit instead of two.
+// workgroup per compute unit instead of two.  Paired variants: the
+// k-contiguous operand copied two 32-deep steps at a time (whole 128-byte
+// lines), the other through 2 or 4 stages.
 #include "mfma_dma_gemm.hpp"
 #include "variants.hpp"
 
@@ -17,6 +19,10 @@ using Dma128s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true>;
 using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
 using Dma128k64s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 2, true>;
 using Dma128k64s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 3, true>;
+using Dma256s4P = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true, PAIR_KC>;
+using Dma256s2P = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 2, true, PAIR_KC>;
+using Dma128s4P = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true, PAIR_KC>;
+using Dma128s2P = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true, PAIR_KC>;
 
 #define BF16_DMA_VARIANT(NAME, CFG) \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, CFG::S, CFG::AHEAD, \
@@ -33,6 +39,10 @@ const Variant* bf16dma_sweep_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late", Dma128s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s2_late", Dma128k64s2L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s3_late", Dma128k64s3L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late_pair", Dma256s4P),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s2_late_pair", Dma256s2P),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair", Dma128s4P),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s2_late_pair", Dma128s2P),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

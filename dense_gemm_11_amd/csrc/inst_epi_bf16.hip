@@ -5,7 +5,7 @@
 
 namespace dg {
 
-using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
+using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
 using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
 
 const EpiFns* epi_fns_bf16(int bm)

@@ -6,7 +6,7 @@
 
 namespace dg {
 
-using SkCfg256 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true>;
+using SkCfg256 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
 
 const SkFns* sk_fns_bf16_256(int kind)
 {

@@ -56,10 +56,23 @@ namespace dg {
 // reads of the step have completed, copying the step S ahead into the stage
 // just read.  The late barrier hides one more step of copy latency with the
 // same number of stages, so two stages suffice.
-template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_, bool LATE_ = false>
+//
+// PAIR_ (late barrier only): PAIR_KC copies every k-contiguous operand two
+// K-steps at a time into one of two pair buffers holding 2*BK k per row, so
+// each group of lanes fetches whole 128-byte lines where a BK = 32 bf16 step
+// covers only half of each line (the other half would be requested again,
+// from L2, one step later); an mn-contiguous operand keeps the S-stage ring,
+// which then needs S = 2 or 4.  PAIR_BOTH_KC does so only when both operands
+// are k-contiguous (measured: pairing pays there, and not when one operand
+// is mn-contiguous).  A pair is copied at the barrier of the odd step that
+// finishes the buffer's previous pair, three steps ahead.
+enum : int { PAIR_NONE = 0, PAIR_KC = 1, PAIR_BOTH_KC = 2 };
+template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_, bool LATE_ = false,
+          int PAIR_ = PAIR_NONE>
 struct DmaConfig {
     static constexpr int KIND = KIND_, BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_;
     static constexpr bool LATE = LATE_;
+    static constexpr int PAIR = PAIR_;
     static constexpr int AHEAD = LATE ? S : S - 1;  // steps between a copy and its use
     using T = typename MfmaShape<KIND>::T;
     static constexpr int ES = sizeof(T);
@@ -74,7 +87,9 @@ struct DmaConfig {
     static constexpr int MF = WTM / FM, NF = WTN / FM;
     static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    // largest LDS footprint over the operand orientations (with PAIR: S
+    // stages of the mn-contiguous operands and two pair buffers of the others)
+    static constexpr int LDS_BYTES = (PAIR != PAIR_NONE && S < 4 ? 4 : S) * STAGE_BYTES;
     static constexpr int A_DMA = A_BYTES / (1024 * WAVES);  // DMA instructions per wave
     static constexpr int B_DMA = B_BYTES / (1024 * WAVES);
     static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
@@ -82,6 +97,8 @@ struct DmaConfig {
                       KIND == MFMA_F32_32x32x2,
                   "instruction kinds with a defined fragment mapping");
     static_assert(S >= (LATE ? 2 : 3) && S <= 5, "stage count");
+    static_assert(PAIR == PAIR_NONE || LATE, "paired copies need the late barrier");
+    static_assert(PAIR != PAIR_KC || S == 2 || S == 4, "a stage ring beside pair buffers: 2 or 4 stages");
     static_assert(NKS >= 2 && NKS % 2 == 0, "barrier sits between fragment steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "DMA split");
     static_assert(BM % (WM * FM) == 0 && BN % (WN * FM) == 0, "wave tile");
@@ -96,10 +113,11 @@ struct DmaConfig {
 // of a 32-lane half (chunks 2 apart) fill a 256-byte window exactly.
 __device__ __forceinline__ int mn_swz(int k) { return (0x0E0A0400 >> (8 * (k & 3))) & 0xFF; }
 
-// LDS layout of one operand tile.  R = rows of the tile in the mn direction.
-template <class Cfg, int R, bool KC>
+// LDS layout of one operand tile.  R = rows of the tile in the mn direction,
+// KD = k per row of a k-contiguous tile (BK, or 2*BK for a pair buffer).
+template <class Cfg, int R, bool KC, int KD = Cfg::BK>
 struct Layout {
-    static constexpr int BK = Cfg::BK;
+    static constexpr int BK = KD;
     static constexpr int CPR_K = BK / Cfg::VEC;   // chunks per [mn][k] row
     static constexpr int CPR_M = R / Cfg::VEC;    // chunks per [k][mn] row
     static_assert(!KC || CPR_K == 4 || CPR_K == 8, "k-major swizzle");
@@ -149,13 +167,19 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t nrec)
                  __builtin_amdgcn_readfirstlane((int)nrec), 0x00020000};
 }
 
-template <class Cfg, int R, bool KC, bool ALIGNED>
+// PAIRED: the operand lives in pair buffers (k-contiguous only): a DMA copy
+// covers two K-steps, register-staged copies one step into half `half`.
+template <class Cfg, int R, bool KC, bool ALIGNED, bool PAIRED = false>
 struct DmaOperand {
-    using L = Layout<Cfg, R, KC>;
+    static_assert(!PAIRED || KC, "only k-contiguous operands are paired");
+    static constexpr int KD = PAIRED ? 2 * Cfg::BK : Cfg::BK;  // k per buffer
+    using L = Layout<Cfg, R, KC, KD>;
     using T = typename Cfg::T;
     static constexpr int VEC = Cfg::VEC;
-    static constexpr int ND = (R * Cfg::BK * Cfg::ES) / (1024 * Cfg::WAVES);  // DMA instructions per wave
-    static constexpr int CHUNKS = L::ROWS * L::CPR;
+    static constexpr int ND = (R * KD * Cfg::ES) / (1024 * Cfg::WAVES);  // DMA instructions per wave
+    static constexpr int BYTES = R * KD * Cfg::ES;                     // one buffer
+    static constexpr int SCPR = KC ? Cfg::BK / VEC : R / VEC;          // chunks per row of one step
+    static constexpr int CHUNKS = (KC ? R : Cfg::BK) * SCPR;           // chunks of one step
     static constexpr int GL = (CHUNKS + Cfg::THREADS - 1) / Cfg::THREADS;  // guarded loads per thread
 
     // Per-lane byte offsets of this lane's DMA chunks from the start of a step
@@ -221,9 +245,10 @@ struct DmaOperand {
         for (int d = 0; d < ND; ++d) dma_one(d, rsrc, kbytes, lds, wave);
     }
 
-    // Register-staged copy with zero fill outside [0, rlim) x [0, K).
+    // Register-staged copy of the step at k0 with zero fill outside
+    // [0, rlim) x [0, K), into half `half` of a pair buffer when PAIRED.
     __device__ __forceinline__ void guarded(const T* panel, int64_t ld, int rlim, int k0, int K,
-                                            char* lds, int tid) const
+                                            char* lds, int tid, int half = 0) const
     {
         // in batches of GB chunks per thread, which bounds the registers this
         // path adds on top of the accumulators and fragments
@@ -235,7 +260,7 @@ struct DmaOperand {
             for (int b = 0; b < GB; ++b) {
                 const int q = tid + (i0 + b) * Cfg::THREADS;
                 if ((CHUNKS % Cfg::THREADS != 0 || GL % GB != 0) && (i0 + b >= GL || q >= CHUNKS)) break;
-                const int row = q / L::CPR, c = q % L::CPR;
+                const int row = q / SCPR, c = q % SCPR;
                 T e[VEC];
                 if constexpr (KC) {   // row = mn, elements along k
                     const int k = k0 + c * VEC;
@@ -262,7 +287,7 @@ struct DmaOperand {
             for (int b = 0; b < GB; ++b) {
                 const int q = tid + (i0 + b) * Cfg::THREADS;
                 if ((CHUNKS % Cfg::THREADS != 0 || GL % GB != 0) && (i0 + b >= GL || q >= CHUNKS)) break;
-                *reinterpret_cast<u32x4*>(lds + L::off(q / L::CPR, q % L::CPR)) = v[b];
+                *reinterpret_cast<u32x4*>(lds + L::off(q / SCPR, q % SCPR + half * SCPR)) = v[b];
             }
             // keep the next batch's loads behind this batch's stores
             asm volatile("" ::: "memory");
@@ -361,16 +386,38 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
     constexpr int MF = Cfg::MF, NF = Cfg::NF, NKS = Cfg::NKS;
     using Acc = typename AccType<Cfg::KIND>::type;
-    using OpA = DmaOperand<Cfg, BM, A_KC, ALIGNED>;
-    using OpB = DmaOperand<Cfg, BN, B_KC, ALIGNED>;
+    // With PAIR, the k-contiguous operands live in two pair buffers and only
+    // the others in the S stage arrays (A's part first in either).
+    constexpr bool PA = A_KC && (Cfg::PAIR == PAIR_KC || (Cfg::PAIR == PAIR_BOTH_KC && B_KC));
+    constexpr bool PB = B_KC && (Cfg::PAIR == PAIR_KC || (Cfg::PAIR == PAIR_BOTH_KC && A_KC));
+    constexpr bool PAIRED = PA || PB;
+    using OpA = DmaOperand<Cfg, BM, A_KC, ALIGNED, PA>;
+    using OpB = DmaOperand<Cfg, BN, B_KC, ALIGNED, PB>;
+    constexpr int A_ST = PA ? 0 : OpA::BYTES, ST_BYTES = A_ST + (PB ? 0 : OpB::BYTES);
+    constexpr int A_PR = PA ? OpA::BYTES : 0, PR_BYTES = A_PR + (PB ? OpB::BYTES : 0);
+    constexpr int ST_DECL = ST_BYTES > 0 ? ST_BYTES : 16, PR_DECL = PR_BYTES > 0 ? PR_BYTES : 16;
 
-    __shared__ __attribute__((aligned(1024))) char st0[Cfg::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char st1[Cfg::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char st2[Cfg::STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? Cfg::STAGE_BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) char st4[S > 4 ? Cfg::STAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char st0[ST_DECL];
+    __shared__ __attribute__((aligned(1024))) char st1[ST_DECL];
+    __shared__ __attribute__((aligned(1024))) char st2[ST_DECL];
+    __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? ST_DECL : 16];
+    __shared__ __attribute__((aligned(1024))) char st4[S > 4 ? ST_DECL : 16];
+    __shared__ __attribute__((aligned(1024))) char pr0[PR_DECL];
+    __shared__ __attribute__((aligned(1024))) char pr1[PR_DECL];
     auto stage = [&](int s) __attribute__((always_inline)) -> char* {
         return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : s == 3 ? st3 : st4;
+    };
+    auto pr = [&](int i) __attribute__((always_inline)) -> char* { return i == 0 ? pr0 : pr1; };
+    // Slots: the step in slot `cur` (its index mod P in a round of P steps)
+    // has its staged operands in stage cur mod S and its paired ones in half
+    // cur mod 2 of pair buffer cur/2 mod 2, i.e. at fragment steps shifted by
+    // NKS in the second half.
+    constexpr int P = PAIRED ? 4 : S;
+    auto a_lds = [&](int cur) __attribute__((always_inline)) -> char* {
+        return PA ? pr((cur >> 1) & 1) : stage(cur % S);
+    };
+    auto b_lds = [&](int cur) __attribute__((always_inline)) -> char* {
+        return PB ? pr((cur >> 1) & 1) + A_PR : stage(cur % S) + A_ST;
     };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -395,6 +442,37 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     Acc acc[MF][NF];
     u32x4 fa[2][MF], fb[2][NF];
 
+    // Copies in flight, per wave.  The barrier of step j issues the staged
+    // operands' copy of step j + AHEAD (NST instructions), and with PAIR, on
+    // odd j, the paired operands' copy of steps j+3 and j+4 (NPR).  Before
+    // the barrier of step t the data of step t+1 must have landed: the count
+    // of copy instructions issued after it, up to the barrier of step
+    // `last`, may still be in flight (copies complete in issue order).
+    constexpr int NST = (PA ? 0 : OpA::ND) + (PB ? 0 : OpB::ND);
+    constexpr int NPR = (PA ? OpA::ND : 0) + (PB ? OpB::ND : 0);
+    constexpr int AHEAD = Cfg::AHEAD;
+    static_assert(NST == 0 || NPR == 0 || 4 % S == 0, "a stage ring beside pair buffers: 2 or 4 stages");
+    constexpr auto pair_in_flight = [](int t, int last) constexpr {
+        // positions (step, 0 = staged / 1 = paired) of step t+1's copies
+        const int js = t + 1 - AHEAD, jp = 2 * ((t + 1) >> 1) - 3;
+        int need = NPR > 0 ? 2 * jp + 1 : -1000;
+        if (NST > 0 && 2 * js > need) need = 2 * js;
+        int n = 0;
+        for (int pos = need + 1; pos <= 2 * last + 1; ++pos) {
+            const int j = pos >> 1;   // floor for negative positions too
+            if ((pos & 1) == 0) n += NST;
+            else if ((j & 1) != 0) n += NPR;
+        }
+        return n;
+    };
+    constexpr int WAIT_E = PAIRED ? pair_in_flight(8, 7) : Cfg::DMA_PER_STAGE * (AHEAD - 2);
+    constexpr int WAIT_O = PAIRED ? pair_in_flight(9, 8) : Cfg::DMA_PER_STAGE * (AHEAD - 2);
+    constexpr int WAIT_PRO = PAIRED ? pair_in_flight(-1, -1) : Cfg::DMA_PER_STAGE * (AHEAD - 1);
+    static_assert(WAIT_E < 64 && WAIT_O < 64 && WAIT_PRO < 64, "vmcnt range");
+    // The counts hold once every copy issued up to the barrier of step t-1
+    // exists: steps up to t + LOOK.
+    constexpr int LOOK = PAIRED ? (AHEAD - 1 > 2 ? AHEAD - 1 : 2) : AHEAD - 1;
+
     // The K-steps [k_lo, k_hi) of output tile (tm, tn), accumulated into acc
     // from zero.  Every wave enters with the LDS stages free.
     auto tile_work = [&](int tm, int tn, int k_lo, int k_hi) __attribute__((always_inline)) {
@@ -415,14 +493,31 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     // exact zeros past K and is always register-staged.
     const int nk_dma = ALIGNED ? ((last && (k_ragged || edge)) ? nk - 1 : nk) : 0;
 
+    // step kt of the staged operands into a stage array
     auto load = [&](int kt, char* base) __attribute__((always_inline)) {
         const int k0 = (k_lo + kt) * BK;
         if (kt < nk_dma) {
-            oa.dma(rsrc_a, OpA::step_bytes(k0, p.lda), base, wave);
-            ob.dma(rsrc_b, OpB::step_bytes(k0, p.ldb), base + Cfg::A_BYTES, wave);
+            if constexpr (!PA) oa.dma(rsrc_a, OpA::step_bytes(k0, p.lda), base, wave);
+            if constexpr (!PB) ob.dma(rsrc_b, OpB::step_bytes(k0, p.ldb), base + A_ST, wave);
         } else {
-            oa.guarded(panel_a, p.lda, rlim_a, k0, p.K, base, tid);
-            ob.guarded(panel_b, p.ldb, rlim_b, k0, p.K, base + Cfg::A_BYTES, tid);
+            if constexpr (!PA) oa.guarded(panel_a, p.lda, rlim_a, k0, p.K, base, tid);
+            if constexpr (!PB) ob.guarded(panel_b, p.ldb, rlim_b, k0, p.K, base + A_ST, tid);
+        }
+    };
+    // steps 2q and 2q+1 of the paired operands into a pair buffer (one DMA
+    // copy when both are DMA steps, else each existing step register-staged)
+    auto load_pair = [&](int q, char* base) __attribute__((always_inline)) {
+        const int k0 = (k_lo + 2 * q) * BK;
+        if (2 * q + 1 < nk_dma) {
+            if constexpr (PA) oa.dma(rsrc_a, OpA::step_bytes(k0, p.lda), base, wave);
+            if constexpr (PB) ob.dma(rsrc_b, OpB::step_bytes(k0, p.ldb), base + A_PR, wave);
+        } else {
+#pragma unroll 1
+            for (int h = 0; h < 2 && 2 * q + h < nk; ++h) {
+                if constexpr (PA) oa.guarded(panel_a, p.lda, rlim_a, k0 + h * BK, p.K, base, tid, h);
+                if constexpr (PB)
+                    ob.guarded(panel_b, p.ldb, rlim_b, k0 + h * BK, p.K, base + A_PR, tid, h);
+            }
         }
     };
 
@@ -431,58 +526,68 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
 #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = Acc{};
 
-    // prologue: steps 0 .. AHEAD-1 in flight, wait for step 0
-    constexpr int AHEAD = Cfg::AHEAD;
+    // prologue: the copies the barriers of steps -VP .. -1 would have issued
+    // (steps 0 .. AHEAD-1, and with PAIR pairs 0 and 1), then wait for step 0
+    if constexpr (!PAIRED) {
 #pragma unroll
-    for (int s = 0; s < AHEAD; ++s)
-        if (s < nk) load(s, stage(s));
-    if (nk >= AHEAD) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 1)>();
-    else wait_vm_lgkm0<0>();
+        for (int s = 0; s < AHEAD; ++s)
+            if (s < nk) load(s, stage(s));
+        if (nk >= AHEAD) wait_vm_lgkm0<WAIT_PRO>();
+        else wait_vm_lgkm0<0>();
+    } else {
+        constexpr int VP = AHEAD > 3 ? AHEAD : 3;
+        static_for<VP>([&](auto i_c) __attribute__((always_inline)) {
+            constexpr int j = decltype(i_c)::value - VP;
+            if constexpr (j + AHEAD >= 0)
+                if (j + AHEAD < nk) load(j + AHEAD, stage((j + AHEAD) % S));
+            if constexpr ((j & 1) != 0 && j + 3 >= 0) {
+                constexpr int q = (j + 3) / 2;
+                if (2 * q < nk) load_pair(q, pr(q & 1));
+            }
+        });
+        if (nk > LOOK) wait_vm_lgkm0<WAIT_PRO>();
+        else wait_vm_lgkm0<0>();
+    }
     barrier_only();
 
-    auto read_frags = [&](const char* base, int ks, int buf) __attribute__((always_inline)) {
+    auto read_frags = [&](int cur, int ks, int buf) __attribute__((always_inline)) {
+        const int ka = ks + (PA ? (cur & 1) * NKS : 0), kb = ks + (PB ? (cur & 1) * NKS : 0);
 #pragma unroll
-        for (int i = 0; i < MF; ++i) fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
+        for (int i = 0; i < MF; ++i) fa[buf][i] = OpA::frag(a_lds(cur), wave_m0 + i * FM, ka, lane);
 #pragma unroll
-        for (int j = 0; j < NF; ++j)
-            fb[buf][j] = OpB::frag(base + Cfg::A_BYTES, wave_n0 + j * FM, ks, lane);
+        for (int j = 0; j < NF; ++j) fb[buf][j] = OpB::frag(b_lds(cur), wave_n0 + j * FM, kb, lane);
     };
-    read_frags(stage(0), 0, 0);
+    read_frags(0, 0, 0);
 
     // Fragment step of a K-step at which the barrier sits, and the stage the
     // copy issued after it fills (relative to the current stage).
     constexpr int BAR_KS = Cfg::LATE ? NKS - 1 : NKS / 2;
     constexpr int FILL = Cfg::LATE ? 0 : S - 1;
 
-    // One K-step held in LDS stage CUR (static, so every LDS address is a
-    // compile-time offset from its own __shared__ array).  STEADY: the step
-    // AHEAD ahead exists and is copied by DMA, so no run-time conditions.
-    auto step = [&](auto cur_c, auto steady_c, int kt) __attribute__((always_inline)) {
+    // One K-step held in slot CUR (static, so every LDS address is a
+    // compile-time offset from its own __shared__ array), with run-time
+    // checks: copies only for steps that exist, guarded copies allowed.
+    auto step = [&](auto cur_c, int kt) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
-        constexpr bool STEADY = decltype(steady_c)::value;
-        constexpr int NXT = (CUR + 1) % S;
+        constexpr int NXT = (CUR + 1) % P;
         constexpr int FAR = (CUR + FILL) % S;
-        const char* base = stage(CUR);
+        constexpr int WAIT = (CUR & 1) ? WAIT_O : WAIT_E;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             if (ks == BAR_KS) {
                 // the next step must have landed in every wave's part of LDS
                 // (and, with the late barrier, this wave's reads of the stage
                 // about to be refilled must be complete: lgkmcnt(0))
-                if (STEADY || kt + AHEAD <= nk) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
+                if (kt + LOOK < nk) wait_vm_lgkm0<WAIT>();
                 else wait_vm_lgkm0<0>();
                 barrier_only();
-                if (STEADY) {
-                    const int kf = (k_lo + kt + AHEAD) * BK;
-                    oa.dma(rsrc_a, OpA::step_bytes(kf, p.lda), stage(FAR), wave);
-                    ob.dma(rsrc_b, OpB::step_bytes(kf, p.ldb), stage(FAR) + Cfg::A_BYTES, wave);
-                } else if (kt + AHEAD < nk) {
-                    load(kt + AHEAD, stage(FAR));
-                }
+                if (kt + AHEAD < nk) load(kt + AHEAD, stage(FAR));
+                if constexpr (PAIRED && (CUR & 1) != 0)
+                    if (kt + 3 < nk) load_pair((kt + 3) / 2, pr(CUR >> 1));
             }
             const int cb = ks & 1;
-            if (ks + 1 < NKS) read_frags(base, ks + 1, cb ^ 1);
-            else if (STEADY || kt + 1 < nk) read_frags(stage(NXT), 0, cb ^ 1);
+            if (ks + 1 < NKS) read_frags(CUR, ks + 1, cb ^ 1);
+            else if (kt + 1 < nk) read_frags(NXT, 0, cb ^ 1);
 #pragma unroll
             for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -499,28 +604,30 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     constexpr int RA = OpA::NREAD_PER_FRAG, RB = OpB::NREAD_PER_FRAG;
     constexpr int NREAD = MF * RA + NF * RB;
     constexpr int NMFMA = MF * NF;
-    constexpr int NDMA = OpA::ND + OpB::ND;
-    auto read_op = [&](int n, const char* base, int ks, int buf) __attribute__((always_inline)) {
+    auto read_op = [&](int n, int cur, int ks, int buf) __attribute__((always_inline)) {
         if (n < MF * RA) {
             const int i = n / RA;
+            const char* ab = a_lds(cur);
+            const int kk = ks + (PA ? (cur & 1) * NKS : 0);
             if constexpr (RA == 1) {
-                fa[buf][i] = OpA::frag(base, wave_m0 + i * FM, ks, lane);
+                fa[buf][i] = OpA::frag(ab, wave_m0 + i * FM, kk, lane);
             } else if constexpr (RA == 4) {
-                fa[buf][i][n % RA] = OpA::frag_f32_piece(base, wave_m0 + i * FM, ks, lane, n % RA);
+                fa[buf][i][n % RA] = OpA::frag_f32_piece(ab, wave_m0 + i * FM, kk, lane, n % RA);
             } else {
-                const uint64_t v = OpA::frag_tr_half(base, wave_m0 + i * FM, ks, lane, n % RA);
+                const uint64_t v = OpA::frag_tr_half(ab, wave_m0 + i * FM, kk, lane, n % RA);
                 fa[buf][i][2 * (n % RA)] = (uint32_t)v;
                 fa[buf][i][2 * (n % RA) + 1] = (uint32_t)(v >> 32);
             }
         } else {
             const int m = n - MF * RA, j = m / RB;
-            const char* bb = base + Cfg::A_BYTES;
+            const char* bb = b_lds(cur);
+            const int kk = ks + (PB ? (cur & 1) * NKS : 0);
             if constexpr (RB == 1) {
-                fb[buf][j] = OpB::frag(bb, wave_n0 + j * FM, ks, lane);
+                fb[buf][j] = OpB::frag(bb, wave_n0 + j * FM, kk, lane);
             } else if constexpr (RB == 4) {
-                fb[buf][j][m % RB] = OpB::frag_f32_piece(bb, wave_n0 + j * FM, ks, lane, m % RB);
+                fb[buf][j][m % RB] = OpB::frag_f32_piece(bb, wave_n0 + j * FM, kk, lane, m % RB);
             } else {
-                const uint64_t v = OpB::frag_tr_half(bb, wave_n0 + j * FM, ks, lane, m % RB);
+                const uint64_t v = OpB::frag_tr_half(bb, wave_n0 + j * FM, kk, lane, m % RB);
                 fb[buf][j][2 * (m % RB)] = (uint32_t)v;
                 fb[buf][j][2 * (m % RB) + 1] = (uint32_t)(v >> 32);
             }
@@ -528,21 +635,28 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     };
     auto steady = [&](auto cur_c, int kt) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
-        constexpr int NXT = (CUR + 1) % S;
+        constexpr int NXT = (CUR + 1) % P;
         constexpr int FAR = (CUR + FILL) % S;
-        const char* base = stage(CUR);
-        const int kfar = (k_lo + kt + AHEAD) * BK;
-        const uint32_t ka = OpA::step_bytes(kfar, p.lda), kb = OpB::step_bytes(kfar, p.ldb);
+        constexpr int WAIT = (CUR & 1) ? WAIT_O : WAIT_E;
+        // copies issued at this step's barrier: the staged operands' step
+        // AHEAD ahead, then (PAIR, odd slots) the paired operands' pair
+        // starting three steps ahead
+        constexpr int NA_ST = PA ? 0 : OpA::ND, NB_ST = PB ? 0 : OpB::ND;
+        constexpr int NA_PR = PA ? OpA::ND : 0;
+        constexpr int NDMA = NST + ((PAIRED && (CUR & 1) != 0) ? NPR : 0);
+        const int kst = (k_lo + kt + AHEAD) * BK, kpr = (k_lo + kt + 3) * BK;
+        const uint32_t ka = OpA::step_bytes(PA ? kpr : kst, p.lda);
+        const uint32_t kb = OpB::step_bytes(PB ? kpr : kst, p.ldb);
         static_for<NKS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
             constexpr int cb = ks & 1;
             constexpr bool mid = ks == BAR_KS;
             if constexpr (mid) {
-                if constexpr (Cfg::LATE) wait_vm_lgkm0<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
-                else wait_vm<Cfg::DMA_PER_STAGE * (AHEAD - 2)>();
+                if constexpr (Cfg::LATE) wait_vm_lgkm0<WAIT>();
+                else wait_vm<WAIT>();
                 barrier_only();
             }
-            const char* rbase = ks + 1 < NKS ? base : stage(NXT);
+            constexpr int rcur = ks + 1 < NKS ? CUR : NXT;
             constexpr int rks = ks + 1 < NKS ? ks + 1 : 0;
             constexpr int nops = NREAD + (mid ? NDMA : 0);
             static_for<NMFMA>([&](auto e_c) __attribute__((always_inline)) {
@@ -562,19 +676,22 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
                                                  : NREAD + (e + 1 - HALF) * (nops - NREAD) / (NMFMA - HALF);
                 static_for<hi - lo>([&](auto oo_c) __attribute__((always_inline)) {
                     constexpr int o = lo + decltype(oo_c)::value;
-                    if constexpr (o < NREAD) read_op(o, rbase, rks, cb ^ 1);
-                    else if constexpr (o - NREAD < OpA::ND)
-                        oa.dma_one(o - NREAD, rsrc_a, ka, stage(FAR), wave);
+                    constexpr int d = o - NREAD;
+                    if constexpr (o < NREAD) read_op(o, rcur, rks, cb ^ 1);
+                    else if constexpr (d < NA_ST)
+                        oa.dma_one(d, rsrc_a, ka, stage(FAR), wave);
+                    else if constexpr (d < NA_ST + NB_ST)
+                        ob.dma_one(d - NA_ST, rsrc_b, kb, stage(FAR) + A_ST, wave);
+                    else if constexpr (d < NA_ST + NB_ST + NA_PR)
+                        oa.dma_one(d - NA_ST - NB_ST, rsrc_a, ka, pr(CUR >> 1), wave);
                     else
-                        ob.dma_one(o - NREAD - OpA::ND, rsrc_b, kb, stage(FAR) + Cfg::A_BYTES, wave);
+                        ob.dma_one(d - NA_ST - NB_ST - NA_PR, rsrc_b, kb, pr(CUR >> 1) + A_PR, wave);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
     };
 
-    using T_ = std::true_type;
-    using F_ = std::false_type;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -582,24 +699,26 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     using I4 = std::integral_constant<int, 4>;
 
     int kt = 0;
-    // steady state: every step of the group issues a DMA copy AHEAD steps ahead
-    for (; kt + S - 1 + AHEAD < nk_dma; kt += S) {
+    // steady state: every step of the round issues its copies as DMA (the
+    // last step of a round copies up to step kt + P - 1 + LAST_AHEAD)
+    constexpr int LAST_AHEAD = PAIRED && AHEAD < 4 ? 4 : AHEAD;
+    for (; kt + P - 1 + LAST_AHEAD < nk_dma; kt += P) {
         steady(I0{}, kt);
         steady(I1{}, kt + 1);
-        if constexpr (S > 2) steady(I2{}, kt + 2);
-        if constexpr (S > 3) steady(I3{}, kt + 3);
-        if constexpr (S > 4) steady(I4{}, kt + 4);
+        if constexpr (P > 2) steady(I2{}, kt + 2);
+        if constexpr (P > 3) steady(I3{}, kt + 3);
+        if constexpr (P > 4) steady(I4{}, kt + 4);
     }
     // tail: remaining steps with run-time checks (guarded copies allowed)
-    for (; kt < nk; kt += S) {
-        step(I0{}, F_{}, kt);
-        if (kt + 1 < nk) step(I1{}, F_{}, kt + 1);
-        if constexpr (S > 2)
-            if (kt + 2 < nk) step(I2{}, F_{}, kt + 2);
-        if constexpr (S > 3)
-            if (kt + 3 < nk) step(I3{}, F_{}, kt + 3);
-        if constexpr (S > 4)
-            if (kt + 4 < nk) step(I4{}, F_{}, kt + 4);
+    for (; kt < nk; kt += P) {
+        step(I0{}, kt);
+        if (kt + 1 < nk) step(I1{}, kt + 1);
+        if constexpr (P > 2)
+            if (kt + 2 < nk) step(I2{}, kt + 2);
+        if constexpr (P > 3)
+            if (kt + 3 < nk) step(I3{}, kt + 3);
+        if constexpr (P > 4)
+            if (kt + 4 < nk) step(I4{}, kt + 4);
     }
     };  // tile_work
 
@@ -661,15 +780,17 @@ __global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
     constexpr int RPI = 64 / CH;       // staged rows per read instruction
     constexpr int NT = FM / RPI;       // read instructions per batch
     constexpr int REGION = FM * DC * 4;
-    constexpr int WPS = Cfg::STAGE_BYTES / REGION;  // wave blocks per stage array
+    // the blocks use the first NSA stage arrays, or the pair buffers when
+    // those are larger (naming only those keeps the others out of the kernel
+    // when S does not need them)
+    constexpr bool USE_PR = PR_BYTES > ST_BYTES;
+    constexpr int WPS = (USE_PR ? PR_BYTES : ST_BYTES) / REGION;  // wave blocks per array
     static_assert(CH >= 16 && CH <= 64 && 64 % CH == 0, "staging shape");
-    // the blocks use the first NSA stage arrays (naming only those keeps the
-    // others out of the kernel when S does not need them)
     constexpr int NSA = WPS >= 1 ? (Cfg::WAVES + WPS - 1) / WPS : 99;
-    static_assert(NSA <= S && NSA <= 3, "staging space");
+    static_assert(NSA <= (USE_PR ? 2 : S) && NSA <= 3, "staging space");
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    char* base = st0;
-    if constexpr (NSA > 1) base = wv / WPS == 1 ? st1 : base;
+    char* base = USE_PR ? pr0 : st0;
+    if constexpr (NSA > 1) base = wv / WPS == 1 ? (USE_PR ? pr1 : st1) : base;
     if constexpr (NSA > 2) base = wv / WPS == 2 ? st2 : base;
     char* const region = base + (wv % WPS) * REGION;
     auto slot = [&](int r, int chunk) __attribute__((always_inline)) -> f32x4* {
