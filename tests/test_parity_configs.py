@@ -74,3 +74,22 @@ def test_vector_fma_kernel_at_4096(handle, name):
                             A, B, C, D, rows=rows, cols=cols)
     print(f"[result] vector-FMA 4096^3 max_rel_err={err:.3e} tol={tol:g}", flush=True)
     assert err <= tol
+
+
+@pytest.mark.parametrize("ta,tb", [("N", "T"), ("T", "N"), ("T", "T")])
+def test_bf16_8192_other_layouts(handle, ta, tb):
+    """The 8192^3 bf16 workload with its operands stored in the other three
+    orientations (the benchmarked NN one is above): each takes a different
+    mainloop path at full size -- both operands k-contiguous copies them two
+    K-steps at a time, TN has no k-contiguous operand, TT is what NN runs as
+    after its transposition."""
+    import dataclasses
+    w = dataclasses.replace(workloads.WORKLOADS["bf16_8192"], transA=ta, transB=tb)
+    announce("bf16 8192^3 layout", ta, tb)
+    A, B, C = workloads.make_inputs(w)
+    D, _, _ = gpu_gemm(handle, w.dtype, ta, tb, w.M, w.N, w.K, w.alpha, w.beta, A, B, C)
+    rows, cols = workloads.sample_indices(w.M, w.N, w.seeds["sample"])
+    err, tol = oracle_check(w.dtype, ta, tb, w.M, w.N, w.K, w.alpha, w.beta, A, B, C, D,
+                            rows=rows, cols=cols)
+    print(f"[result] bf16 8192^3 {ta}{tb} max_rel_err={err:.3e} tol={tol:g}", flush=True)
+    assert err <= tol
