@@ -103,16 +103,18 @@ int device_cus()
 // whose operands are element-aligned and whose panel offsets fit in 32 bits;
 // the register-staged kernels take the rest.  The direct-to-LDS variants
 // chosen place their barrier before the last fragment step of a K-step:
-// three 32-deep stages for bf16 (measured 8-10 % faster than the half-way
-// barrier with four stages on 8192^3 with k-contiguous A) and two 32-deep
-// stages for fp32 (1 % faster than three 16-deep ones on 4096^3).
+// three 32-deep stages for bf16 256x256 tiles (measured 8-10 % faster than
+// the half-way barrier with four stages on 8192^3 with k-contiguous A), four
+// for bf16 128x128 tiles (2-5 % faster than three on six shapes from 2048^3
+// to 8192x4096x1792, same occupancy of 2), and two 32-deep stages for fp32
+// (1 % faster than three 16-deep ones on 4096^3).
 // The direct-to-LDS variant with 256x256 (big) or 128x128 tiles for a dtype.
 int dma_variant(int dtype, bool big)
 {
     static const int ids[2][2] = {
         {find_variant("f32_dma32x32x2_128x128x16_w2x2_s3_late"),
          find_variant("f32_dma32x32x2_256x256x32_w2x2_s2_late")},
-        {find_variant("bf16_dma32x32x16_128x128x32_w2x2_s3_late"),
+        {find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late"),
          find_variant("bf16_dma32x32x16_256x256x32_w2x2_s3_late")}};
     return ids[dtype == GEMM_DTYPE_BF16_F32][big];
 }

@@ -7,7 +7,7 @@
 namespace dg {
 
 using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
-using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
 
 #define bf16_out_table(BM)                                                                   \
     {{{bf16_out_fns(BM).fn[0][0][0], bf16_out_fns(BM).fn[0][0][1]},                         \
@@ -26,7 +26,7 @@ const Variant* bf16dma_variant_table(int* count)
 {
     static const Variant table[] = {
         BF16_DMA_SK_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3_late", Dma256s3L),
-        BF16_DMA_SK_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late", Dma128s3L),
+        BF16_DMA_SK_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late", Dma128s4L),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

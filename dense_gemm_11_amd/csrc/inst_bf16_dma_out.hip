@@ -6,12 +6,12 @@
 namespace dg {
 
 using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
-using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
 
 const Bf16OutFns& bf16_out_fns(int bm)
 {
     static const Bf16OutFns big = {DG_BO_TABLE(dma_gemm_kernel, Dma256s3L)};
-    static const Bf16OutFns mid = {DG_BO_TABLE(dma_gemm_kernel, Dma128s3L)};
+    static const Bf16OutFns mid = {DG_BO_TABLE(dma_gemm_kernel, Dma128s4L)};
     return bm == 256 ? big : mid;
 }
 

@@ -1,7 +1,7 @@
 // bf16 direct-to-LDS variants kept for measurement: the pipeline-depth and
 // barrier-placement sweep.  256x256 tiles: half-way barrier with 3 or 4
 // stages, late barrier with 4 stages, 2 stages of 64-deep steps.  128x128
-// tiles: late barrier with 2 or 4 stages of 32-deep steps, and 2 or 3 stages
+// tiles: late barrier with 2, 3 or 5 stages of 32-deep steps, and 2 or 3 stages
 // of 64-deep steps, where the third stage (96 KiB of LDS) leaves room for one
 // workgroup per compute unit instead of two.  Paired variants: the
 // k-contiguous operand copied two 32-deep steps at a time (whole 128-byte
@@ -16,7 +16,8 @@ using Dma256s3 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3>;
 using Dma256s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true>;
 using Dma256k64s2L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 2, 2, true>;
 using Dma128s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true>;
-using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
+using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+using Dma128s5L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 5, true>;
 using Dma128k64s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 2, true>;
 using Dma128k64s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 3, true>;
 using Dma256s4P = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true, PAIR_KC>;
@@ -36,7 +37,8 @@ const Variant* bf16dma_sweep_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late", Dma256s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x2_s2_late", Dma256k64s2L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s2_late", Dma128s2L),
-        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late", Dma128s4L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late", Dma128s3L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s5_late", Dma128s5L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s2_late", Dma128k64s2L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s3_late", Dma128k64s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late_pair", Dma256s4P),

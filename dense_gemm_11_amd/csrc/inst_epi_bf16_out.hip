@@ -6,12 +6,12 @@
 namespace dg {
 
 using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
-using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
 
 const EpiFns* epi_fns_bf16_out(int bm)
 {
     static const EpiFns big = DG_EPI_TABLE(dma_gemm_kernel, Dma256s3L, true);
-    static const EpiFns mid = DG_EPI_TABLE(dma_gemm_kernel, Dma128s3L, true);
+    static const EpiFns mid = DG_EPI_TABLE(dma_gemm_kernel, Dma128s4L, true);
     return bm == 256 ? &big : bm == 128 ? &mid : nullptr;
 }
 

@@ -6,7 +6,7 @@
 
 namespace dg {
 
-using SkCfg128 = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
+using SkCfg128 = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
 
 const SkFns* sk_fns_bf16_128(int kind)
 {
