@@ -545,6 +545,18 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
             }
         }
     }
+    // bf16 128x128 whole tiles: the 2-stage ring fits 3 workgroups on a
+    // compute unit where the 4-stage one fits 2.  The shallower ring wins
+    // when that removes a round of tiles (4093x2051x1537: 544 tiles in one
+    // round instead of a full round and a nearly empty one; measured 0.0593
+    // vs 0.0624 ms), which the round and pipeline-depth model above decides.
+    // That variant has no transposed-output, bf16-output or fused-epilogue
+    // instantiations, so only plain fp32-output calls take it.
+    if (sk == 0 && h->forced_variant < 0 && aligned && !epi && !out_bf16 &&
+        id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
+        static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
+        if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < dp_us) id = s2;
+    }
     const Variant& vr = table()[id];
     a.tiles_m = (int)ceil_div(M, vr.bm);
     a.tiles_n = (int)ceil_div(N, vr.bn);
