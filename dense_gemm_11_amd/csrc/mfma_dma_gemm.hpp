@@ -67,12 +67,17 @@ namespace dg {
 // is mn-contiguous).  A pair is copied at the barrier of the odd step that
 // finishes the buffer's previous pair, three steps ahead.
 enum : int { PAIR_NONE = 0, PAIR_KC = 1, PAIR_BOTH_KC = 2 };
+//
+// WPE_ > 0 asks the compiler for at least that many waves per SIMD, i.e.
+// that many resident workgroups per compute unit for 4-wave workgroups
+// (a register budget of 512 / WPE_ per lane).
 template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_, bool LATE_ = false,
-          int PAIR_ = PAIR_NONE>
+          int PAIR_ = PAIR_NONE, int WPE_ = 0>
 struct DmaConfig {
     static constexpr int KIND = KIND_, BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_;
     static constexpr bool LATE = LATE_;
     static constexpr int PAIR = PAIR_;
+    static constexpr int WPE = WPE_ > 0 ? WPE_ : 1;
     static constexpr int AHEAD = LATE ? S : S - 1;  // steps between a copy and its use
     using T = typename MfmaShape<KIND>::T;
     static constexpr int ES = sizeof(T);
@@ -381,7 +386,8 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // no second kernel reads D back.
 template <class Cfg, bool A_KC, bool B_KC, bool ALIGNED, bool SK = false, bool OUT_T = false,
           bool OUT_BF16 = false, bool EPI = false>
-__global__ __launch_bounds__(Cfg::THREADS) void dma_gemm_kernel(GemmArgs p)
+__global__ __launch_bounds__(Cfg::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg::WPE)))
+void dma_gemm_kernel(GemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
     constexpr int MF = Cfg::MF, NF = Cfg::NF, NKS = Cfg::NKS;
