@@ -1,0 +1,63 @@
+"""The automatic kernel choice for representative shapes (with a stream-K
+workspace attached, as the benchmark runs): tile size, the stage count of
+128x128 bf16 tiles, stream-K or whole tiles.  These pin the measured policy;
+the results themselves are checked against the oracle by the parity tests."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from .gpu_support import announce, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+P = "bf16_dma32x32x16_"
+CASES = [
+    # dtype, transA, transB, M, N, K, beta, bf16 output, expected variant, stream-K?
+    ("f32", "N", "N", 4096, 4096, 4096, 0.0, False, "f32_dma32x32x2_256x256x32_w2x2_s2_late", False),
+    ("bf16", "N", "N", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x2_s3_late", False),
+    ("bf16", "N", "T", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x2_s3_late", False),
+    # 544 tiles of 128x128: one round at 3 workgroups per CU (2-stage ring)
+    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, False, P + "128x128x32_w2x2_s2_late", False),
+    ("bf16", "N", "N", 3000, 3000, 512, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
+    # ... but not with bf16 output, which only the 4-stage variant carries
+    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, True, P + "128x128x32_w2x2_s4_late", False),
+    # at most one round at 2 per CU: the 4-stage ring
+    ("bf16", "N", "N", 2048, 2048, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    # few tiles, long K: stream-K
+    ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
+]
+
+
+@pytest.fixture(scope="module")
+def g_handle():
+    require_gpu()
+    import dense_gemm_11_amd as g
+    h = g.gemm_create()
+    ws = g.attach_workspace(h)
+    torch.cuda.synchronize()
+    yield g, h
+    g.gemm_set_workspace(h, None, 0, None)
+    g.gemm_destroy(h)
+    del ws
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}_{c[1]}{c[2]}_{c[3]}x{c[4]}x{c[5]}"
+                         + ("_bf16out" if c[7] else ""))
+def test_automatic_choice(g_handle, case):
+    g, h = g_handle
+    dtype, ta, tb, M, N, K, beta, bf16_out, expected, stream_k = case
+    announce("selection", case)
+    el = torch.float32 if dtype == "f32" else torch.bfloat16
+    out = torch.bfloat16 if bf16_out else torch.float32
+    A = torch.zeros((M, K) if ta == "N" else (K, M), dtype=el, device="cuda")
+    B = torch.zeros((K, N) if tb == "N" else (N, K), dtype=el, device="cuda")
+    C = torch.zeros((M, N), dtype=out, device="cuda") if beta else None
+    D = torch.empty((M, N), dtype=out, device="cuda")
+    s = g.run_tensors(h, A, B, D, C=C, transA=ta, transB=tb, alpha=1.0, beta=beta, check=False)
+    torch.cuda.synchronize()
+    assert s == g.GEMM_OK, g.gemm_status_string(s)
+    assert g.gemm_variant_name(g.gemm_last_variant(h)) == expected
+    assert (g.gemm_last_stream_k(h) > 0) == stream_k
+    assert torch.count_nonzero(D).item() == 0
