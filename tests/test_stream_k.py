@@ -174,6 +174,36 @@ def test_stream_k_with_fewer_workgroups_than_tiles(handle, dtype):
         g.gemm_set_stream_k(handle, -1)
 
 
+@pytest.mark.parametrize("ta,tb", list(itertools.product("NT", "NT")))
+def test_stream_k_on_large_tiles_every_layout(handle, ta, tb):
+    """Forced stream-K on 256x256 bf16 tiles (196 of them) in every operand
+    layout: with both operands k-contiguous the kernel copies them two
+    K-steps at a time, and the split ranges start at odd as well as even
+    K-steps; K = 232 leaves a ragged last step, K = 1000 an odd step count."""
+    import dense_gemm_11_amd as g
+    big = [i for i, name, _, _ in g.variants()
+           if name == "bf16_dma32x32x16_256x256x32_w2x2_s3_late"][0]
+    assert g.gemm_set_stream_k(handle, 1) == g.GEMM_OK
+    assert g.gemm_set_variant(handle, big) == g.GEMM_OK
+    try:
+        for n, K in enumerate([232, 1000]):
+            M = N = 3584
+            alpha, beta = ((1.0, 0.0), (0.5, -1.0))[n]
+            announce("stream-k 256 tiles", ta, tb, M, N, K)
+            A, B, C = make_case("bf16", ta, tb, M, N, K, seed=4400 + n, with_c=beta != 0)
+            D, _, _ = gpu_gemm(handle, "bf16", ta, tb, M, N, K, alpha, beta, A, B, C)
+            bm, bn, _ = g.gemm_variant_tile(g.gemm_last_variant(handle))
+            assert (bm, bn) == (256, 256)
+            assert g.gemm_last_stream_k(handle) > 1
+            rows, cols = workloads.sample_indices(M, N, 4400 + n)
+            err, tol = oracle_check("bf16", ta, tb, M, N, K, alpha, beta, A, B, C, D,
+                                    rows=rows, cols=cols)
+            assert err <= tol, (ta, tb, K, err)
+    finally:
+        g.gemm_set_stream_k(handle, -1)
+        g.gemm_set_variant(handle, -1)
+
+
 @pytest.mark.parametrize("name", ["bf16_outproj", "bf16_mlp_down", "bf16_qkv", "bf16_8192"])
 def test_automatic_policy_keeps_full_waves_whole(handle, name):
     """Shapes with at least a full wave of large tiles stay data-parallel
