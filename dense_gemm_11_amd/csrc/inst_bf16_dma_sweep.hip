@@ -5,8 +5,10 @@
 // of 64-deep steps, where the third stage (96 KiB of LDS) leaves room for one
 // workgroup per compute unit instead of two.  Paired variants: the
 // k-contiguous operand copied two 32-deep steps at a time (whole 128-byte
-// lines), the other through 2 or 4 stages.  `_o3`: registers capped so that
-// three workgroups fit on a compute unit.
+// lines), the other through 2 or 4 stages.  `_pair3`: only a k-contiguous
+// operand beside an mn-contiguous one is paired, in three pair buffers (each
+// pair copied five steps ahead).  `_o3`: registers capped so that three
+// workgroups fit on a compute unit.
 #include "mfma_dma_gemm.hpp"
 #include "variants.hpp"
 
@@ -20,6 +22,8 @@ using Dma128s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true>;
 using Dma128s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true>;
 using Dma128s5L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 5, true>;
 using Dma128s3LO3 = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 3, true, PAIR_NONE, 3>;
+using Dma256s3P3 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_ONE_KC, 0, 3>;
+using Dma256s2P3 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 2, true, PAIR_ONE_KC, 0, 3>;
 using Dma128k64s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 2, true>;
 using Dma128k64s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 3, true>;
 using Dma256s4P = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true, PAIR_KC>;
@@ -42,6 +46,8 @@ const Variant* bf16dma_sweep_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late", Dma128s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s5_late", Dma128s5L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late_o3", Dma128s3LO3),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3_late_pair3", Dma256s3P3),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s2_late_pair3", Dma256s2P3),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s2_late", Dma128k64s2L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s3_late", Dma128k64s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late_pair", Dma256s4P),

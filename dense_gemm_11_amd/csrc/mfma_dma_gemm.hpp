@@ -61,23 +61,27 @@ namespace dg {
 // K-steps at a time into one of two pair buffers holding 2*BK k per row, so
 // each group of lanes fetches whole 128-byte lines where a BK = 32 bf16 step
 // covers only half of each line (the other half would be requested again,
-// from L2, one step later); an mn-contiguous operand keeps the S-stage ring,
-// which then needs S = 2 or 4.  PAIR_BOTH_KC does so only when both operands
+// from L2, one step later); an mn-contiguous operand keeps the S-stage ring
+// (a round of slots, the least common multiple of S and 2*NP, is at most 6
+// steps).  PAIR_BOTH_KC does so only when both operands
 // are k-contiguous (measured: pairing pays there, and not when one operand
-// is mn-contiguous).  A pair is copied at the barrier of the odd step that
-// finishes the buffer's previous pair, three steps ahead.
-enum : int { PAIR_NONE = 0, PAIR_KC = 1, PAIR_BOTH_KC = 2 };
+// is mn-contiguous), PAIR_ONE_KC only when the other one is mn-contiguous.
+// A pair is copied at the barrier of the odd step that finishes the
+// buffer's previous pair.
+enum : int { PAIR_NONE = 0, PAIR_KC = 1, PAIR_BOTH_KC = 2, PAIR_ONE_KC = 3 };
 //
 // WPE_ > 0 asks the compiler for at least that many waves per SIMD, i.e.
 // that many resident workgroups per compute unit for 4-wave workgroups
-// (a register budget of 512 / WPE_ per lane).
+// (a register budget of 512 / WPE_ per lane).  NP_ = 2 or 3 pair buffers:
+// with NP, a pair is copied 2*NP - 1 steps ahead of its first step.
 template <int KIND_, int BM_, int BN_, int BK_, int WM_, int WN_, int S_, bool LATE_ = false,
-          int PAIR_ = PAIR_NONE, int WPE_ = 0>
+          int PAIR_ = PAIR_NONE, int WPE_ = 0, int NP_ = 2>
 struct DmaConfig {
     static constexpr int KIND = KIND_, BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, S = S_;
     static constexpr bool LATE = LATE_;
     static constexpr int PAIR = PAIR_;
     static constexpr int WPE = WPE_ > 0 ? WPE_ : 1;
+    static constexpr int NP = NP_;
     static constexpr int AHEAD = LATE ? S : S - 1;  // steps between a copy and its use
     using T = typename MfmaShape<KIND>::T;
     static constexpr int ES = sizeof(T);
@@ -92,9 +96,23 @@ struct DmaConfig {
     static constexpr int MF = WTM / FM, NF = WTN / FM;
     static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    // largest LDS footprint over the operand orientations (with PAIR: S
-    // stages of the mn-contiguous operands and two pair buffers of the others)
-    static constexpr int LDS_BYTES = (PAIR != PAIR_NONE && S < 4 ? 4 : S) * STAGE_BYTES;
+    // whether an operand that is (kc) k-contiguous is paired when the other
+    // one is (other_kc)
+    static constexpr bool pairs(bool kc, bool other_kc)
+    {
+        return kc && (PAIR == PAIR_KC || (PAIR == PAIR_BOTH_KC && other_kc) ||
+                      (PAIR == PAIR_ONE_KC && !other_kc));
+    }
+    static constexpr int lds_for(bool a_kc, bool b_kc)
+    {
+        const bool pa = pairs(a_kc, b_kc), pb = pairs(b_kc, a_kc);
+        return S * ((pa ? 0 : A_BYTES) + (pb ? 0 : B_BYTES)) +
+               NP * 2 * ((pa ? A_BYTES : 0) + (pb ? B_BYTES : 0));
+    }
+    static constexpr int max2(int x, int y) { return x > y ? x : y; }
+    // largest LDS footprint over the four operand orientations
+    static constexpr int LDS_BYTES = max2(max2(lds_for(false, false), lds_for(false, true)),
+                                          max2(lds_for(true, false), lds_for(true, true)));
     static constexpr int A_DMA = A_BYTES / (1024 * WAVES);  // DMA instructions per wave
     static constexpr int B_DMA = B_BYTES / (1024 * WAVES);
     static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
@@ -103,7 +121,7 @@ struct DmaConfig {
                   "instruction kinds with a defined fragment mapping");
     static_assert(S >= (LATE ? 2 : 3) && S <= 5, "stage count");
     static_assert(PAIR == PAIR_NONE || LATE, "paired copies need the late barrier");
-    static_assert(PAIR != PAIR_KC || S == 2 || S == 4, "a stage ring beside pair buffers: 2 or 4 stages");
+    static_assert(NP == 2 || NP == 3, "pair buffers");
     static_assert(NKS >= 2 && NKS % 2 == 0, "barrier sits between fragment steps");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "DMA split");
     static_assert(BM % (WM * FM) == 0 && BN % (WN * FM) == 0, "wave tile");
@@ -394,9 +412,9 @@ void dma_gemm_kernel(GemmArgs p)
     using Acc = typename AccType<Cfg::KIND>::type;
     // With PAIR, the k-contiguous operands live in two pair buffers and only
     // the others in the S stage arrays (A's part first in either).
-    constexpr bool PA = A_KC && (Cfg::PAIR == PAIR_KC || (Cfg::PAIR == PAIR_BOTH_KC && B_KC));
-    constexpr bool PB = B_KC && (Cfg::PAIR == PAIR_KC || (Cfg::PAIR == PAIR_BOTH_KC && A_KC));
+    constexpr bool PA = Cfg::pairs(A_KC, B_KC), PB = Cfg::pairs(B_KC, A_KC);
     constexpr bool PAIRED = PA || PB;
+    constexpr int NP = Cfg::NP;
     using OpA = DmaOperand<Cfg, BM, A_KC, ALIGNED, PA>;
     using OpB = DmaOperand<Cfg, BN, B_KC, ALIGNED, PB>;
     constexpr int A_ST = PA ? 0 : OpA::BYTES, ST_BYTES = A_ST + (PB ? 0 : OpB::BYTES);
@@ -410,20 +428,36 @@ void dma_gemm_kernel(GemmArgs p)
     __shared__ __attribute__((aligned(1024))) char st4[S > 4 ? ST_DECL : 16];
     __shared__ __attribute__((aligned(1024))) char pr0[PR_DECL];
     __shared__ __attribute__((aligned(1024))) char pr1[PR_DECL];
+    __shared__ __attribute__((aligned(1024))) char pr2[NP > 2 ? PR_DECL : 16];
     auto stage = [&](int s) __attribute__((always_inline)) -> char* {
         return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : s == 3 ? st3 : st4;
     };
-    auto pr = [&](int i) __attribute__((always_inline)) -> char* { return i == 0 ? pr0 : pr1; };
+    auto pr = [&](int i) __attribute__((always_inline)) -> char* {
+        return i == 0 ? pr0 : i == 1 ? pr1 : pr2;
+    };
     // Slots: the step in slot `cur` (its index mod P in a round of P steps)
     // has its staged operands in stage cur mod S and its paired ones in half
-    // cur mod 2 of pair buffer cur/2 mod 2, i.e. at fragment steps shifted by
-    // NKS in the second half.
-    constexpr int P = PAIRED ? 4 : S;
+    // cur mod 2 of pair buffer cur/2 mod NP, i.e. at fragment steps shifted
+    // by NKS in the second half.
+    constexpr auto lcm = [](int x, int y) constexpr {
+        int a = x, b = y;
+        while (b != 0) {
+            const int r = a % b;
+            a = b;
+            b = r;
+        }
+        return x / a * y;
+    };
+    // no staged operand with both paired: the stage ring plays no part
+    constexpr int P = !PAIRED ? S : (PA && PB) ? 2 * NP : lcm(S, 2 * NP);
+    static_assert(P % S == 0 || (PA && PB), "a round covers whole stage rings");
+    static_assert(!PAIRED || P % (2 * NP) == 0, "a round covers whole pair-buffer cycles");
+    static_assert(P <= 6, "slots of a round");
     auto a_lds = [&](int cur) __attribute__((always_inline)) -> char* {
-        return PA ? pr((cur >> 1) & 1) : stage(cur % S);
+        return PA ? pr((cur >> 1) % NP) : stage(cur % S);
     };
     auto b_lds = [&](int cur) __attribute__((always_inline)) -> char* {
-        return PB ? pr((cur >> 1) & 1) + A_PR : stage(cur % S) + A_ST;
+        return PB ? pr((cur >> 1) % NP) + A_PR : stage(cur % S) + A_ST;
     };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -450,17 +484,17 @@ void dma_gemm_kernel(GemmArgs p)
 
     // Copies in flight, per wave.  The barrier of step j issues the staged
     // operands' copy of step j + AHEAD (NST instructions), and with PAIR, on
-    // odd j, the paired operands' copy of steps j+3 and j+4 (NPR).  Before
+    // odd j, the paired operands' copy of steps j + 2NP - 1 and j + 2NP
+    // (NPR) into the pair buffer that step j finished.  Before
     // the barrier of step t the data of step t+1 must have landed: the count
     // of copy instructions issued after it, up to the barrier of step
     // `last`, may still be in flight (copies complete in issue order).
     constexpr int NST = (PA ? 0 : OpA::ND) + (PB ? 0 : OpB::ND);
     constexpr int NPR = (PA ? OpA::ND : 0) + (PB ? OpB::ND : 0);
     constexpr int AHEAD = Cfg::AHEAD;
-    static_assert(NST == 0 || NPR == 0 || 4 % S == 0, "a stage ring beside pair buffers: 2 or 4 stages");
     constexpr auto pair_in_flight = [](int t, int last) constexpr {
         // positions (step, 0 = staged / 1 = paired) of step t+1's copies
-        const int js = t + 1 - AHEAD, jp = 2 * ((t + 1) >> 1) - 3;
+        const int js = t + 1 - AHEAD, jp = 2 * ((t + 1) >> 1) - 2 * NP + 1;
         int need = NPR > 0 ? 2 * jp + 1 : -1000;
         if (NST > 0 && 2 * js > need) need = 2 * js;
         int n = 0;
@@ -471,13 +505,13 @@ void dma_gemm_kernel(GemmArgs p)
         }
         return n;
     };
-    constexpr int WAIT_E = PAIRED ? pair_in_flight(8, 7) : Cfg::DMA_PER_STAGE * (AHEAD - 2);
-    constexpr int WAIT_O = PAIRED ? pair_in_flight(9, 8) : Cfg::DMA_PER_STAGE * (AHEAD - 2);
+    constexpr int WAIT_E = PAIRED ? pair_in_flight(12, 11) : Cfg::DMA_PER_STAGE * (AHEAD - 2);
+    constexpr int WAIT_O = PAIRED ? pair_in_flight(13, 12) : Cfg::DMA_PER_STAGE * (AHEAD - 2);
     constexpr int WAIT_PRO = PAIRED ? pair_in_flight(-1, -1) : Cfg::DMA_PER_STAGE * (AHEAD - 1);
     static_assert(WAIT_E < 64 && WAIT_O < 64 && WAIT_PRO < 64, "vmcnt range");
     // The counts hold once every copy issued up to the barrier of step t-1
     // exists: steps up to t + LOOK.
-    constexpr int LOOK = PAIRED ? (AHEAD - 1 > 2 ? AHEAD - 1 : 2) : AHEAD - 1;
+    constexpr int LOOK = PAIRED ? (AHEAD - 1 > 2 * NP - 2 ? AHEAD - 1 : 2 * NP - 2) : AHEAD - 1;
 
     // The K-steps [k_lo, k_hi) of output tile (tm, tn), accumulated into acc
     // from zero.  Every wave enters with the LDS stages free.
@@ -541,14 +575,14 @@ void dma_gemm_kernel(GemmArgs p)
         if (nk >= AHEAD) wait_vm_lgkm0<WAIT_PRO>();
         else wait_vm_lgkm0<0>();
     } else {
-        constexpr int VP = AHEAD > 3 ? AHEAD : 3;
+        constexpr int VP = AHEAD > 2 * NP - 1 ? AHEAD : 2 * NP - 1;
         static_for<VP>([&](auto i_c) __attribute__((always_inline)) {
             constexpr int j = decltype(i_c)::value - VP;
             if constexpr (j + AHEAD >= 0)
                 if (j + AHEAD < nk) load(j + AHEAD, stage((j + AHEAD) % S));
-            if constexpr ((j & 1) != 0 && j + 3 >= 0) {
-                constexpr int q = (j + 3) / 2;
-                if (2 * q < nk) load_pair(q, pr(q & 1));
+            if constexpr ((j & 1) != 0 && j + 2 * NP - 1 >= 0) {
+                constexpr int q = (j + 2 * NP - 1) / 2;
+                if (2 * q < nk) load_pair(q, pr(q % NP));
             }
         });
         if (nk > LOOK) wait_vm_lgkm0<WAIT_PRO>();
@@ -589,7 +623,7 @@ void dma_gemm_kernel(GemmArgs p)
                 barrier_only();
                 if (kt + AHEAD < nk) load(kt + AHEAD, stage(FAR));
                 if constexpr (PAIRED && (CUR & 1) != 0)
-                    if (kt + 3 < nk) load_pair((kt + 3) / 2, pr(CUR >> 1));
+                    if (kt + 2 * NP - 1 < nk) load_pair((kt + 2 * NP - 1) / 2, pr((CUR >> 1) % NP));
             }
             const int cb = ks & 1;
             if (ks + 1 < NKS) read_frags(CUR, ks + 1, cb ^ 1);
@@ -646,11 +680,11 @@ void dma_gemm_kernel(GemmArgs p)
         constexpr int WAIT = (CUR & 1) ? WAIT_O : WAIT_E;
         // copies issued at this step's barrier: the staged operands' step
         // AHEAD ahead, then (PAIR, odd slots) the paired operands' pair
-        // starting three steps ahead
+        // starting 2NP - 1 steps ahead
         constexpr int NA_ST = PA ? 0 : OpA::ND, NB_ST = PB ? 0 : OpB::ND;
         constexpr int NA_PR = PA ? OpA::ND : 0;
         constexpr int NDMA = NST + ((PAIRED && (CUR & 1) != 0) ? NPR : 0);
-        const int kst = (k_lo + kt + AHEAD) * BK, kpr = (k_lo + kt + 3) * BK;
+        const int kst = (k_lo + kt + AHEAD) * BK, kpr = (k_lo + kt + 2 * NP - 1) * BK;
         const uint32_t ka = OpA::step_bytes(PA ? kpr : kst, p.lda);
         const uint32_t kb = OpB::step_bytes(PB ? kpr : kst, p.ldb);
         static_for<NKS>([&](auto ks_c) __attribute__((always_inline)) {
@@ -689,9 +723,10 @@ void dma_gemm_kernel(GemmArgs p)
                     else if constexpr (d < NA_ST + NB_ST)
                         ob.dma_one(d - NA_ST, rsrc_b, kb, stage(FAR) + A_ST, wave);
                     else if constexpr (d < NA_ST + NB_ST + NA_PR)
-                        oa.dma_one(d - NA_ST - NB_ST, rsrc_a, ka, pr(CUR >> 1), wave);
+                        oa.dma_one(d - NA_ST - NB_ST, rsrc_a, ka, pr((CUR >> 1) % NP), wave);
                     else
-                        ob.dma_one(d - NA_ST - NB_ST - NA_PR, rsrc_b, kb, pr(CUR >> 1) + A_PR, wave);
+                        ob.dma_one(d - NA_ST - NB_ST - NA_PR, rsrc_b, kb, pr((CUR >> 1) % NP) + A_PR,
+                                   wave);
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -703,17 +738,19 @@ void dma_gemm_kernel(GemmArgs p)
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
 
     int kt = 0;
     // steady state: every step of the round issues its copies as DMA (the
     // last step of a round copies up to step kt + P - 1 + LAST_AHEAD)
-    constexpr int LAST_AHEAD = PAIRED && AHEAD < 4 ? 4 : AHEAD;
+    constexpr int LAST_AHEAD = PAIRED && AHEAD < 2 * NP ? 2 * NP : AHEAD;
     for (; kt + P - 1 + LAST_AHEAD < nk_dma; kt += P) {
         steady(I0{}, kt);
         steady(I1{}, kt + 1);
         if constexpr (P > 2) steady(I2{}, kt + 2);
         if constexpr (P > 3) steady(I3{}, kt + 3);
         if constexpr (P > 4) steady(I4{}, kt + 4);
+        if constexpr (P > 5) steady(I5{}, kt + 5);
     }
     // tail: remaining steps with run-time checks (guarded copies allowed)
     for (; kt < nk; kt += P) {
@@ -725,6 +762,8 @@ void dma_gemm_kernel(GemmArgs p)
             if (kt + 3 < nk) step(I3{}, kt + 3);
         if constexpr (P > 4)
             if (kt + 4 < nk) step(I4{}, kt + 4);
+        if constexpr (P > 5)
+            if (kt + 5 < nk) step(I5{}, kt + 5);
     }
     };  // tile_work
 
