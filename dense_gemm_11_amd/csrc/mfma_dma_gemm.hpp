@@ -58,7 +58,7 @@ namespace dg {
 // same number of stages, so two stages suffice.
 //
 // PAIR_ (late barrier only): PAIR_KC copies every k-contiguous operand two
-// K-steps at a time into one of two pair buffers holding 2*BK k per row, so
+// K-steps at a time into one of NP pair buffers holding 2*BK k per row, so
 // each group of lanes fetches whole 128-byte lines where a BK = 32 bf16 step
 // covers only half of each line (the other half would be requested again,
 // from L2, one step later); an mn-contiguous operand keeps the S-stage ring
@@ -410,8 +410,8 @@ void dma_gemm_kernel(GemmArgs p)
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, S = Cfg::S;
     constexpr int MF = Cfg::MF, NF = Cfg::NF, NKS = Cfg::NKS;
     using Acc = typename AccType<Cfg::KIND>::type;
-    // With PAIR, the k-contiguous operands live in two pair buffers and only
-    // the others in the S stage arrays (A's part first in either).
+    // Paired operands (see PAIR_) live in NP pair buffers and the others in
+    // the S stage arrays (A's part first in either).
     constexpr bool PA = Cfg::pairs(A_KC, B_KC), PB = Cfg::pairs(B_KC, A_KC);
     constexpr bool PAIRED = PA || PB;
     constexpr int NP = Cfg::NP;
@@ -567,7 +567,8 @@ void dma_gemm_kernel(GemmArgs p)
         for (int j = 0; j < NF; ++j) acc[i][j] = Acc{};
 
     // prologue: the copies the barriers of steps -VP .. -1 would have issued
-    // (steps 0 .. AHEAD-1, and with PAIR pairs 0 and 1), then wait for step 0
+    // (steps 0 .. AHEAD-1, and when paired pairs 0 .. NP-1), then wait for
+    // step 0
     if constexpr (!PAIRED) {
 #pragma unroll
         for (int s = 0; s < AHEAD; ++s)

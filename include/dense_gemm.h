@@ -182,8 +182,9 @@ gemm_status_t gemm_variant_tile(int id, int* bm, int* bn, int* bk);
  * K-steps between a step's copy into LDS and its first use (*ahead; S for a
  * barrier late in the step, S-1 for one half way).  Variants that copy
  * k-contiguous operands two K-steps at a time into pair buffers report the
- * ring of their other operands; a pair is copied three steps ahead of its
- * first step.  Any may be NULL.  GEMM_ERR_INVALID_VALUE for an unknown id. */
+ * ring of their other operands; a pair is copied three steps (with three
+ * pair buffers five steps) ahead of its first step.  Any may be NULL.
+ * GEMM_ERR_INVALID_VALUE for an unknown id. */
 gemm_status_t gemm_variant_pipeline(int id, int* stages, int* ahead);
 
 /* Workgroups of variant `id` (its NN kernel with 16-byte access) that fit on
