@@ -385,15 +385,16 @@ def oracle_full_small(cores: int):
     return out
 
 
+# How the traffic record is made ($OUT: the directory the profiler writes to)
 PMC_COMMANDS = {
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o fetch --output-format csv "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_fetch -o fetch --output-format csv "
              "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras "
              "--copy-probe 512",
-    "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o write --output-format csv "
+    "write": "rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_write -o write --output-format csv "
              "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras "
              "--copy-probe 512",
-    "ingest": "python bench.py --ingest-pmc gpurun_out/pmc_fetch/fetch_counter_collection.csv "
-              "gpurun_out/pmc_write/write_counter_collection.csv > profiles/hbm_traffic.json",
+    "ingest": "python bench.py --ingest-pmc $OUT/pmc_fetch/fetch_counter_collection.csv "
+              "$OUT/pmc_write/write_counter_collection.csv > profiles/hbm_traffic.json",
 }
 
 
