@@ -550,12 +550,22 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     // when that removes a round of tiles (4093x2051x1537: 544 tiles in one
     // round instead of a full round and a nearly empty one; measured 0.0593
     // vs 0.0624 ms), which the round and pipeline-depth model above decides.
-    // That variant has no transposed-output, bf16-output or fused-epilogue
-    // instantiations, so only plain fp32-output calls take it.
+    // Neither variant has transposed-output, bf16-output or fused-epilogue
+    // instantiations, so only plain fp32-output calls take them.
     if (sk == 0 && h->forced_variant < 0 && aligned && !epi && !out_bf16 &&
         id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
         static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
         if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < dp_us) id = s2;
+        // Otherwise, with a k-contiguous operand and more tiles than compute
+        // units (two workgroups on a unit hide the latency of the larger
+        // copies), the 4-stage ring copying that operand two K-steps at a
+        // time: measured 5-16 % faster from 324 to 544 tiles (2304^3 36.9
+        // vs 44.0 us, 2560^2 x 4096 62.0 vs 72.8) and 5-22 % slower at 256
+        // tiles and fewer.
+        static const int pair = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair");
+        if (id != s2 && pair >= 0 && (a_kc || b_kc) &&
+            ceil_div(M, 128) * ceil_div(N, 128) > (int64_t)device_cus())
+            id = pair;
     }
     const Variant& vr = table()[id];
     a.tiles_m = (int)ceil_div(M, vr.bm);

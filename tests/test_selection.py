@@ -22,9 +22,13 @@ CASES = [
     ("bf16", "N", "N", 3000, 3000, 512, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
     # ... but not with bf16 output, which only the 4-stage variant carries
     ("bf16", "T", "N", 4093, 2051, 1537, 1.5, True, P + "128x128x32_w2x2_s4_late", False),
-    # at most one round at 2 per CU: the 4-stage ring
+    # at most one tile per CU: the 4-stage ring
     ("bf16", "N", "N", 2048, 2048, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
-    ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    # more tiles than CUs, at most 2 per CU, a k-contiguous operand: paired copies
+    ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    ("bf16", "N", "T", 2304, 2304, 2304, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    # ... but not without one
+    ("bf16", "T", "N", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]
