@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -83,16 +84,20 @@ MFMA_KIND = {"mfma32x32x2": 0, "mfma16x16x4": 1, "mfma32x32x16": 2, "mfma16x16x3
 
 
 def kernel_name_key(variant_name: str, tile) -> str:
-    """Substring of the demangled kernel name that identifies a variant."""
+    """Start of the template arguments, in the demangled kernel name, that
+    identify a variant (the direct-to-LDS configuration continues with its
+    pairing mode, register hint and pair-buffer count, which the selected
+    variants' names do not spell out; they are one kernel each in a
+    record)."""
     bm, bn, bk = tile
     for tag, kind in MFMA_KIND.items():
         if f"_{tag}_" in variant_name:
             return f"MfmaConfig<{kind}, {bm}, {bn}, {bk},"
         if f"_dma{tag[4:]}_" in variant_name:
-            late = variant_name.endswith("_late")
-            stages = variant_name.removesuffix("_late").rsplit("_s", 1)[1]
+            late = "_late" in variant_name
+            stages = re.search(r"_s(\d+)(?:_|$)", variant_name).group(1)
             return (f"DmaConfig<{kind}, {bm}, {bn}, {bk}, 2, 2, {stages}, "
-                    f"{'true' if late else 'false'}>")
+                    f"{'true' if late else 'false'}")
     return f"FmaConfig<{bm}, {bn}, {bk}>"
 
 
@@ -107,7 +112,8 @@ def measured_traffic(variant_name: str, tile):
     if rec.get("kernel_src_digest") != kernel_source_digest():
         return None
     key = kernel_name_key(variant_name, tile)
-    hits = [v["hbm_bytes_per_launch"] for k, v in rec.get("kernels", {}).items() if key in k]
+    hits = [v["hbm_bytes_per_launch"] for k, v in rec.get("kernels", {}).items()
+            if key + ">" in k or key + ", " in k]
     return hits[0] if len(hits) == 1 else None
 
 

@@ -242,3 +242,20 @@ def test_pipeline_model_fit_recovers_parameters():
     capped = [r for r in m["rows"] if r["variant"] == "capped"][0]
     assert abs(capped["extended_err"]) < 0.01
     assert abs(capped["simple_err"] - (0.5 ** -0.4 - 1.0)) < 0.01
+
+
+def test_traffic_record_names_the_step_kernels():
+    """The committed HBM-traffic record holds exactly one kernel for each step
+    variant under the name matching bench.py uses (a record measured on other
+    sources is reported as null, but its names must still resolve)."""
+    import json
+    import os
+
+    import bench
+    with open(os.path.join(os.path.dirname(bench.__file__), "profiles", "hbm_traffic.json")) as f:
+        rec = json.load(f)
+    for name, tile in (("f32_dma32x32x2_256x256x32_w2x2_s2_late", (256, 256, 32)),
+                       ("bf16_dma32x32x16_256x256x32_w2x2_s3_late", (256, 256, 32))):
+        key = bench.kernel_name_key(name, tile)
+        hits = [k for k in rec["kernels"] if key + ">" in k or key + ", " in k]
+        assert len(hits) == 1, (name, key, list(rec["kernels"]))
