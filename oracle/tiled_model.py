@@ -1,4 +1,4 @@
-"""Counted naive and tiled matrix products and the closed-form traffic model.
+"""Counted untiled and tiled matrix products and the closed-form traffic model.
 
 Test infrastructure only (see the package docstring).
 
@@ -6,9 +6,9 @@ Follows "Understanding Roofline and Tiling through Matrix Multiplication —
 arithmetic intensity, data reuse, tile size":
   * section 6.2 (4x4 product with 2x2 output tiles and K-chunks of 2) and
     section 6.3 (logical order: per output tile, keep a T x T accumulator, walk
-    K in chunks of T, copy the A and B chunks on chip, accumulate, store the
+    K in chunks of T, bring the A and B chunks on chip, accumulate, store the
     tile once at the end);
-  * section 7.2 (no reuse: every multiply reads its A and B element again);
+  * section 7.2 (no reuse: every multiply fetches its A and B element again);
   * section 8.1 (traffic of the tiled product, Q_T = 8N^3/T + 4N^2 bytes for
     fp32) and section 8.5 (one-pass traffic 12N^2);
   * section 4.1 (roofline: t = max(F/P, Q/BW), ceiling min(P, BW*I)), and
@@ -16,10 +16,11 @@ arithmetic intensity, data reuse, tile size":
   * section 9.2.2 (resident blocks = min of the per-resource floors) and
     section 9.2.3 (occupancy = resident warps / maximum warps).
 
-Read/write counts are in elements (4 bytes each, fp32); a value copied into an
-on-chip chunk is counted once however often it is reused, and the accumulator
-is never written back before the K loop ends.  Pure Python loops: meant for
-tiny N only.
+Accounting rule (section 6.3 and 7.2 prose): an element counts as one
+off-chip read each time it is fetched from the operand matrices; once it sits
+in an on-chip block it is reused for free.  Writes count each output stored
+to C, and the accumulator is stored once, after its last K-chunk.  Counts are
+in elements (4 bytes each, fp32).  Pure Python: meant for tiny N only.
 """
 from __future__ import annotations
 
@@ -28,57 +29,86 @@ from fractions import Fraction
 ELEM_BYTES = 4
 
 
-def naive_counted(a, b):
-    """C = A @ B for square lists, re-reading A and B for every multiply."""
+class _Tally:
+    """Off-chip element reads and writes, and FLOPs (a multiply-add is 2)."""
+
+    def __init__(self):
+        self.reads = 0
+        self.writes = 0
+        self.flops = 0
+
+    def as_dict(self):
+        return {"reads": self.reads, "writes": self.writes, "flops": self.flops}
+
+
+def count_untiled_product(a, b):
+    """C = A @ B for square lists with no on-chip reuse (section 7.2).
+
+    Every output's dot product fetches its row of A and its column of B from
+    the operand matrices again.  Returns (C, totals)."""
     n = len(a)
-    counts = {"reads": 0, "writes": 0, "flops": 0}
-    c = [[0] * n for _ in range(n)]
-    for i in range(n):
+    tally = _Tally()
+    out = []
+    for row in a:
+        out_row = []
         for j in range(n):
-            acc = 0
-            for k in range(n):
-                x = a[i][k]
-                y = b[k][j]
-                counts["reads"] += 2
-                acc += x * y
-                counts["flops"] += 2          # one fused multiply-add = 2 FLOPs
-            c[i][j] = acc
-            counts["writes"] += 1
-    return c, counts
+            column = [b_row[j] for b_row in b]     # n fetches from B
+            tally.reads += len(row) + len(column)  # ... and n from A
+            value = 0
+            for x, y in zip(row, column):
+                value += x * y
+            tally.flops += 2 * n
+            out_row.append(value)
+            tally.writes += 1
+        out.append(out_row)
+    return out, tally.as_dict()
 
 
-def tiled_counted(a, b, tile):
+def _fetch_block(m, r0, c0, size):
+    """On-chip copy of the size x size block of m at (r0, c0), flat, row-major.
+
+    Its length is the number of off-chip element reads it costs."""
+    return [m[r0 + r][c0 + c] for r in range(size) for c in range(size)]
+
+
+def count_tiled_product(a, b, tile):
     """C = A @ B with tile x tile output tiles and K-chunks of width tile.
 
-    Returns the product, totals, and a per-(tile, K-step) log of reads/flops.
-    """
+    Output tiles are visited in row-major tile order; each keeps a flat
+    accumulator across its K-chunks.  For each chunk the A block (tile rows,
+    chunk columns) and the B block (chunk rows, tile columns) are fetched once
+    and every output of the tile takes its partial dot product from them.
+    Returns (C, totals, log) where log has one entry per (tile, K-chunk) with
+    the reads and FLOPs of that chunk."""
     n = len(a)
     if n % tile:
         raise ValueError("tile must divide n")
-    counts = {"reads": 0, "writes": 0, "flops": 0}
-    steps = []
-    c = [[None] * n for _ in range(n)]
-    for i0 in range(0, n, tile):
-        for j0 in range(0, n, tile):
-            acc = [[0] * tile for _ in range(tile)]
-            for k0 in range(0, n, tile):
-                step = {"reads": 0, "flops": 0}
-                at = [[a[i0 + i][k0 + k] for k in range(tile)] for i in range(tile)]
-                bt = [[b[k0 + k][j0 + j] for j in range(tile)] for k in range(tile)]
-                step["reads"] += 2 * tile * tile
-                for i in range(tile):
-                    for j in range(tile):
-                        for k in range(tile):
-                            acc[i][j] += at[i][k] * bt[k][j]
-                            step["flops"] += 2
-                counts["reads"] += step["reads"]
-                counts["flops"] += step["flops"]
-                steps.append(step)
-            for i in range(tile):
-                for j in range(tile):
-                    c[i0 + i][j0 + j] = acc[i][j]
-                    counts["writes"] += 1
-    return c, counts, steps
+    blocks = n // tile
+    tally = _Tally()
+    log = []
+    out = [[None] * n for _ in range(n)]
+    for t in range(blocks * blocks):
+        bi, bj = divmod(t, blocks)
+        acc = [0] * (tile * tile)
+        for q in range(blocks):
+            a_blk = _fetch_block(a, bi * tile, q * tile, tile)
+            b_blk = _fetch_block(b, q * tile, bj * tile, tile)
+            reads = len(a_blk) + len(b_blk)
+            flops = 0
+            for e in range(tile * tile):
+                r, c = divmod(e, tile)
+                a_part = a_blk[r * tile:(r + 1) * tile]   # row r of the A block
+                b_part = b_blk[c::tile]                   # column c of the B block
+                acc[e] += sum(x * y for x, y in zip(a_part, b_part))
+                flops += 2 * tile
+            tally.reads += reads
+            tally.flops += flops
+            log.append({"tile": (bi, bj), "chunk": q, "reads": reads, "flops": flops})
+        for e, value in enumerate(acc):
+            r, c = divmod(e, tile)
+            out[bi * tile + r][bj * tile + c] = value
+            tally.writes += 1
+    return out, tally.as_dict(), log
 
 
 def flops_square(n: int) -> int:

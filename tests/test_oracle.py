@@ -56,9 +56,13 @@ def test_worked_example_4x4_counts_and_result(lib):
     g = _golden("p5_worked_example_4x4.json")
     rng = np.random.default_rng(11)
     a, b = _int_matrix(rng, 4), _int_matrix(rng, 4)
-    c_t, cnt_t, steps = tm.tiled_counted(a, b, g["tile"])
-    c_n, cnt_n = tm.naive_counted(a, b)
+    c_t, cnt_t, steps = tm.count_tiled_product(a, b, g["tile"])
+    c_n, cnt_n = tm.count_untiled_product(a, b)
     eb = g["elem_bytes"]
+    # one log entry per (output tile, K-chunk), each visited once
+    n_chunks = 4 // g["tile"]
+    assert sorted((s["tile"], s["chunk"]) for s in steps) == sorted(
+        ((i, j), q) for i in range(n_chunks) for j in range(n_chunks) for q in range(n_chunks))
     # every (tile, K-step) reads 8 inputs and does 16 FLOPs
     assert all(s["reads"] == g["per_tile_step"]["reads"] for s in steps)
     assert all(s["flops"] == g["per_tile_step"]["flops"] for s in steps)
@@ -89,12 +93,12 @@ def test_counted_traffic_matches_closed_forms(lib, n):
     rng = np.random.default_rng(n)
     a, b = _int_matrix(rng, n), _int_matrix(rng, n)
     ref = _oracle_square(lib, a, b)
-    c_n, cnt_n = tm.naive_counted(a, b)
+    c_n, cnt_n = tm.count_untiled_product(a, b)
     assert (cnt_n["reads"] + cnt_n["writes"]) * 4 == tm.traffic_tiled_bytes(n, 1)
     assert cnt_n["flops"] == tm.flops_square(n)
     assert np.array_equal(np.array(c_n, np.float64), ref)
     for t in [t for t in range(1, n + 1) if n % t == 0]:
-        c_t, cnt_t, _ = tm.tiled_counted(a, b, t)
+        c_t, cnt_t, _ = tm.count_tiled_product(a, b, t)
         assert (cnt_t["reads"] + cnt_t["writes"]) * 4 == tm.traffic_tiled_bytes(n, t)
         assert cnt_t["flops"] == tm.flops_square(n)
         assert np.array_equal(np.array(c_t, np.float64), ref)
