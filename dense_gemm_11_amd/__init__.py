@@ -33,6 +33,7 @@ GEMM_ERR_INVALID_VALUE = 1
 GEMM_ERR_NOT_SUPPORTED = 2
 GEMM_ERR_HIP = 3
 GEMM_ERR_ALLOC = 4
+GEMM_ERR_STREAM_K = 5
 GEMM_ACT_NONE = 0
 GEMM_ACT_RELU = 1
 GEMM_ACT_GELU = 2
@@ -43,7 +44,8 @@ EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
            "gemm_variant_tile", "gemm_set_variant", "gemm_last_variant",
            "gemm_select_variant", "gemm_stream_k_workspace_bytes", "gemm_set_workspace",
            "gemm_set_stream_k", "gemm_last_stream_k", "gemm_run_epilogue",
-           "gemm_variant_pipeline", "gemm_variant_occupancy")
+           "gemm_variant_pipeline", "gemm_variant_occupancy", "gemm_stream_k_status",
+           "gemm_set_stream_k_poll_limit")
 
 
 class GemmEpilogue(ctypes.Structure):
@@ -124,6 +126,10 @@ def _load():
     lib.gemm_set_stream_k.restype = i32
     lib.gemm_last_stream_k.argtypes = [vp]
     lib.gemm_last_stream_k.restype = i32
+    lib.gemm_stream_k_status.argtypes = [vp, vp]
+    lib.gemm_stream_k_status.restype = i32
+    lib.gemm_set_stream_k_poll_limit.argtypes = [vp, i32]
+    lib.gemm_set_stream_k_poll_limit.restype = i32
     return lib
 
 
@@ -223,6 +229,15 @@ def gemm_set_stream_k(h, mode: int) -> int:
 
 def gemm_last_stream_k(h) -> int:
     return lib.gemm_last_stream_k(h)
+
+
+def gemm_stream_k_status(h, stream) -> int:
+    """Raw call: stream is an integer (0/None for the default stream)."""
+    return lib.gemm_stream_k_status(h, stream)
+
+
+def gemm_set_stream_k_poll_limit(h, polls: int) -> int:
+    return lib.gemm_set_stream_k_poll_limit(h, polls)
 
 
 def attach_workspace(h, nbytes=None, device=None):

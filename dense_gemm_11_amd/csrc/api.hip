@@ -1,6 +1,7 @@
 // C ABI of the dense GEMM library: argument validation, degenerate cases,
 // per-shape kernel selection and the launch.  Declared in include/dense_gemm.h.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -10,6 +11,7 @@
 #include "dense_gemm.h"
 #include "common.hpp"
 #include "variants.hpp"
+#include "sk_ranges.hpp"
 
 struct gemm_handle_s {
     int forced_variant;  // -1: automatic selection
@@ -18,6 +20,7 @@ struct gemm_handle_s {
     int last_stream_k;   // stream-K workgroups of the last call (0: data-parallel)
     void* ws;            // caller-owned device workspace for stream-K, or null
     size_t ws_bytes;
+    int sk_spin;         // polls a stream-K finisher spends on each contributor
 };
 
 namespace dg {
@@ -48,9 +51,14 @@ __global__ __launch_bounds__(256) void clear_flags_kernel(unsigned* flags, int n
 
 namespace {
 
-// Stream-K workspace layout: SK_MAX_WG flags, then one BM*BN fp32 slot per workgroup.
+// Stream-K workspace layout: SK_MAX_WG flags, the sticky error word (padded
+// to 256 bytes), then one BM*BN fp32 slot per workgroup.
 constexpr int SK_MAX_WG = 4096;
-constexpr size_t SK_FLAG_BYTES = SK_MAX_WG * sizeof(unsigned);
+constexpr int SK_FLAG_WORDS = SK_MAX_WG + 64;
+constexpr size_t SK_FLAG_BYTES = SK_FLAG_WORDS * sizeof(unsigned);
+// Default bound on a finisher's wait, in polls of about 100 ns per
+// contributor: far beyond any wait a resident contributor needs.
+constexpr int SK_SPIN_DEFAULT = 1 << 20;
 
 const std::vector<Variant>& table()
 {
@@ -58,7 +66,8 @@ const std::vector<Variant>& table()
         std::vector<Variant> v;
         for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
                          bf16dma_variant_table, f32dma_variant_table,
-                         bf16dma_sweep_variant_table, f32dma_sweep_variant_table}) {
+                         bf16dma_sweep_variant_table, f32dma_sweep_variant_table,
+                         bf16dma_tile_variant_table}) {
             int n = 0;
             const Variant* t = get(&n);
             v.insert(v.end(), t, t + n);
@@ -78,20 +87,34 @@ int find_variant(const char* name)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Compute units of the current device (cached per device id).
+// Per-device caches are indexed by device ordinal; devices beyond this many
+// are answered without caching.
+constexpr int MAX_DEVICES = 64;
+
+// Ordinal of the current device, or -1 when it cannot be queried.
+int current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    return dev;
+}
+
+// Compute units of the current device (cached per device; entry points may
+// be called from several threads at once, so the cache is atomic and a
+// value is only ever replaced by the same value).
 int device_cus()
 {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    static std::atomic<int> cached[MAX_DEVICES];
+    const int dev = current_device();
+    if (dev < 0) return 256;
+    int n = dev < MAX_DEVICES ? cached[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        if (dev < MAX_DEVICES) cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Per-shape selection.  Large tiles give the most reuse per LDS byte
@@ -160,15 +183,23 @@ double step_us(const Variant& v)
 }
 
 // Workgroups per compute unit of v's stream-K kernel (sk = true) or of its
-// data-parallel kernel, from the HIP occupancy query (cached per variant).
+// data-parallel kernel, from the HIP occupancy query (cached per device and
+// variant, atomically as for device_cus).
 int variant_occupancy(const Variant& v, bool sk = true)
 {
-    static int cache[2][64] = {};
+    constexpr int MAX_VARIANTS = 128;
+    static std::atomic<int> cache[MAX_DEVICES][2][MAX_VARIANTS];
     const int vid = (int)(&v - table().data());
     const OccFn f = sk ? v.sk_occ : v.occ;
-    if (!f || vid < 0 || vid >= 64) return v.bm * v.bn >= 256 * 256 ? 1 : 2;
-    if (cache[sk][vid] == 0) cache[sk][vid] = std::max(1, f());
-    return cache[sk][vid];
+    if (!f) return v.bm * v.bn >= 256 * 256 ? 1 : 2;
+    const int dev = current_device();
+    const bool cacheable = dev >= 0 && dev < MAX_DEVICES && vid >= 0 && vid < MAX_VARIANTS;
+    int n = cacheable ? cache[dev][sk][vid].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        n = std::max(1, f());
+        if (cacheable) cache[dev][sk][vid].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Estimated time of the data-parallel launch: waves of concurrently resident
@@ -209,14 +240,18 @@ int stream_k_grid(const Variant& v, int64_t M, int64_t N, int64_t K, int mode, s
     const int mf = v.bm / 2 / 32;  // fragment rows per wave (2x2 waves, 32-row fragments)
     int64_t cand[24];
     int nc = 0;
-    if (slots < 2 * tiles) cand[nc++] = std::max(slots, ceil_div(tiles, 2));
+    // Every workgroup of a stream-K grid must be resident at once (a finisher
+    // waits for lower-numbered workgroups), so the grid never exceeds the
+    // slots; a range spans at most two tiles' worth of iterations, so it is
+    // never below half the tiles.
+    if (slots < 2 * tiles && ceil_div(tiles, 2) <= slots) cand[nc++] = slots;
     for (int64_t g = 2 * tiles; g <= slots && nc < 24; g *= 2) cand[nc++] = g;
     int64_t best_g = 0;
     double best_us = 0.0;
     for (int i = 0; i < nc; ++i) {
         const int64_t gg = std::min<int64_t>(cand[i], W / 4);
         // each workgroup's range within two tiles' worth of iterations
-        if (gg < 2 || gg > SK_MAX_WG || ceil_div(W, gg) > 2 * nk) continue;
+        if (gg < 2 || gg > SK_MAX_WG || gg > slots || !sk_grid_ok(W, gg, nk)) continue;
         const size_t need = SK_FLAG_BYTES + (size_t)gg * v.bm * v.bn * sizeof(float);
         if (need > ws_bytes) continue;
         const int64_t per = ceil_div(W, gg);
@@ -265,6 +300,139 @@ bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
+// What a call looks like to the kernel choice.
+struct CallDesc {
+    int dtype;          // gemm_dtype_t
+    bool a_kc, b_kc;    // A with transA == N, B with transB == T
+    int64_t M, N, K, lda, ldb;
+    bool epi;           // a fused epilogue with something to do
+    bool wide;          // A and B element-aligned (16-byte accesses allowed)
+    int forced;         // forced variant, or -1
+    int sk_mode;        // stream-K policy (-1 automatic, 0 never, 1 when allowed)
+    size_t ws_bytes;    // stream-K workspace bytes (0: none)
+};
+
+// The choice for one call: the variant, stream-K grid (0: whole tiles),
+// whether the direct-to-LDS kernel's 16-byte path applies, whether a bf16 NN
+// call runs as D^T = B^T A^T, and the launch tables it needs.
+struct Plan {
+    int id = -1;
+    int sk = 0;
+    bool aligned = false;
+    bool nn_t = false;
+    const LaunchFn (*sk_fn)[2] = nullptr;
+    const EpiFns* ef = nullptr;
+};
+
+// Stream-K launch functions of a variant for a call's output type and
+// epilogue (null: the variant has none, so whole tiles).
+const LaunchFn (*sk_launchers(const Variant& x, int op_dtype, bool out_bf16, bool epi))[2]
+{
+    if (x.kind != KIND_MFMA_DMA || !x.sk_occ) return nullptr;
+    if (!out_bf16 && !epi) return x.sk_fn;
+    if (x.bm != 256 && x.bm != 128) return nullptr;
+    if (&x != &table()[dma_variant(op_dtype, x.bm == 256)]) return nullptr;
+    const SkFns* f = nullptr;
+    if (op_dtype == GEMM_DTYPE_F32) {
+        f = epi ? sk_fns_f32(x.bm) : nullptr;
+    } else {
+        const int kind = !epi ? 0 : out_bf16 ? 2 : 1;
+        f = x.bm == 256 ? sk_fns_bf16_256(kind) : sk_fns_bf16_128(kind);
+    }
+    return f ? f->fn : nullptr;
+}
+
+// The whole host choice for a call, shared by gemm_run and
+// gemm_select_variant.  Returns GEMM_OK or why the call cannot run.
+gemm_status_t plan_call(const CallDesc& c, Plan& pl)
+{
+    const int op_dtype = c.dtype == GEMM_DTYPE_F32 ? GEMM_DTYPE_F32 : GEMM_DTYPE_BF16_F32;
+    const bool out_bf16 = c.dtype == GEMM_DTYPE_BF16_BF16;
+    const int64_t es = op_dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    const int64_t M = c.M, N = c.N, K = c.K;
+    int id = c.forced;
+    if (id < 0) {
+        const Variant& big = table()[select_variant(op_dtype, M, N, K, true)];
+        id = select_variant(op_dtype, M, N, K,
+                            c.wide && dma_offsets_fit(big, c.a_kc, c.b_kc, K, c.lda, c.ldb, es));
+    }
+    const Variant& v = table()[id];
+    if (v.dtype != op_dtype) return GEMM_ERR_NOT_SUPPORTED;
+    // bf16 C/D: only the selected direct-to-LDS variants carry that epilogue,
+    // for element-aligned operands whose panel offsets fit in 32 bits
+    if (out_bf16 && !v.bo_nn_t_fn) return GEMM_ERR_NOT_SUPPORTED;
+    // a direct-to-LDS kernel whose offsets would overflow stages every step
+    // through registers instead (its ALIGNED == false instantiation)
+    const bool aligned =
+        c.wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, c.a_kc, c.b_kc, K, c.lda, c.ldb, es));
+    const double dp_us = data_parallel_us(v, M, N, K);
+    double sk_us = 0.0;
+    int sk = (aligned && sk_launchers(v, op_dtype, out_bf16, c.epi))
+                 ? stream_k_grid(v, M, N, K, c.sk_mode, c.ws_bytes, dp_us, &sk_us)
+                 : 0;
+    if (c.forced < 0 && aligned && v.kind == KIND_MFMA_DMA && c.sk_mode != 0) {
+        // With a workspace, stream-K on the other tile size competes too; the
+        // lowest estimate wins.
+        const int other = dma_variant(op_dtype, v.bm < 256);
+        if (other != id && sk_launchers(table()[other], op_dtype, out_bf16, c.epi) &&
+            dma_offsets_fit(table()[other], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
+            double o_us = 0.0;
+            const int sk_o =
+                stream_k_grid(table()[other], M, N, K, c.sk_mode, c.ws_bytes, dp_us, &o_us);
+            if (sk_o > 0 && (sk == 0 || o_us < sk_us)) {
+                id = other;
+                sk = sk_o;
+            }
+        }
+    }
+    // bf16 128x128 whole tiles: the 2-stage ring fits 3 workgroups on a
+    // compute unit where the 4-stage one fits 2.  The shallower ring wins
+    // when that removes a round of tiles (4093x2051x1537: 544 tiles in one
+    // round instead of a full round and a nearly empty one; measured 0.0593
+    // vs 0.0624 ms), which the round and pipeline-depth model above decides.
+    // Neither variant has transposed-output, bf16-output or fused-epilogue
+    // instantiations, so only plain fp32-output calls take them.
+    if (sk == 0 && c.forced < 0 && aligned && !c.epi && !out_bf16 &&
+        id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
+        static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
+        if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < dp_us) id = s2;
+        // Otherwise, with a k-contiguous operand and more tiles than compute
+        // units (two workgroups on a unit hide the latency of the larger
+        // copies), the 4-stage ring copying that operand two K-steps at a
+        // time: measured 5-16 % faster from 324 to 544 tiles (2304^3 36.9
+        // vs 44.0 us, 2560^2 x 4096 62.0 vs 72.8) and 5-22 % slower at 256
+        // tiles and fewer.
+        static const int pair = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair");
+        if (id != s2 && pair >= 0 && (c.a_kc || c.b_kc) &&
+            ceil_div(M, 128) * ceil_div(N, 128) > (int64_t)device_cus())
+            id = pair;
+    }
+    const Variant& vr = table()[id];
+    // bf16 NN with whole tiles: run as D^T = B^T A^T, which puts the
+    // mn-contiguous operand first (measured on 8192^3, same box: TT layout
+    // 1282 vs NN 1235 TFLOP/s); the transposed-output epilogue writes D.
+    const bool nn_t = sk == 0 && c.forced < 0 && vr.nn_t_fn && aligned && c.a_kc && !c.b_kc &&
+                      dma_offsets_fit(vr, false, true, K, c.ldb, c.lda, es);
+    if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
+    // fused epilogue: only the selected direct-to-LDS variants, whole tiles
+    // and wide access, carry it
+    const EpiFns* ef = nullptr;
+    if (c.epi) {
+        if (!aligned || id != dma_variant(op_dtype, vr.bm == 256)) return GEMM_ERR_NOT_SUPPORTED;
+        ef = op_dtype == GEMM_DTYPE_F32 ? epi_fns_f32(vr.bm)
+             : out_bf16                 ? epi_fns_bf16_out(vr.bm)
+                                        : epi_fns_bf16(vr.bm);
+        if (!ef) return GEMM_ERR_NOT_SUPPORTED;
+    }
+    pl.id = id;
+    pl.sk = sk;
+    pl.aligned = aligned;
+    pl.nn_t = nn_t;
+    pl.sk_fn = sk > 0 ? sk_launchers(vr, op_dtype, out_bf16, c.epi) : nullptr;
+    pl.ef = ef;
+    return GEMM_OK;
+}
+
 }  // namespace
 }  // namespace dg
 
@@ -273,7 +441,7 @@ extern "C" {
 gemm_status_t gemm_create(gemm_handle_t* out)
 {
     if (!out) return GEMM_ERR_INVALID_VALUE;
-    gemm_handle_t h = new (std::nothrow) gemm_handle_s{-1, -1, -1, 0, nullptr, 0};
+    gemm_handle_t h = new (std::nothrow) gemm_handle_s{-1, -1, -1, 0, nullptr, 0, dg::SK_SPIN_DEFAULT};
     if (!h) return GEMM_ERR_ALLOC;
     *out = h;
     return GEMM_OK;
@@ -293,6 +461,7 @@ const char* gemm_status_string(gemm_status_t s)
     case GEMM_ERR_NOT_SUPPORTED: return "GEMM_ERR_NOT_SUPPORTED";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
     case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC";
+    case GEMM_ERR_STREAM_K: return "GEMM_ERR_STREAM_K";
     }
     return "unknown status";
 }
@@ -348,6 +517,36 @@ int gemm_last_variant(gemm_handle_t h) { return h ? h->last_variant : -1; }
 
 int gemm_last_stream_k(gemm_handle_t h) { return h ? h->last_stream_k : -1; }
 
+gemm_status_t gemm_set_stream_k_poll_limit(gemm_handle_t h, int polls)
+{
+    if (!h || polls < -1) return GEMM_ERR_INVALID_VALUE;
+    h->sk_spin = polls < 0 ? dg::SK_SPIN_DEFAULT : polls;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_stream_k_status(gemm_handle_t h, hipStream_t stream)
+{
+    using namespace dg;
+    if (!h) return GEMM_ERR_INVALID_VALUE;
+    if (!h->ws) return GEMM_OK;
+    unsigned err = 0;
+    const unsigned* word = static_cast<const unsigned*>(h->ws) + SK_MAX_WG;
+    if (hipMemcpyAsync(&err, word, sizeof(err), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    if (err == 0) return GEMM_OK;
+    // a finisher gave up: contributors it did not wait for may have raised
+    // their flags after it; clear every flag and the error word
+    unsigned* flags = static_cast<unsigned*>(h->ws);
+    int n = SK_FLAG_WORDS;
+    void* kargs[] = {&flags, &n};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_flags_kernel), dim3(16), dim3(256),
+                        kargs, 0, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    return GEMM_ERR_STREAM_K;
+}
+
 size_t gemm_stream_k_workspace_bytes(void)
 {
     using namespace dg;
@@ -371,7 +570,7 @@ gemm_status_t gemm_set_workspace(gemm_handle_t h, void* ws, size_t bytes, hipStr
     }
     if (!aligned_to(ws, 256) || bytes < SK_FLAG_BYTES) return GEMM_ERR_INVALID_VALUE;
     unsigned* flags = static_cast<unsigned*>(ws);
-    int n = SK_MAX_WG;
+    int n = SK_FLAG_WORDS;
     void* kargs[] = {&flags, &n};
     if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_flags_kernel), dim3(16), dim3(256),
                         kargs, 0, stream) != hipSuccess)
@@ -394,8 +593,25 @@ int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, 
     if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16_F32 && dtype != GEMM_DTYPE_BF16_BF16) ||
         (transA != GEMM_OP_N && transA != GEMM_OP_T) || (transB != GEMM_OP_N && transB != GEMM_OP_T))
         return -1;
-    return dg::select_variant(dtype == GEMM_DTYPE_F32 ? GEMM_DTYPE_F32 : GEMM_DTYPE_BF16_F32, M, N,
-                              K, true);
+    if (M < 0 || N < 0 || K < 0) return -1;
+    // a call with element-aligned, tightly packed operands, no workspace and
+    // no fused epilogue
+    dg::CallDesc cd;
+    cd.dtype = dtype;
+    cd.a_kc = transA == GEMM_OP_N;
+    cd.b_kc = transB == GEMM_OP_T;
+    cd.M = M;
+    cd.N = N;
+    cd.K = K;
+    cd.lda = std::max<int64_t>(1, cd.a_kc ? K : M);
+    cd.ldb = std::max<int64_t>(1, cd.b_kc ? K : N);
+    cd.epi = false;
+    cd.wide = true;
+    cd.forced = -1;
+    cd.sk_mode = -1;
+    cd.ws_bytes = 0;
+    dg::Plan pl;
+    return dg::plan_call(cd, pl) == GEMM_OK ? pl.id : -1;
 }
 
 static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M,
@@ -472,6 +688,8 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     a.d_vec = aligned_to(D, es_out);
     a.sk_partials = nullptr;
     a.sk_flags = nullptr;
+    a.sk_error = nullptr;
+    a.sk_spin = h->sk_spin;
     a.bias = epi ? ep->bias : nullptr;
     a.act = epi ? (int)ep->activation : EPI_ACT_NONE;
     a.clamp = epi && ep->clamp;
@@ -487,86 +705,27 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
         return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     }
 
-    const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
-    // operand precision: the variants are keyed by it (bf16 operands serve
-    // both bf16 dtypes)
-    const int op_dtype = dtype == GEMM_DTYPE_F32 ? GEMM_DTYPE_F32 : GEMM_DTYPE_BF16_F32;
-    const bool a_kc = transA == GEMM_OP_N, b_kc = transB == GEMM_OP_T;
+    CallDesc cd;
+    cd.dtype = dtype;
+    cd.a_kc = transA == GEMM_OP_N;
+    cd.b_kc = transB == GEMM_OP_T;
+    cd.M = M;
+    cd.N = N;
+    cd.K = K;
+    cd.lda = lda;
+    cd.ldb = ldb;
+    cd.epi = epi;
     // wide (16-byte) operand access needs element-aligned A and B only
-    const bool wide = aligned_to(A, es) && aligned_to(B, es);
-    int id = h->forced_variant;
-    if (id < 0) {
-        const Variant& big = table()[select_variant(op_dtype, M, N, K, true)];
-        id = select_variant(op_dtype, M, N, K,
-                            wide && dma_offsets_fit(big, a_kc, b_kc, K, lda, ldb, es));
-    }
-    const Variant& v = table()[id];
-    if (v.dtype != op_dtype) return GEMM_ERR_NOT_SUPPORTED;
-    // bf16 C/D: only the selected direct-to-LDS variants carry that epilogue,
-    // for element-aligned operands whose panel offsets fit in 32 bits
-    if (out_bf16 && !v.bo_nn_t_fn) return GEMM_ERR_NOT_SUPPORTED;
-    // a direct-to-LDS kernel whose offsets would overflow stages every step
-    // through registers instead (its ALIGNED == false instantiation)
-    const bool aligned =
-        wide && (v.kind != KIND_MFMA_DMA || dma_offsets_fit(v, a_kc, b_kc, K, lda, ldb, es));
-    const double dp_us = data_parallel_us(v, M, N, K);
-    double sk_us = 0.0;
-    // stream-K launch functions of a variant for this call's output type and
-    // epilogue (null: the variant has none, so whole tiles)
-    auto sk_fns = [&](const Variant& x) -> const LaunchFn(*)[2] {
-        if (x.kind != KIND_MFMA_DMA || !x.sk_occ) return nullptr;
-        if (!out_bf16 && !epi) return x.sk_fn;
-        if (x.bm != 256 && x.bm != 128) return nullptr;
-        if (&x != &table()[dma_variant(op_dtype, x.bm == 256)]) return nullptr;
-        const SkFns* f = nullptr;
-        if (op_dtype == GEMM_DTYPE_F32) {
-            f = epi ? sk_fns_f32(x.bm) : nullptr;
-        } else {
-            const int kind = !epi ? 0 : out_bf16 ? 2 : 1;
-            f = x.bm == 256 ? sk_fns_bf16_256(kind) : sk_fns_bf16_128(kind);
-        }
-        return f ? f->fn : nullptr;
-    };
-    int sk = (aligned && sk_fns(v))
-                 ? stream_k_grid(v, M, N, K, h->stream_k_mode, h->ws_bytes, dp_us, &sk_us)
-                 : 0;
-    if (h->forced_variant < 0 && aligned && v.kind == KIND_MFMA_DMA && h->stream_k_mode != 0) {
-        // With a workspace, stream-K on the other tile size competes too; the
-        // lowest estimate wins.
-        const int other = dma_variant(op_dtype, v.bm < 256);
-        if (other != id && sk_fns(table()[other]) &&
-            dma_offsets_fit(table()[other], a_kc, b_kc, K, lda, ldb, es)) {
-            double o_us = 0.0;
-            const int sk_o = stream_k_grid(table()[other], M, N, K, h->stream_k_mode, h->ws_bytes,
-                                           dp_us, &o_us);
-            if (sk_o > 0 && (sk == 0 || o_us < sk_us)) {
-                id = other;
-                sk = sk_o;
-            }
-        }
-    }
-    // bf16 128x128 whole tiles: the 2-stage ring fits 3 workgroups on a
-    // compute unit where the 4-stage one fits 2.  The shallower ring wins
-    // when that removes a round of tiles (4093x2051x1537: 544 tiles in one
-    // round instead of a full round and a nearly empty one; measured 0.0593
-    // vs 0.0624 ms), which the round and pipeline-depth model above decides.
-    // Neither variant has transposed-output, bf16-output or fused-epilogue
-    // instantiations, so only plain fp32-output calls take them.
-    if (sk == 0 && h->forced_variant < 0 && aligned && !epi && !out_bf16 &&
-        id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
-        static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
-        if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < dp_us) id = s2;
-        // Otherwise, with a k-contiguous operand and more tiles than compute
-        // units (two workgroups on a unit hide the latency of the larger
-        // copies), the 4-stage ring copying that operand two K-steps at a
-        // time: measured 5-16 % faster from 324 to 544 tiles (2304^3 36.9
-        // vs 44.0 us, 2560^2 x 4096 62.0 vs 72.8) and 5-22 % slower at 256
-        // tiles and fewer.
-        static const int pair = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair");
-        if (id != s2 && pair >= 0 && (a_kc || b_kc) &&
-            ceil_div(M, 128) * ceil_div(N, 128) > (int64_t)device_cus())
-            id = pair;
-    }
+    const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    cd.wide = aligned_to(A, es) && aligned_to(B, es);
+    cd.forced = h->forced_variant;
+    cd.sk_mode = h->stream_k_mode;
+    cd.ws_bytes = h->ws_bytes;
+    Plan pl;
+    const gemm_status_t ps = plan_call(cd, pl);
+    if (ps != GEMM_OK) return ps;
+    const int id = pl.id, sk = pl.sk;
+    const bool aligned = pl.aligned, nn_t = pl.nn_t, a_kc = cd.a_kc, b_kc = cd.b_kc;
     const Variant& vr = table()[id];
     a.tiles_m = (int)ceil_div(M, vr.bm);
     a.tiles_n = (int)ceil_div(N, vr.bn);
@@ -576,26 +735,12 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
     hipError_t e;
-    // bf16 NN with whole tiles: run as D^T = B^T A^T, which puts the
-    // mn-contiguous operand first (measured on 8192^3, same box: TT layout
-    // 1282 vs NN 1235 TFLOP/s); the transposed-output epilogue writes D.
-    const bool nn_t = sk == 0 && h->forced_variant < 0 && vr.nn_t_fn && aligned && a_kc &&
-                      !b_kc && dma_offsets_fit(vr, false, true, K, ldb, lda, es);
-    if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
-    // fused epilogue: only the selected direct-to-LDS variants, whole tiles
-    // and wide access, carry it
-    const EpiFns* ef = nullptr;
-    if (epi) {
-        if (!aligned || id != dma_variant(op_dtype, vr.bm == 256)) return GEMM_ERR_NOT_SUPPORTED;
-        ef = op_dtype == GEMM_DTYPE_F32 ? epi_fns_f32(vr.bm)
-             : out_bf16                 ? epi_fns_bf16_out(vr.bm)
-                                        : epi_fns_bf16(vr.bm);
-        if (!ef) return GEMM_ERR_NOT_SUPPORTED;
-    }
+    const EpiFns* ef = pl.ef;
     if (sk > 0) {
         a.sk_flags = static_cast<unsigned*>(h->ws);
+        a.sk_error = a.sk_flags + SK_MAX_WG;
         a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
-        e = sk_fns(vr)[a_kc][b_kc](a, sk, stream);
+        e = pl.sk_fn[a_kc][b_kc](a, sk, stream);
     } else if (nn_t) {
         GemmArgs t = a;
         t.A = B;

@@ -26,6 +26,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
+// Vectors for global-memory accesses at addresses that are only element
+// aligned (odd leading dimensions, sub-views).  The declared alignment is the
+// real one; the AMDGPU backend still emits a single 16- or 8-byte access for
+// them, relying on the unaligned access mode that the ROCm driver enables on
+// gfx9 and later, in which the memory system serves such accesses whole.
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint16_t u16x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef __bf16 bf16x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+// 16 bytes of elements of type T at an address aligned to sizeof(T)
+template <typename T>
+using u32x4_elem = std::conditional_t<sizeof(T) == 2, u32x4_a2, u32x4_a4>;
+
 // Everything a kernel needs for one GEMM call (passed by value as kernarg).
 struct GemmArgs {
     const void* A;
@@ -39,9 +53,13 @@ struct GemmArgs {
     int group_m;           // tile-rows walked together for L2/MALL reuse
     int c_vec;             // C rows allow 16-byte loads (pointer and ldc aligned)
     int d_vec;             // D rows allow 16-byte stores
-    // stream-K only: one BM*BN partial-sum slot and one flag per workgroup
+    // stream-K only: one BM*BN partial-sum slot and one flag per workgroup,
+    // a sticky error word set when a finisher's wait gives up, and the bound
+    // on that wait (polls per contributor)
     float* sk_partials;
     unsigned* sk_flags;
+    unsigned* sk_error;
+    int sk_spin;
     // fused epilogue, applied after alpha*acc + beta*C in this order: bias
     // (one value per D column, element type of D; null = none), activation
     // (EPI_ACT_*), clamp to [clamp_lo, clamp_hi] when clamp != 0

@@ -63,7 +63,7 @@ struct FmaLoader {
                 const int k = k0 + (q % (BK / 4)) * 4;
                 const float* src = panel + (int64_t)row * ld + k;
                 if (!GUARD || (ALIGNED && row < rlim && k + 4 <= K)) {
-                    reg[i] = *reinterpret_cast<const f32x4*>(src);
+                    reg[i] = *reinterpret_cast<const f32x4_a4*>(src);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) reg[i][j] = (row < rlim && k + j < K) ? src[j] : 0.0f;
@@ -73,7 +73,7 @@ struct FmaLoader {
                 const int k = k0 + q / (R / 4);
                 const float* src = panel + (int64_t)k * ld + mn;
                 if (!GUARD || (ALIGNED && k < K && mn + 4 <= rlim)) {
-                    reg[i] = *reinterpret_cast<const f32x4*>(src);
+                    reg[i] = *reinterpret_cast<const f32x4_a4*>(src);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) reg[i][j] = (k < K && mn + j < rlim) ? src[j] : 0.0f;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
             if (p.d_vec && col + 4 <= p.N) {
                 if (beta != 0.0f) {
                     if (p.c_vec) {
-                        const f32x4 c = *reinterpret_cast<const f32x4*>(crow + col);
+                        const f32x4 c = *reinterpret_cast<const f32x4_a4*>(crow + col);
 #pragma unroll
                         for (int s = 0; s < 4; ++s) out[s] += beta * c[s];
                     } else {
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 4))) voi
                         for (int s = 0; s < 4; ++s) out[s] += beta * crow[col + s];
                     }
                 }
-                *reinterpret_cast<f32x4*>(drow + col) = f32x4{out[0], out[1], out[2], out[3]};
+                *reinterpret_cast<f32x4_a4*>(drow + col) = f32x4{out[0], out[1], out[2], out[3]};
             } else {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {

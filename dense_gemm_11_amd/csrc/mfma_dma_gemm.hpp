@@ -47,6 +47,7 @@
 
 #include "common.hpp"
 #include "mfma_gemm.hpp"
+#include "sk_ranges.hpp"
 
 namespace dg {
 
@@ -275,7 +276,8 @@ struct DmaOperand {
     {
         // in batches of GB chunks per thread, which bounds the registers this
         // path adds on top of the accumulators and fragments
-        constexpr int GB = GL < 4 ? GL : 4;
+        constexpr int GB_MAX = Cfg::WPE > 1 ? 1 : 4;
+        constexpr int GB = GL < GB_MAX ? GL : GB_MAX;
 #pragma unroll
         for (int i0 = 0; i0 < GL; i0 += GB) {
             u32x4 v[GB];
@@ -289,7 +291,7 @@ struct DmaOperand {
                     const int k = k0 + c * VEC;
                     const T* src = panel + (int64_t)row * ld + k;
                     if (ALIGNED && row < rlim && k + VEC <= K) {
-                        v[b] = *reinterpret_cast<const u32x4*>(src);
+                        v[b] = *reinterpret_cast<const u32x4_elem<T>*>(src);
                         continue;
                     }
 #pragma unroll
@@ -298,7 +300,7 @@ struct DmaOperand {
                     const int k = k0 + row, mn = c * VEC;
                     const T* src = panel + (int64_t)k * ld + mn;
                     if (ALIGNED && k < K && mn + VEC <= rlim) {
-                        v[b] = *reinterpret_cast<const u32x4*>(src);
+                        v[b] = *reinterpret_cast<const u32x4_elem<T>*>(src);
                         continue;
                     }
 #pragma unroll
@@ -788,15 +790,15 @@ void dma_gemm_kernel(GemmArgs p)
     using OutT = std::conditional_t<OUT_BF16, bf16_t, float>;
     auto load4 = [](const OutT* q) __attribute__((always_inline)) -> f32x4 {
         if constexpr (OUT_BF16) {
-            const u16x4 h = *reinterpret_cast<const u16x4*>(q);
+            const u16x4 h = *reinterpret_cast<const u16x4_a2*>(q);
             return f32x4{to_f32(h[0]), to_f32(h[1]), to_f32(h[2]), to_f32(h[3])};
         } else {
-            return *reinterpret_cast<const f32x4*>(q);
+            return *reinterpret_cast<const f32x4_a4*>(q);
         }
     };
     auto store4 = [](OutT* q, f32x4 v) __attribute__((always_inline)) {
-        if constexpr (OUT_BF16) *reinterpret_cast<bf16x4*>(q) = __builtin_convertvector(v, bf16x4);
-        else *reinterpret_cast<f32x4*>(q) = v;
+        if constexpr (OUT_BF16) *reinterpret_cast<bf16x4_a2*>(q) = __builtin_convertvector(v, bf16x4);
+        else *reinterpret_cast<f32x4_a4*>(q) = v;
     };
 
     // ---- epilogue.  A lane's accumulator group holds 4 adjacent columns of
@@ -813,27 +815,41 @@ void dma_gemm_kernel(GemmArgs p)
     // GPUs", section 4: the epilogue stores the accumulator in the output
     // layout).  Stream-K partial sums (contributors c0..c1, none when
     // c0 == c1) are added in registers, in workgroup order, before staging.
-    auto epilogue = [&](int tm, int tn, int64_t c0, int64_t c1) __attribute__((always_inline)) {
+    // poison: write NaN-scaled results (a stream-K finisher whose wait for a
+    // contributor gave up; the sticky error word is the authoritative signal)
+    auto epilogue = [&](int tm, int tn, int64_t c0, int64_t c1, bool poison = false)
+                        __attribute__((always_inline)) {
     const int m0 = tm * BM, n0 = tn * BN;
-    const float alpha = p.alpha, beta = p.beta;
+    const float alpha = poison ? __builtin_nanf("") : p.alpha, beta = p.beta;
     constexpr int VG = Cfg::ACC / 4;
     // D is M x N, or N x M when the output is transposed
     const int d_rows = OUT_T ? p.N : p.M, d_cols = OUT_T ? p.M : p.N;
     const int in_frag = FM == 32 ? 4 * (lane >> 5) : 4 * (lane >> 4);
-    constexpr int NO = OUT_T ? NF : MF, NQ = OUT_T ? MF : NF;
-    constexpr int DC = NQ * FM;        // D columns of the wave's block
-    constexpr int CH = DC / 4;         // 16-byte chunks per staged row
-    constexpr int RPI = 64 / CH;       // staged rows per read instruction
-    constexpr int NT = FM / RPI;       // read instructions per batch
-    constexpr int REGION = FM * DC * 4;
+    constexpr int NO = OUT_T ? NF : MF, NQA = OUT_T ? MF : NF;
     // the blocks use the first NSA stage arrays, or the pair buffers when
     // those are larger (naming only those keeps the others out of the kernel
     // when S does not need them)
     constexpr bool USE_PR = PR_BYTES > ST_BYTES;
-    constexpr int WPS = (USE_PR ? PR_BYTES : ST_BYTES) / REGION;  // wave blocks per array
-    static_assert(CH >= 16 && CH <= 64 && 64 % CH == 0, "staging shape");
-    constexpr int NSA = WPS >= 1 ? (Cfg::WAVES + WPS - 1) / WPS : 99;
-    static_assert(NSA <= (USE_PR ? 2 : S) && NSA <= 3, "staging space");
+    constexpr int ARR = USE_PR ? PR_BYTES : ST_BYTES;
+    constexpr int MAXA = USE_PR ? 2 : (S < 3 ? S : 3);
+    // fragment columns staged per pass: all NQA of a fragment row when every
+    // wave's block fits in MAXA arrays, else half of them in two passes
+    constexpr auto fits = [](int qb) constexpr {
+        const int wps = ARR / (FM * qb * FM * 4);
+        return qb * FM / 4 >= 16 && qb * FM / 4 <= 64 && wps >= 1 &&
+               (Cfg::WAVES + wps - 1) / wps <= MAXA;
+    };
+    constexpr int NQ = fits(NQA) ? NQA : NQA / 2;
+    static_assert(NQ >= 1 && NQA % NQ == 0 && fits(NQ), "staging space");
+    constexpr int QH = NQA / NQ;       // passes per fragment row
+    constexpr int DC = NQ * FM;        // D columns of the wave's block in one pass
+    constexpr int CH = DC / 4;         // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CH;       // staged rows per read instruction
+    constexpr int NT = FM / RPI;       // read instructions per batch
+    constexpr int REGION = FM * DC * 4;
+    constexpr int WPS = ARR / REGION;  // wave blocks per array
+    static_assert(64 % CH == 0, "staging shape");
+    constexpr int NSA = (Cfg::WAVES + WPS - 1) / WPS;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     char* base = USE_PR ? pr0 : st0;
     if constexpr (NSA > 1) base = wv / WPS == 1 ? (USE_PR ? pr1 : st1) : base;
@@ -842,27 +858,32 @@ void dma_gemm_kernel(GemmArgs p)
     auto slot = [&](int r, int chunk) __attribute__((always_inline)) -> f32x4* {
         return reinterpret_cast<f32x4*>(region + r * (DC * 4) + ((chunk ^ (r & 15)) * 16));
     };
-    // first D row and column of the wave's block; the lane's 4 D columns
+    // first D row and column of the wave's block; the lane's 4 D columns in
+    // pass qh start at col0 + qh * DC
     const int wr0 = OUT_T ? n0 + wave_n0 : m0 + wave_m0;
-    const int col = (OUT_T ? m0 + wave_m0 : n0 + wave_n0) + 4 * (lane % CH);
-    const bool col_vec = p.d_vec && col + 4 <= d_cols;
+    const int col0 = (OUT_T ? m0 + wave_m0 : n0 + wave_n0) + 4 * (lane % CH);
     // whole tile inside D with 16-byte rows: no per-row or per-element checks
     const bool interior = m0 + BM <= p.M && n0 + BN <= p.N && p.d_vec &&
                           (beta == 0.0f || p.c_vec);
-    // the lane's columns are the same in every batch: their bias is read once
-    float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // the lane's columns are the same in every fragment row: their bias is
+    // read once
+    float bias4[QH][4] = {};
     if constexpr (EPI) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            if (col + s < d_cols) bias4[s] = bias_of<OutT>(p, col + s);
+        for (int qh = 0; qh < QH; ++qh)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (col0 + qh * DC + s < d_cols) bias4[qh][s] = bias_of<OutT>(p, col0 + qh * DC + s);
     }
     __syncthreads();  // every wave is done reading operands from the stage arrays
-    static_for<NO>([&](auto o_c) __attribute__((always_inline)) {
-        constexpr int o = decltype(o_c)::value;
+    static_for<NO * QH>([&](auto oq_c) __attribute__((always_inline)) {
+        constexpr int o = decltype(oq_c)::value / QH, qh = decltype(oq_c)::value % QH;
+        const int col = col0 + qh * DC;
+        const bool col_vec = p.d_vec && col + 4 <= d_cols;
         f32x4 sum[NQ][VG];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int i = OUT_T ? q : o, j = OUT_T ? o : q;
+            const int i = OUT_T ? qh * NQ + q : o, j = OUT_T ? o : qh * NQ + q;
 #pragma unroll
             for (int vg = 0; vg < VG; ++vg)
                 sum[q][vg] = f32x4{acc[i][j][4 * vg], acc[i][j][4 * vg + 1], acc[i][j][4 * vg + 2],
@@ -879,8 +900,8 @@ void dma_gemm_kernel(GemmArgs p)
                         v[q][vg] = __builtin_bit_cast(
                             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                        rsrc,
-                                       part_index(OUT_T ? q : o, OUT_T ? o : q, vg) * 16, 0,
-                                       CPOL_SC1));
+                                       part_index(OUT_T ? qh * NQ + q : o, OUT_T ? o : qh * NQ + q, vg) * 16,
+                                       0, CPOL_SC1));
 #pragma unroll
                 for (int q = 0; q < NQ; ++q)
 #pragma unroll
@@ -909,7 +930,7 @@ void dma_gemm_kernel(GemmArgs p)
                     out += beta * load4(reinterpret_cast<const OutT*>(p.C) + row * p.ldc + col);
                 if constexpr (EPI)
                     out = epilogue_fixed4<decltype(act_c)::value, decltype(clamp_c)::value>(p, out,
-                                                                                          bias4);
+                                                                                          bias4[qh]);
                 store4(reinterpret_cast<OutT*>(p.D) + row * p.ldd + col, out);
             }
         };
@@ -947,7 +968,7 @@ void dma_gemm_kernel(GemmArgs p)
                     }
                     out += beta * cv;
                 }
-                if constexpr (EPI) out = epilogue_op4(p, out, bias4);
+                if constexpr (EPI) out = epilogue_op4(p, out, bias4[qh]);
                 OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
                 if (col_vec) {
                     store4(drow + col, out);
@@ -970,24 +991,28 @@ void dma_gemm_kernel(GemmArgs p)
         // Stream-K ("GEMM on NVIDIA GPUs", section 5: split-K partial sums
         // P^(s) = sum over a K range, reduced afterwards).  The grid's G
         // workgroups split the W = tiles * nk_all (tile, K-step) iterations
-        // evenly: workgroup g takes [g*W/G, (g+1)*W/G).  Its range is the
-        // tail of a first tile, a whole tile, and the head of a last tile.  A
-        // tile is finished by the workgroup that reaches its last K-step;
-        // every other workgroup touching the tile ends its range inside it,
-        // stores its partial sums to its own workspace slot and raises its
-        // flag (a workgroup contributes to at most one tile: the one its
-        // range ends in).  A workgroup does that contributing segment first
-        // and its whole tiles next, so no contribution waits behind another
-        // tile's fix-up; the finishing segment comes last.  The finisher
-        // waits for the lower-numbered contributors, adds their partials in
-        // workgroup (= K) order, so the result is reproducible, and runs the
-        // epilogue.  Contributions are published before any wait, and a
-        // finisher only waits for lower-numbered workgroups, which were
-        // dispatched before it, so the waits cannot deadlock; they are
-        // bounded as well.
+        // evenly (sk_ranges.hpp).  A tile is finished by the workgroup that
+        // reaches its last K-step; every other workgroup touching the tile
+        // ends its range inside it, stores its partial sums to its own
+        // workspace slot and raises its flag (a workgroup contributes to at
+        // most one tile: the one its range ends in).  A workgroup does that
+        // contributing segment first and its whole tiles next, so no
+        // contribution waits behind another tile's fix-up; the finishing
+        // segment comes last.  The finisher waits for the lower-numbered
+        // contributors, adds their partials in workgroup (= K) order, so the
+        // result is reproducible, clears their flags and runs the epilogue.
+        // Contributions are published before any wait, and a finisher only
+        // waits for lower-numbered workgroups, which the host keeps resident
+        // at the same time (the grid never exceeds the workgroup slots), so
+        // the waits cannot deadlock.  They are bounded as well (p.sk_spin
+        // polls per contributor): a finisher that gives up adds no partial
+        // and clears no flag, writes NaN to its tile and sets the sticky
+        // error word; the host reports it and clears the whole flag area.
+        __shared__ int sk_ok;
         const int64_t W = (int64_t)p.tiles_m * p.tiles_n * nk_all;
         const int64_t G = gridDim.x, g = blockIdx.x;
-        const int64_t w_end = (g + 1) * W / G;
+        const SkRange rg = sk_range(W, G, g, nk_all);
+        const int64_t w_end = rg.w_end;
         // one segment: the iterations from w to the end of w's tile or of the
         // range, whichever comes first
         auto segment = [&](int64_t w) __attribute__((always_inline)) {
@@ -1001,23 +1026,37 @@ void dma_gemm_kernel(GemmArgs p)
             tile_work(tm, tn, k_lo, k_hi);
             if (k_hi == nk_all) {
                 // contributors: the workgroups owning iterations t*nk_all .. w-1
-                const int64_t c0 = k_lo > 0 ? ((int64_t)t * nk_all * G + G - 1) / W : g;
+                const int64_t c0 = k_lo > 0 ? sk_owner((int64_t)t * nk_all, W, G) : g;
+                bool ok = true;
                 if (c0 < g) {
                     if (tid == 0) {
-                        for (int64_t c = c0; c < g; ++c) {
-                            for (int it = 0; it < (1 << 20); ++it) {
+                        int got = 1;
+                        for (int64_t c = c0; c < g && got; ++c) {
+                            got = 0;
+                            for (int it = 0; it < p.sk_spin; ++it) {
                                 if (__hip_atomic_load(p.sk_flags + c, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                                                      __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                                    got = 1;
                                     break;
+                                }
                                 __builtin_amdgcn_s_sleep(2);
                             }
-                            __hip_atomic_store(p.sk_flags + c, 0u, __ATOMIC_RELAXED,
+                        }
+                        if (got) {
+                            for (int64_t c = c0; c < g; ++c)
+                                __hip_atomic_store(p.sk_flags + c, 0u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                        } else {
+                            __hip_atomic_store(p.sk_error, 1u, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
                         }
+                        sk_ok = got;
                     }
                     __syncthreads();
+                    ok = sk_ok != 0;
                 }
-                epilogue(tm, tn, c0, g);
+                if (ok) epilogue(tm, tn, c0, g);
+                else epilogue(tm, tn, g, g, true);
             } else {
                 const auto rsrc = part_rsrc(g);
 #pragma unroll
@@ -1038,20 +1077,14 @@ void dma_gemm_kernel(GemmArgs p)
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
         };
-        // The host keeps every range within two tiles' worth of iterations
-        // (G >= W / (2 nk)), so a range is at most a first tile's tail (or
-        // the whole first tile), one whole tile, and a last tile's head:
-        // three straight-line segments (a loop over them keeps far more
-        // registers live).
-        const int64_t w0 = g * W / G;
-        if (w0 >= w_end) return;
-        const int64_t t_first = w0 / nk_all, t_last = (w_end - 1) / nk_all;
-        // the range ends inside a later tile: its head is the contribution
-        const bool head = t_last > t_first && w_end < (t_last + 1) * nk_all;
-        const bool mid = t_last - t_first - (head ? 1 : 0) >= 1;  // one whole tile after the first
-        if (head) segment(t_last * nk_all);
-        if (mid) segment((t_first + 1) * nk_all);
-        segment(w0);
+        // The host keeps every range within two tiles' worth of iterations,
+        // so a range is at most a first tile's tail (or the whole first
+        // tile), one whole tile, and a last tile's head: three straight-line
+        // segments (a loop over them keeps far more registers live).
+        if (rg.w0 >= w_end) return;
+        if (rg.head) segment(rg.t_last * nk_all);
+        if (rg.mid) segment((rg.t_first + 1) * nk_all);
+        segment(rg.w0);
     }
 }
 

@@ -186,7 +186,7 @@ struct TileLoader {
                 const int k = k0 + (q % CPR) * VEC;
                 const T* src = panel + (int64_t)row * ld + k;
                 if (!GUARD || (ALIGNED && row < rlim && k + VEC <= K)) {
-                    reg[i] = *reinterpret_cast<const u32x4*>(src);
+                    reg[i] = *reinterpret_cast<const u32x4_elem<T>*>(src);
                 } else {
                     T e[VEC];
 #pragma unroll
@@ -206,7 +206,7 @@ struct TileLoader {
                     const int k = kb + kk;
                     const T* src = panel + (int64_t)k * ld + mn;
                     if (!GUARD || (ALIGNED && k < K && mn + VEC <= rlim)) {
-                        reg[b * VEC + kk] = *reinterpret_cast<const u32x4*>(src);
+                        reg[b * VEC + kk] = *reinterpret_cast<const u32x4_elem<T>*>(src);
                     } else {
                         T e[VEC];
 #pragma unroll
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void mfma_gemm_kernel(GemmArgs p)
                     if (beta != 0.0f) {
                         const float* crow = p.C + (int64_t)row * p.ldc;
                         if (p.c_vec) {
-                            const f32x4 c = *reinterpret_cast<const f32x4*>(crow + col);
+                            const f32x4 c = *reinterpret_cast<const f32x4_a4*>(crow + col);
 #pragma unroll
                             for (int s = 0; s < IL; ++s) out[s] += beta * c[s];
                         } else {
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void mfma_gemm_kernel(GemmArgs p)
                             for (int s = 0; s < IL; ++s) out[s] += beta * crow[col + s];
                         }
                     }
-                    *reinterpret_cast<f32x4*>(drow + col) = f32x4{out[0], out[1 % IL], out[2 % IL], out[3 % IL]};
+                    *reinterpret_cast<f32x4_a4*>(drow + col) = f32x4{out[0], out[1 % IL], out[2 % IL], out[3 % IL]};
                 } else {
 #pragma unroll
                     for (int s = 0; s < IL; ++s) {

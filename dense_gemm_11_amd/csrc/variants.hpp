@@ -93,6 +93,7 @@ const Variant* bf16dma_variant_table(int* count);
 const Variant* f32dma_variant_table(int* count);
 const Variant* bf16dma_sweep_variant_table(int* count);
 const Variant* f32dma_sweep_variant_table(int* count);
+const Variant* bf16dma_tile_variant_table(int* count);
 
 }  // namespace dg
 

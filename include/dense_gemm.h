@@ -60,6 +60,8 @@
  *       does not handle the call's dtype.
  *   GEMM_ERR_HIP : the HIP runtime rejected the kernel launch.
  *   GEMM_ERR_ALLOC : gemm_create could not allocate its handle.
+ *   GEMM_ERR_STREAM_K : reported by gemm_stream_k_status only: a stream-K
+ *       finisher gave up waiting for a contributor (see that function).
  * Pointer alignment is never an error: misaligned operands select kernels
  * with narrower memory accesses.
  */
@@ -89,7 +91,8 @@ typedef enum {
     GEMM_ERR_INVALID_VALUE = 1,
     GEMM_ERR_NOT_SUPPORTED = 2,
     GEMM_ERR_HIP = 3,
-    GEMM_ERR_ALLOC = 4
+    GEMM_ERR_ALLOC = 4,
+    GEMM_ERR_STREAM_K = 5
 } gemm_status_t;
 
 /* Create a handle (*out receives it).  Makes no HIP call. */
@@ -235,8 +238,10 @@ size_t gemm_stream_k_workspace_bytes(void);
  * aligned, used by h's stream-K calls until replaced or cleared (ws == NULL or
  * bytes == 0).  Enqueues one small kernel on `stream` that clears the
  * workspace's flag area; the calls that use it must be ordered after that
- * kernel.  Layout: 4096 32-bit flags, then one BM*BN fp32 partial-sum slot
- * per workgroup.  Each stream-K call leaves every flag zero again.  Calls that
+ * kernel.  Layout: 4096 32-bit flags, one 32-bit sticky error word (then
+ * padding to byte 16640), then one BM*BN fp32 partial-sum slot per
+ * workgroup.  Each stream-K call leaves every flag zero again unless a
+ * finisher's bounded wait gave up (gemm_stream_k_status).  Calls that
  * share a workspace must not overlap in time (use one handle and workspace
  * per concurrently used stream).  GEMM_ERR_INVALID_VALUE: NULL handle, a
  * misaligned pointer or fewer bytes than the flag area; GEMM_ERR_HIP: the
@@ -251,6 +256,28 @@ gemm_status_t gemm_set_stream_k(gemm_handle_t h, int mode);
 /* Stream-K workgroups used by the last gemm_run on h (0: data-parallel tiles;
  * -1 for a NULL handle). */
 int gemm_last_stream_k(gemm_handle_t h);
+
+/* Failure report of h's stream-K calls.  A finisher waits for each
+ * contributor's flag a bounded number of polls (about 100 ns each).  Every
+ * contributor of a stream-K grid is resident at the same time as its
+ * finisher, so the bound is never reached in a correct run; if it is, the
+ * finisher adds no partial sum and clears no flag, writes NaN in place of its
+ * tile (where the fused epilogue's activation or clamp does not map NaN to a
+ * number) and sets the workspace's sticky error word.  This call waits for
+ * `stream`, reads that word and, when it is set, clears the whole flag area
+ * and the word on `stream` (waiting again) and returns GEMM_ERR_STREAM_K: the
+ * results of the stream-K calls since the last check are not to be trusted.
+ * GEMM_OK when the word is clear or h has no workspace; GEMM_ERR_HIP when the
+ * copy or the clearing kernel fails; GEMM_ERR_INVALID_VALUE for a NULL
+ * handle.  Synchronizing: not for use inside graph capture. */
+gemm_status_t gemm_stream_k_status(gemm_handle_t h, hipStream_t stream);
+
+/* Bound on a stream-K finisher's wait, in polls per contributor, for h's later
+ * calls: -1 restores the default (2^20); 0 makes every finisher that has
+ * contributors give up at once, which lets a test exercise the failure report
+ * with every kernel ending normally.  GEMM_ERR_INVALID_VALUE for a NULL handle
+ * or a value below -1. */
+gemm_status_t gemm_set_stream_k_poll_limit(gemm_handle_t h, int polls);
 
 #ifdef __cplusplus
 }

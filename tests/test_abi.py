@@ -39,6 +39,7 @@ def test_status_strings():
     assert g.gemm_status_string(g.GEMM_ERR_NOT_SUPPORTED) == "GEMM_ERR_NOT_SUPPORTED"
     assert g.gemm_status_string(g.GEMM_ERR_HIP) == "GEMM_ERR_HIP"
     assert g.gemm_status_string(g.GEMM_ERR_ALLOC) == "GEMM_ERR_ALLOC"
+    assert g.gemm_status_string(g.GEMM_ERR_STREAM_K) == "GEMM_ERR_STREAM_K"
     assert g.gemm_status_string(77) == "unknown status"
 
 
@@ -159,13 +160,22 @@ def test_stream_k_controls_validate_arguments(h):
     assert g.gemm_set_workspace(h, FAKE, 64, None) == g.GEMM_ERR_INVALID_VALUE
     # clearing the workspace makes no HIP call either
     assert g.gemm_set_workspace(h, None, 0, None) == g.GEMM_OK
+    # the poll bound: -1 (default) and any count >= 0; the status query of a
+    # handle without a workspace makes no HIP call
+    for polls in (-1, 0, 1, 1 << 20):
+        assert g.gemm_set_stream_k_poll_limit(h, polls) == g.GEMM_OK
+    assert g.gemm_set_stream_k_poll_limit(h, -2) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_set_stream_k_poll_limit(None, 0) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_stream_k_status(None, None) == g.GEMM_ERR_INVALID_VALUE
+    assert g.gemm_stream_k_status(h, None) == g.GEMM_OK
 
 
 def test_stream_k_workspace_size_covers_the_flag_area_and_one_slot_per_workgroup():
     n = g.gemm_stream_k_workspace_bytes()
-    # 4096 flags, then at least one 256x256 fp32 slot per compute unit
-    assert n >= 4096 * 4 + 256 * 256 * 4
-    assert (n - 4096 * 4) % (128 * 128 * 4) == 0
+    # 4096 flags and the error word (16640 bytes with padding), then at least
+    # one 256x256 fp32 slot per compute unit
+    assert n >= 16640 + 256 * 256 * 4
+    assert (n - 16640) % (128 * 128 * 4) == 0
 
 
 def test_bf16_output_dtype_validates_with_2_byte_elements(h):
@@ -259,3 +269,34 @@ def test_traffic_record_names_the_step_kernels():
         key = bench.kernel_name_key(name, tile)
         hits = [k for k in rec["kernels"] if key + ">" in k or key + ", " in k]
         assert len(hits) == 1, (name, key, list(rec["kernels"]))
+
+
+def test_selection_queries_from_many_threads_agree():
+    """The host caches (compute units, occupancy) are filled lazily; entry
+    points may be called from several threads at once (ctypes releases the
+    GIL), and every thread must see the same answers."""
+    import threading
+    shapes = [(dt, ta, tb, M, N, K) for dt in (0, 1, 2) for ta in (0, 1) for tb in (0, 1)
+              for (M, N, K) in ((256, 256, 256), (4093, 2051, 1537), (8192, 8192, 8192),
+                                (1024, 1024, 32768), (3000, 3000, 512))]
+    want = [g.gemm_select_variant(*s) for s in shapes]
+    occ_want = [g.gemm_variant_occupancy(i) for i in range(g.gemm_variant_count())]
+    errors = []
+
+    def worker(seed):
+        order = list(range(len(shapes)))
+        order = order[seed % len(order):] + order[:seed % len(order)]
+        for _ in range(20):
+            for i in order:
+                if g.gemm_select_variant(*shapes[i]) != want[i]:
+                    errors.append(("select", shapes[i]))
+            for v in range(g.gemm_variant_count()):
+                if g.gemm_variant_occupancy(v) != occ_want[v]:
+                    errors.append(("occupancy", v))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]

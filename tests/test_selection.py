@@ -64,4 +64,11 @@ def test_automatic_choice(g_handle, case):
     assert s == g.GEMM_OK, g.gemm_status_string(s)
     assert g.gemm_variant_name(g.gemm_last_variant(h)) == expected
     assert (g.gemm_last_stream_k(h) > 0) == stream_k
+    if not stream_k:
+        # the query (no workspace, packed operands) agrees with the call
+        dt = g.GEMM_DTYPE_F32 if dtype == "f32" else (
+            g.GEMM_DTYPE_BF16_BF16 if bf16_out else g.GEMM_DTYPE_BF16_F32)
+        q = g.gemm_select_variant(dt, g.GEMM_OP_N if ta == "N" else g.GEMM_OP_T,
+                                  g.GEMM_OP_N if tb == "N" else g.GEMM_OP_T, M, N, K)
+        assert q == g.gemm_last_variant(h)
     assert torch.count_nonzero(D).item() == 0
