@@ -34,6 +34,8 @@ GEMM_ERR_NOT_SUPPORTED = 2
 GEMM_ERR_HIP = 3
 GEMM_ERR_ALLOC = 4
 GEMM_ERR_STREAM_K = 5
+# bytes of the static stream-K array gemm_run_no_alloc uses on each GPU
+GEMM_NO_ALLOC_SCRATCH_BYTES = 16640 + (16 << 20)
 GEMM_ACT_NONE = 0
 GEMM_ACT_RELU = 1
 GEMM_ACT_GELU = 2
@@ -45,7 +47,7 @@ EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
            "gemm_select_variant", "gemm_stream_k_workspace_bytes", "gemm_set_workspace",
            "gemm_set_stream_k", "gemm_last_stream_k", "gemm_run_epilogue",
            "gemm_variant_pipeline", "gemm_variant_occupancy", "gemm_stream_k_status",
-           "gemm_set_stream_k_poll_limit")
+           "gemm_set_stream_k_poll_limit", "gemm_run_no_alloc")
 
 
 class GemmEpilogue(ctypes.Structure):
@@ -94,6 +96,9 @@ def _load():
     lib.gemm_run.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                              vp, i64, i32, vp]
     lib.gemm_run.restype = i32
+    lib.gemm_run_no_alloc.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32,
+                                      vp, i64, vp, i64, i32, vp]
+    lib.gemm_run_no_alloc.restype = i32
     lib.gemm_run_epilogue.argtypes = [vp, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32,
                                       vp, i64, vp, i64, i32, ctypes.POINTER(GemmEpilogue), vp]
     lib.gemm_run_epilogue.restype = i32
@@ -153,6 +158,13 @@ def gemm_run(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D,
     """Raw call: pointers and the stream are integers (0/None for NULL)."""
     return lib.gemm_run(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                         D, ldd, dtype, stream)
+
+
+def gemm_run_no_alloc(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D,
+                      ldd, dtype, stream) -> int:
+    """Raw call: pointers and the stream are integers (0/None for NULL)."""
+    return lib.gemm_run_no_alloc(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                 ldc, D, ldd, dtype, stream)
 
 
 def gemm_run_epilogue(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd,
@@ -263,7 +275,7 @@ def variants():
 
 def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
                 stream=None, check=True, bias=None, activation=GEMM_ACT_NONE,
-                clamp=None) -> int:
+                clamp=None, no_alloc=False) -> int:
     """gemm_run on torch tensors (row-major 2-D views with unit column stride).
 
     A: op(A) is M x K (A stored M x K for "N", K x M for "T"); B likewise;
@@ -302,7 +314,12 @@ def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
             A.data_ptr(), ld(A), B.data_ptr(), ld(B), float(beta),
             None if C is None else C.data_ptr(), ld(C) if C is not None else N,
             D.data_ptr(), ld(D), dtype)
-    if bias is None and activation == GEMM_ACT_NONE and clamp is None:
+    plain = bias is None and activation == GEMM_ACT_NONE and clamp is None
+    if no_alloc:
+        if not plain:
+            raise ValueError("gemm_run_no_alloc has no fused epilogue")
+        s = gemm_run_no_alloc(*args, stream)
+    elif plain:
         s = gemm_run(*args, stream)
     else:
         lo, hi = (0.0, 0.0) if clamp is None else clamp

@@ -5,6 +5,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -49,6 +50,13 @@ __global__ __launch_bounds__(256) void clear_flags_kernel(unsigned* flags, int n
     for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) flags[i] = 0u;
 }
 
+// Stream-K workspace of gemm_run_no_alloc, one copy per GPU for the life of
+// the process: the flag area (flags and error word), then partial-sum slots.
+// Host code never passes this name to a kernel or a copy: it stands for a
+// host-side shadow there.  The device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+static __device__ __align__(256) char scratch[GEMM_NO_ALLOC_SCRATCH_BYTES];
+
 namespace {
 
 // Stream-K workspace layout: SK_MAX_WG flags, the sticky error word (padded
@@ -59,6 +67,9 @@ constexpr size_t SK_FLAG_BYTES = SK_FLAG_WORDS * sizeof(unsigned);
 // Default bound on a finisher's wait, in polls of about 100 ns per
 // contributor: far beyond any wait a resident contributor needs.
 constexpr int SK_SPIN_DEFAULT = 1 << 20;
+static_assert(GEMM_NO_ALLOC_SCRATCH_BYTES > SK_FLAG_BYTES &&
+                  GEMM_NO_ALLOC_SCRATCH_BYTES % 256 == 0,
+              "no-alloc scratch holds the flag area and whole slots");
 
 const std::vector<Variant>& table()
 {
@@ -300,6 +311,57 @@ bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes
     return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
+// Device address of each device's copy of `scratch` (null until set up).
+std::atomic<void*> scratch_addr[MAX_DEVICES];
+
+// The current device's copy of `scratch`: its address is looked up, and its
+// flag area (flags and error word) cleared by a kernel on `stream`, on the
+// first call on each device.  Null if the lookup or the clearing launch
+// fails.
+void* scratch_address(hipStream_t stream)
+{
+    static std::mutex init;
+    const int dev = current_device();
+    if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(init);
+    p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* dp = nullptr;
+    if (hipGetSymbolAddress(&dp, HIP_SYMBOL(scratch)) != hipSuccess || !dp) return nullptr;
+    unsigned* flags = static_cast<unsigned*>(dp);
+    int n = SK_FLAG_WORDS;
+    void* kargs[] = {&flags, &n};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_flags_kernel), dim3(16), dim3(256),
+                        kargs, 0, stream) != hipSuccess)
+        return nullptr;
+    scratch_addr[dev].store(dp, std::memory_order_release);
+    return dp;
+}
+
+// Read a stream-K workspace's error word after `stream` drains; when it is
+// set, clear the flag area on `stream` and report GEMM_ERR_STREAM_K.
+gemm_status_t check_and_clear(void* ws, hipStream_t stream)
+{
+    unsigned err = 0;
+    const unsigned* word = static_cast<const unsigned*>(ws) + SK_MAX_WG;
+    if (hipMemcpyAsync(&err, word, sizeof(err), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    if (err == 0) return GEMM_OK;
+    // a finisher gave up: contributors it did not wait for may have raised
+    // their flags after it; clear every flag and the error word
+    unsigned* flags = static_cast<unsigned*>(ws);
+    int n = SK_FLAG_WORDS;
+    void* kargs[] = {&flags, &n};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_flags_kernel), dim3(16), dim3(256),
+                        kargs, 0, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    return GEMM_ERR_STREAM_K;
+}
+
 // What a call looks like to the kernel choice.
 struct CallDesc {
     int dtype;          // gemm_dtype_t
@@ -528,23 +590,17 @@ gemm_status_t gemm_stream_k_status(gemm_handle_t h, hipStream_t stream)
 {
     using namespace dg;
     if (!h) return GEMM_ERR_INVALID_VALUE;
-    if (!h->ws) return GEMM_OK;
-    unsigned err = 0;
-    const unsigned* word = static_cast<const unsigned*>(h->ws) + SK_MAX_WG;
-    if (hipMemcpyAsync(&err, word, sizeof(err), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return GEMM_ERR_HIP;
-    if (err == 0) return GEMM_OK;
-    // a finisher gave up: contributors it did not wait for may have raised
-    // their flags after it; clear every flag and the error word
-    unsigned* flags = static_cast<unsigned*>(h->ws);
-    int n = SK_FLAG_WORDS;
-    void* kargs[] = {&flags, &n};
-    if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_flags_kernel), dim3(16), dim3(256),
-                        kargs, 0, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return GEMM_ERR_HIP;
-    return GEMM_ERR_STREAM_K;
+    gemm_status_t st = GEMM_OK;
+    if (h->ws) st = check_and_clear(h->ws, stream);
+    // the current device's gemm_run_no_alloc scratch, once it is set up
+    const int dev = current_device();
+    void* sp = dev >= 0 && dev < MAX_DEVICES ? scratch_addr[dev].load(std::memory_order_acquire)
+                                             : nullptr;
+    if (sp && st != GEMM_ERR_HIP) {
+        const gemm_status_t s2 = check_and_clear(sp, stream);
+        if (s2 != GEMM_OK) st = s2;
+    }
+    return st;
 }
 
 size_t gemm_stream_k_workspace_bytes(void)
@@ -618,7 +674,7 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
                               int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
                               const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
                               void* D, int64_t ldd, gemm_dtype_t dtype, const gemm_epilogue_t* ep,
-                              hipStream_t stream)
+                              void* ws, size_t ws_bytes, hipStream_t stream)
 {
     using namespace dg;
     if (!h) return GEMM_ERR_INVALID_VALUE;
@@ -720,7 +776,7 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     cd.wide = aligned_to(A, es) && aligned_to(B, es);
     cd.forced = h->forced_variant;
     cd.sk_mode = h->stream_k_mode;
-    cd.ws_bytes = h->ws_bytes;
+    cd.ws_bytes = ws ? ws_bytes : 0;
     Plan pl;
     const gemm_status_t ps = plan_call(cd, pl);
     if (ps != GEMM_OK) return ps;
@@ -737,9 +793,12 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     hipError_t e;
     const EpiFns* ef = pl.ef;
     if (sk > 0) {
-        a.sk_flags = static_cast<unsigned*>(h->ws);
+        // the plan only takes grids whose slots fit in the workspace
+        const size_t need = SK_FLAG_BYTES + (size_t)sk * vr.bm * vr.bn * sizeof(float);
+        if (need > cd.ws_bytes) return GEMM_ERR_NOT_SUPPORTED;
+        a.sk_flags = static_cast<unsigned*>(ws);
         a.sk_error = a.sk_flags + SK_MAX_WG;
-        a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(h->ws) + SK_FLAG_BYTES);
+        a.sk_partials = reinterpret_cast<float*>(static_cast<char*>(ws) + SK_FLAG_BYTES);
         e = pl.sk_fn[a_kc][b_kc](a, sk, stream);
     } else if (nn_t) {
         GemmArgs t = a;
@@ -769,8 +828,28 @@ gemm_status_t gemm_run(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int6
                        float beta, const void* C, int64_t ldc, void* D, int64_t ldd,
                        gemm_dtype_t dtype, hipStream_t stream)
 {
+    if (!h) return GEMM_ERR_INVALID_VALUE;
     return run_gemm(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, dtype,
-                    nullptr, stream);
+                    nullptr, h->ws, h->ws_bytes, stream);
+}
+
+gemm_status_t gemm_run_no_alloc(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M,
+                                int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, float beta, const void* C,
+                                int64_t ldc, void* D, int64_t ldd, gemm_dtype_t dtype,
+                                hipStream_t stream)
+{
+    using namespace dg;
+    if (!h) return GEMM_ERR_INVALID_VALUE;
+    // set up (first call on this device) only once the arguments look like a
+    // call that launches something; run_gemm validates them all again
+    void* ws = nullptr;
+    if (M > 0 && N > 0 && D) {
+        ws = scratch_address(stream);
+        if (!ws) return GEMM_ERR_HIP;
+    }
+    return run_gemm(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, dtype,
+                    nullptr, ws, GEMM_NO_ALLOC_SCRATCH_BYTES, stream);
 }
 
 gemm_status_t gemm_run_epilogue(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB, int64_t M,
@@ -779,8 +858,9 @@ gemm_status_t gemm_run_epilogue(gemm_handle_t h, gemm_op_t transA, gemm_op_t tra
                                 int64_t ldc, void* D, int64_t ldd, gemm_dtype_t dtype,
                                 const gemm_epilogue_t* epilogue, hipStream_t stream)
 {
+    if (!h) return GEMM_ERR_INVALID_VALUE;
     return run_gemm(h, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, D, ldd, dtype,
-                    epilogue, stream);
+                    epilogue, h->ws, h->ws_bytes, stream);
 }
 
 }  // extern "C"

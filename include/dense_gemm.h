@@ -267,10 +267,41 @@ int gemm_last_stream_k(gemm_handle_t h);
  * `stream`, reads that word and, when it is set, clears the whole flag area
  * and the word on `stream` (waiting again) and returns GEMM_ERR_STREAM_K: the
  * results of the stream-K calls since the last check are not to be trusted.
+ * The same is done for the current device's gemm_run_no_alloc array once a
+ * call has set it up.
  * GEMM_OK when the word is clear or h has no workspace; GEMM_ERR_HIP when the
  * copy or the clearing kernel fails; GEMM_ERR_INVALID_VALUE for a NULL
  * handle.  Synchronizing: not for use inside graph capture. */
 gemm_status_t gemm_stream_k_status(gemm_handle_t h, hipStream_t stream);
+
+/* ---- a gemm_run that allocates nothing ----------------------------------
+ * For callers that cannot allocate device memory at call time (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * gemm_run_no_alloc takes gemm_run's arguments and computes the same result
+ * with the same kernel choice, except that its stream-K workspace is the
+ * library's own: a static device array of GEMM_NO_ALLOC_SCRATCH_BYTES per GPU
+ * (the 16640-byte flag area, then 16 MiB of partial-sum slots: 64 slots of
+ * 256x256 fp32 or 256 of 128x128), which each GPU the library runs on holds
+ * until the process ends.  The handle's own workspace, if any, is not used.
+ * The automatic choice only takes stream-K grids whose slots fit in it, as it
+ * does for a caller's workspace of that size; should a plan need more, the
+ * call returns GEMM_ERR_NOT_SUPPORTED before enqueuing anything.  It makes no
+ * hipMalloc, hipFree or other allocating call.  The first call on a device
+ * looks up that device's copy (hipGetSymbolAddress) and enqueues one small
+ * kernel on `stream` that clears its flag area; later stream-K calls leave the
+ * flags zero again.  Every call on a GPU shares that GPU's copy: calls that
+ * may overlap in time on one GPU (several streams, several threads) race and
+ * must be serialized by the caller.  gemm_stream_k_status reports and clears
+ * a failed wait in the current device's copy as well.  Errors as for
+ * gemm_run, plus GEMM_ERR_HIP when the first call on a device cannot set the
+ * array up. */
+#define GEMM_NO_ALLOC_SCRATCH_BYTES ((size_t)16640 + ((size_t)16 << 20))
+
+gemm_status_t gemm_run_no_alloc(gemm_handle_t h, gemm_op_t transA, gemm_op_t transB,
+                                int64_t M, int64_t N, int64_t K, float alpha,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                float beta, const void* C, int64_t ldc,
+                                void* D, int64_t ldd, gemm_dtype_t dtype, hipStream_t stream);
 
 /* Bound on a stream-K finisher's wait, in polls per contributor, for h's later
  * calls: -1 restores the default (2^20); 0 makes every finisher that has
