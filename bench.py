@@ -65,8 +65,8 @@ def compulsory_bytes(w: workloads.Workload, out_bytes: int = 4) -> int:
 
 # the sources that define the step's kernels (the direct-to-LDS template and
 # the instantiation files of the selected variants)
-STEP_KERNEL_SOURCES = ("common.hpp", "mfma_dma_gemm.hpp", "variants.hpp", "inst_bf16_dma.hip",
-                       "inst_f32_dma.hip")
+STEP_KERNEL_SOURCES = ("common.hpp", "mfma_dma_gemm.hpp", "sk_ranges.hpp", "variants.hpp",
+                       "selected_configs.hpp", "inst_bf16_dma.hip", "inst_f32_dma.hip")
 
 
 def kernel_source_digest() -> str:
@@ -96,7 +96,8 @@ def kernel_name_key(variant_name: str, tile) -> str:
         if f"_dma{tag[4:]}_" in variant_name:
             late = "_late" in variant_name
             stages = re.search(r"_s(\d+)(?:_|$)", variant_name).group(1)
-            return (f"DmaConfig<{kind}, {bm}, {bn}, {bk}, 2, 2, {stages}, "
+            wm, wn = re.search(r"_w(\d+)x(\d+)_", variant_name).groups()
+            return (f"DmaConfig<{kind}, {bm}, {bn}, {bk}, {wm}, {wn}, {stages}, "
                     f"{'true' if late else 'false'}")
     return f"FmaConfig<{bm}, {bn}, {bk}>"
 
@@ -314,26 +315,37 @@ def amd_smi_sample():
             "mem_clock_mhz": mem[0] if mem else None}
 
 
-def telemetry_under_load(part, stream_handle, seconds: float = 1.5):
-    """Clocks and power while part's kernel runs back to back: one amd-smi
-    sample taken half way through ~`seconds` of launches, and one just
-    before (the bf16 matrix cores are power limited, so the clock under load
-    belongs with the timing)."""
+def telemetry_under_load(part, stream_handle, lead: float = 0.3):
+    """Clocks and power while part's kernel runs back to back (the bf16 matrix
+    cores are power limited, so the clock under load belongs with the
+    timing): one amd-smi sample taken idle, then one started `lead` seconds
+    into a run of launches that goes on until that sample has been read
+    (amd-smi takes a second or more), so the GPU is busy throughout it."""
     import threading
-    result = {}
-    th = threading.Thread(target=lambda: (time.sleep(seconds / 2),
-                                          result.update(sample=amd_smi_sample())))
     before = amd_smi_sample()
     if before is None:
         return None
-    th.start()
+    result = {}
+
+    def sample():
+        time.sleep(lead)
+        t = time.perf_counter()
+        result["sample"] = amd_smi_sample()
+        result["sample_s"] = round(time.perf_counter() - t, 2)
+
+    th = threading.Thread(target=sample)
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(8):
+    th.start()
+    launches = 0
+    while th.is_alive():
+        for _ in range(4):
             part.launch(stream_handle)
+        launches += 4
         torch.cuda.synchronize()
     th.join()
-    return {"workload": part.name, "before": before, "under_load": result.get("sample")}
+    return {"workload": part.name, "before": before, "under_load": result.get("sample"),
+            "sample_seconds": result.get("sample_s"), "launches_during_sample": launches,
+            "load_seconds": round(time.perf_counter() - t0, 2)}
 
 
 def oracle_sample_rate(part: Part, cores: int, budget_s: float):
@@ -591,6 +603,9 @@ def main(argv=None):
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of "
                          "a --copy-probe run into the HBM-traffic record, then exit")
+    ap.add_argument("--vector-fma-only", action="store_true",
+                    help="time only the fp32 vector-FMA kernel at 4096^3 (for counter runs), "
+                         "print one JSON object, then exit")
     ap.add_argument("--pipeline-sweep", action="store_true",
                     help="time every direct-to-LDS variant on the NN step shapes, fit the "
                          "pipeline-depth model, print one JSON object, then exit")
@@ -616,6 +631,11 @@ def main(argv=None):
     h = g.gemm_create()
     if args.pipeline_sweep:
         print(json.dumps(pipeline_sweep(g, h)), flush=True)
+        g.gemm_destroy(h)
+        return 0
+    if args.vector_fma_only:
+        print(json.dumps(time_extra(g, h, "fp32_4096", VECTOR_FMA_VARIANT, reps=args.steps,
+                                    warmup=args.warmup)), flush=True)
         g.gemm_destroy(h)
         return 0
     # a stream-K workspace (the automatic policy keeps the two step workloads
@@ -736,6 +756,16 @@ def main(argv=None):
         finally:
             g.gemm_set_stream_k(h, -1)
         extras["bf16_small_mn_long_k"]["whole_tiles_kernel_ms"] = whole["kernel_ms"]
+        # the MFMA instruction shape on the same kernel template, tile (128x128),
+        # depth (64-deep steps, 2 stages) and problem
+        extras["mfma_instruction_shape"] = {
+            "workload": workloads.WORKLOADS["bf16_4096_tn"].description,
+            "v_mfma_f32_32x32x16_bf16": time_extra(
+                g, h, "bf16_4096_tn", "bf16_dma32x32x16_128x128x64_w2x2_s2_late", reps=10,
+                warmup=3),
+            "v_mfma_f32_16x16x32_bf16": time_extra(
+                g, h, "bf16_4096_tn", "bf16_dma16x16x32_128x128x64_w2x2_s2_late", reps=10,
+                warmup=3)}
 
     cpu = None
     if not args.no_cpu_baseline:

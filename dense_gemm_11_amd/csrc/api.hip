@@ -78,7 +78,7 @@ const std::vector<Variant>& table()
         for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
                          bf16dma_variant_table, f32dma_variant_table,
                          bf16dma_sweep_variant_table, f32dma_sweep_variant_table,
-                         bf16dma_tile_variant_table}) {
+                         bf16dma_tile_variant_table, small_variant_table}) {
             int n = 0;
             const Variant* t = get(&n);
             v.insert(v.end(), t, t + n);
@@ -149,7 +149,7 @@ int dma_variant(int dtype, bool big)
         {find_variant("f32_dma32x32x2_128x128x16_w2x2_s3_late"),
          find_variant("f32_dma32x32x2_256x256x32_w2x2_s2_late")},
         {find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late"),
-         find_variant("bf16_dma32x32x16_256x256x32_w2x2_s3_late")}};
+         find_variant("bf16_dma32x32x16_256x256x32_w2x4_s3_late")}};
     return ids[dtype == GEMM_DTYPE_BF16_F32][big];
 }
 
@@ -369,6 +369,7 @@ struct CallDesc {
     int64_t M, N, K, lda, ldb;
     bool epi;           // a fused epilogue with something to do
     bool wide;          // A and B element-aligned (16-byte accesses allowed)
+    bool rows16;        // every row of A and B starts 16-byte aligned
     int forced;         // forced variant, or -1
     int sk_mode;        // stream-K policy (-1 automatic, 0 never, 1 when allowed)
     size_t ws_bytes;    // stream-K workspace bytes (0: none)
@@ -413,6 +414,22 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     const int64_t es = op_dtype == GEMM_DTYPE_F32 ? 4 : 2;
     const int64_t M = c.M, N = c.N, K = c.K;
     int id = c.forced;
+    // Small problems: where 128x128 tiles would occupy at most a sixteenth of
+    // the compute units (256^3: 4 tiles), one 16x16 block per workgroup
+    // spreads the output over them (fp32 256^3 measured 19.5 us on four
+    // 128x128 tiles).  Not when stream-K is forced, nor for bf16 output or a
+    // fused epilogue, which the small kernel does not carry.
+    if (id < 0 && !c.epi && !out_bf16 && c.sk_mode != 1 && K <= 4096 &&
+        16 * ceil_div(M, 128) * ceil_div(N, 128) <= (int64_t)device_cus()) {
+        static const int small[2] = {find_variant("f32_small16x16x16_w4"),
+                                     find_variant("bf16_small16x16x32_w4")};
+        if (small[op_dtype] >= 0) {
+            pl.id = small[op_dtype];
+            pl.sk = 0;
+            pl.aligned = c.wide;
+            return GEMM_OK;
+        }
+    }
     if (id < 0) {
         const Variant& big = table()[select_variant(op_dtype, M, N, K, true)];
         id = select_variant(op_dtype, M, N, K,
@@ -445,6 +462,41 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                 id = other;
                 sk = sk_o;
             }
+        }
+    }
+    // bf16 operands, fp32 output, whole tiles: tile shapes beyond the two
+    // square ones, from measurements on MI355X (us, one box, automatic
+    // choice before -> after):
+    //  * K <= 1024 with at least a full wave of 256x256 tiles: 128x256 tiles,
+    //    two workgroups per compute unit, so one's prologue and epilogue hide
+    //    behind the other's matrix work (8192x4096x512 56.8 -> 46.2,
+    //    16384x4096x512 119 -> 95, 8192^2 x 512 111 -> 87).
+    //  * Fewer 256x256 tiles than three quarters of a wave, K >= 2048, and
+    //    128x256 tiles that fill between three quarters of a wave and one
+    //    per compute unit: 128x256 (4096x2048x4096 66.9 -> 62.6, 2560^2 x
+    //    4096 57.7 -> 55.5).
+    //  * Otherwise, at least half a wave of 256x256 tiles and a long K, or
+    //    rows that are not 16-byte aligned (every 16-byte copy then
+    //    straddles two units, and two waves per SIMD hide that latency): the
+    //    8-wave 256x256 kernel (3072^3 76.5 -> 58.6; 4093x2051x1537 A^T B
+    //    58.5 -> 50.1).
+    if (sk == 0 && c.forced < 0 && aligned && !c.epi && !out_bf16 &&
+        op_dtype == GEMM_DTYPE_BF16_F32) {
+        static const int wide_tile = find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late");
+        const int64_t cus = device_cus();
+        const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+        const int64_t t12 = ceil_div(M, 128) * ceil_div(N, 256);
+        const int big_id = dma_variant(GEMM_DTYPE_BF16_F32, true);
+        if (wide_tile >= 0 && K <= 1024 && t256 >= cus &&
+            dma_offsets_fit(table()[wide_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
+            id = wide_tile;
+        } else if (4 * t256 < 3 * cus) {
+            if (wide_tile >= 0 && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus &&
+                dma_offsets_fit(table()[wide_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
+                id = wide_tile;
+            else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) &&
+                     dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
+                id = big_id;
         }
     }
     // bf16 128x128 whole tiles: the 2-stage ring fits 3 workgroups on a
@@ -663,6 +715,8 @@ int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB, 
     cd.ldb = std::max<int64_t>(1, cd.b_kc ? K : N);
     cd.epi = false;
     cd.wide = true;
+    cd.rows16 = (cd.lda * (dtype == GEMM_DTYPE_F32 ? 4 : 2)) % 16 == 0 &&
+                (cd.ldb * (dtype == GEMM_DTYPE_F32 ? 4 : 2)) % 16 == 0;
     cd.forced = -1;
     cd.sk_mode = -1;
     cd.ws_bytes = 0;
@@ -774,6 +828,8 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     // wide (16-byte) operand access needs element-aligned A and B only
     const int64_t es = dtype == GEMM_DTYPE_F32 ? 4 : 2;
     cd.wide = aligned_to(A, es) && aligned_to(B, es);
+    cd.rows16 = aligned_to(A, 16) && aligned_to(B, 16) && (lda * es) % 16 == 0 &&
+                (ldb * es) % 16 == 0;
     cd.forced = h->forced_variant;
     cd.sk_mode = h->stream_k_mode;
     cd.ws_bytes = ws ? ws_bytes : 0;

@@ -2,12 +2,13 @@
 // the ones the selector uses, each with a stream-K instantiation and a
 // transposed-output instantiation for NN problems.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
-using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
+using Dma256s3L = SelBf16Big;
+using Dma128s4L = SelBf16Mid;
 
 #define bf16_out_table(BM)                                                                   \
     {{{bf16_out_fns(BM).fn[0][0][0], bf16_out_fns(BM).fn[0][0][1]},                         \
@@ -25,7 +26,7 @@ using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
 const Variant* bf16dma_variant_table(int* count)
 {
     static const Variant table[] = {
-        BF16_DMA_SK_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3_late", Dma256s3L),
+        BF16_DMA_SK_VARIANT("bf16_dma32x32x16_256x256x32_w2x4_s3_late", Dma256s3L),
         BF16_DMA_SK_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late", Dma128s4L),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));

@@ -1,12 +1,13 @@
 // bf16-output (GEMM_DTYPE_BF16_BF16) instantiations of the selected bf16
 // direct-to-LDS variants: C and D bfloat16, fp32 accumulation.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using Dma256s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
-using Dma128s4L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
+using Dma256s3L = SelBf16Big;
+using Dma128s4L = SelBf16Mid;
 
 const Bf16OutFns& bf16_out_fns(int bm)
 {

@@ -1,6 +1,7 @@
 // bf16 direct-to-LDS variants kept for measurement: the pipeline-depth and
-// barrier-placement sweep.  256x256 tiles: half-way barrier with 3 or 4
-// stages, late barrier with 4 stages, 2 stages of 64-deep steps.  128x128
+// barrier-placement sweep.  256x256 tiles with 4 waves: half-way barrier with
+// 3 or 4 stages, late barrier with 3 (pair buffers when both operands are
+// k-contiguous) or 4 stages, 2 stages of 64-deep steps.  128x128
 // tiles: late barrier with 2, 3 or 5 stages of 32-deep steps, and 2 or 3 stages
 // of 64-deep steps, where the third stage (96 KiB of LDS) leaves room for one
 // workgroup per compute unit instead of two.  Paired variants: the
@@ -15,6 +16,7 @@
 namespace dg {
 
 using Dma256s4 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4>;
+using Dma256s3LP = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
 using Dma256s3 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3>;
 using Dma256s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 4, true>;
 using Dma256k64s2L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 2, 2, true>;
@@ -39,6 +41,7 @@ const Variant* bf16dma_sweep_variant_table(int* count)
 {
     static const Variant table[] = {
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4", Dma256s4),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3_late", Dma256s3LP),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3", Dma256s3),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late", Dma256s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x2_s2_late", Dma256k64s2L),

@@ -1,12 +1,13 @@
 // Fused-epilogue (bias, activation, clamp) instantiations of the selected
 // fp32 direct-to-LDS variants: fp32 A, B, C, D.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using F32Dma256k32s2L = DmaConfig<MFMA_F32_32x32x2, 256, 256, 32, 2, 2, 2, true>;
-using F32Dma128s3L = DmaConfig<MFMA_F32_32x32x2, 128, 128, 16, 2, 2, 3, true>;
+using F32Dma256k32s2L = SelF32Big;
+using F32Dma128s3L = SelF32Mid;
 
 const EpiFns* epi_fns_f32(int bm)
 {

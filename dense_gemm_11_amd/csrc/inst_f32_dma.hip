@@ -1,12 +1,13 @@
 // fp32 matrix-core variants with direct-to-LDS loads and an S-stage LDS ring:
 // the ones the selector uses, each with a stream-K instantiation.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using F32Dma256k32s2L = DmaConfig<MFMA_F32_32x32x2, 256, 256, 32, 2, 2, 2, true>;
-using F32Dma128s3L = DmaConfig<MFMA_F32_32x32x2, 128, 128, 16, 2, 2, 3, true>;
+using F32Dma256k32s2L = SelF32Big;
+using F32Dma128s3L = SelF32Mid;
 
 #define F32_DMA_SK_VARIANT(NAME, CFG)                                                       \
     {NAME, 0, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES,       \

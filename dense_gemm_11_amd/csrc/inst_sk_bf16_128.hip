@@ -2,11 +2,12 @@
 // 128x128 tiles for bf16 output and for the fused epilogue (fp32 or bf16
 // output); the partial sums handed between workgroups stay fp32.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using SkCfg128 = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true>;
+using SkCfg128 = SelBf16Mid;
 
 const SkFns* sk_fns_bf16_128(int kind)
 {

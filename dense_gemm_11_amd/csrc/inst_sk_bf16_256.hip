@@ -2,11 +2,12 @@
 // 256x256 tiles for bf16 output and for the fused epilogue (fp32 or bf16
 // output); the partial sums handed between workgroups stay fp32.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using SkCfg256 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 2, 3, true, PAIR_BOTH_KC>;
+using SkCfg256 = SelBf16Big;
 
 const SkFns* sk_fns_bf16_256(int kind)
 {

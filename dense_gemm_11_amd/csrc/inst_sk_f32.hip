@@ -1,12 +1,13 @@
 // Stream-K instantiations of the selected fp32 direct-to-LDS variants for the
 // fused epilogue.
 #include "mfma_dma_gemm.hpp"
+#include "selected_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using SkF32Cfg256 = DmaConfig<MFMA_F32_32x32x2, 256, 256, 32, 2, 2, 2, true>;
-using SkF32Cfg128 = DmaConfig<MFMA_F32_32x32x2, 128, 128, 16, 2, 2, 3, true>;
+using SkF32Cfg256 = SelF32Big;
+using SkF32Cfg128 = SelF32Mid;
 
 const SkFns* sk_fns_f32(int bm)
 {

@@ -135,7 +135,7 @@ struct DmaConfig {
 // per 16 lanes, 2 adjacent chunks (32 bytes): with these masks the 4 rows'
 // chunk pairs fill a 128-byte bank window exactly, and the two 16-lane groups
 // of a 32-lane half (chunks 2 apart) fill a 256-byte window exactly.
-__device__ __forceinline__ int mn_swz(int k) { return (0x0E0A0400 >> (8 * (k & 3))) & 0xFF; }
+__host__ __device__ constexpr int mn_swz(int k) { return (0x0E0A0400 >> (8 * (k & 3))) & 0xFF; }
 
 // LDS layout of one operand tile.  R = rows of the tile in the mn direction,
 // KD = k per row of a k-contiguous tile (BK, or 2*BK for a pair buffer).
@@ -150,7 +150,7 @@ struct Layout {
     // transposing reads (table above); fp32 rows are read by 32-bit reads in
     // which the two half-waves take rows 4 apart, so rows with bit 2 of k set
     // move to the other 128-byte half of each 256-byte window.
-    __device__ static __forceinline__ int mswz(int k)
+    __host__ __device__ static constexpr int mswz(int k)
     {
         if constexpr (Cfg::ES == 2) return mn_swz(k);
         else return ((k >> 2) & 1) << 3;
@@ -161,13 +161,13 @@ struct Layout {
     // With 4 chunks per row (64-byte rows) measured bank-conflict counts on
     // gfx950 are zero for (r ^ r>>2) & 3 but four cycles per ds_read_b128 for
     // any swizzle that mixes in row bit 3, such as ((r>>1) ^ (r>>3)) & 3.
-    __device__ static __forceinline__ int kswz(int r)
+    __host__ __device__ static constexpr int kswz(int r)
     {
         if constexpr (CPR_K == 4) return (r ^ (r >> 2)) & 3;
-        else return swz<CPR_K>(r);
+        else return (r ^ (r >> 3)) & 7;
     }
     // byte offset of 16-byte chunk `chunk` in LDS row `row`
-    __device__ static __forceinline__ int off(int row, int chunk)
+    __host__ __device__ static constexpr int off(int row, int chunk)
     {
         if constexpr (KC)
             return row * (CPR_K * 16) + ((chunk ^ kswz(row)) << 4);
@@ -176,6 +176,115 @@ struct Layout {
     }
     static constexpr int ROWS = KC ? R : BK;        // LDS rows
     static constexpr int CPR = KC ? CPR_K : CPR_M;  // chunks per LDS row
+};
+
+// Addresses of the MFMA operand fragments a wave reads from one LDS buffer
+// of an operand (Layout<Cfg, R, KC, KD>), for a wave tile WT wide along mn
+// and NWP wave positions along mn (wave tile w starts at mn = w * WT).
+// Fragment (i, kk) is the FM x KSTEP operand slice of rows w*WT + i*FM ..
+// +FM-1 at k-fragment kk of the buffer, read in NPC pieces: one ds_read_b128
+// (k-contiguous), two transposing ds_read_b64_tr_b16 (bf16, mn-contiguous)
+// or four 32-bit reads (fp32, mn-contiguous).
+//
+// The swizzles make a lane's offset a different permutation for some
+// (i, kk, piece) combinations, but many combinations differ from one another
+// by the same constant in every lane.  PLAN groups them at compile time,
+// checking every lane and wave position: each group keeps one per-lane base
+// register, and a read adds its combination's constant, which the LDS
+// instruction's offset field absorbs.  So a wave needs a few address
+// registers instead of one per combination and stage.
+template <class Cfg, int R, bool KC, int KD, int WT, int NWP>
+struct FragAddr {
+    using L = Layout<Cfg, R, KC, KD>;
+    static constexpr int FM = Cfg::FM, KG = Cfg::KG, KSTEP = Cfg::KSTEP, VEC = Cfg::VEC;
+    static constexpr int NPC = KC ? 1 : (Cfg::ES == 2 ? 2 : 4);  // pieces per fragment
+    static constexpr int NFRAG = WT / FM;
+    static constexpr int NKSA = KD / KSTEP;
+    static constexpr int NCOMBO = NFRAG * NKSA * NPC;
+    static_assert(WT % FM == 0 && KD % KSTEP == 0, "fragment grid");
+    __host__ __device__ static constexpr int combo(int i, int kk, int pc)
+    {
+        return (i * NKSA + kk) * NPC + pc;
+    }
+
+    // Byte offset of piece pc of fragment (i, kk) for `lane` of the wave
+    // whose tile starts at mn index wmn0 (the MFMA operand lane mappings:
+    // k-contiguous, lane l holds row l % FM, k-chunk l / FM; transposing
+    // reads, lane r + 4j of each 16-lane group g addresses k-row j (+4 for the
+    // second piece, +8 per group pair) at mn 4r (+16 for odd groups with
+    // 32-wide fragments); fp32 32-bit reads, lane l holds mn l % 32 at k
+    // 4 (l / 32) + piece).
+    __host__ __device__ static constexpr int raw_off(int i, int kk, int pc, int lane, int wmn0)
+    {
+        const int mn0 = wmn0 + i * FM;
+        if constexpr (KC) {
+            return L::off(mn0 + lane % FM, kk * KG + lane / FM);
+        } else if constexpr (Cfg::ES == 4) {
+            const int mn = mn0 + (lane & 31);
+            const int k = kk * KSTEP + 4 * (lane >> 5) + pc;
+            return L::off(k, mn / VEC) + (mn % VEC) * 4;
+        } else {
+            const int g = lane >> 4, q = lane & 15, r = q & 3, j = q >> 2;
+            int mn = 0, k = 0;
+            if constexpr (FM == 32) {
+                mn = mn0 + 16 * (g & 1) + 4 * r;
+                k = kk * KSTEP + 8 * (g >> 1) + 4 * pc + j;
+            } else {
+                mn = mn0 + 4 * r;
+                k = kk * KSTEP + 8 * g + 4 * pc + j;
+            }
+            return L::off(k, mn >> 3) + (mn & 7) * 2;
+        }
+    }
+
+    struct Plan {
+        int nbase = 0;
+        int base_combo[NCOMBO] = {};  // the combination each base register is computed for
+        int base_shift[NCOMBO] = {};  // ... plus this constant
+        int cls[NCOMBO] = {};         // base register of each combination
+        int delta[NCOMBO] = {};       // ... and its constant (>= 0)
+    };
+    __host__ __device__ static constexpr int off_of(int x, int lane, int wmn0)
+    {
+        return raw_off(x / (NKSA * NPC), (x / NPC) % NKSA, x % NPC, lane, wmn0);
+    }
+    // whether combinations x and y differ by one constant d in every lane and
+    // wave position
+    __host__ __device__ static constexpr bool same_class(int x, int y, int& d)
+    {
+        d = off_of(x, 0, 0) - off_of(y, 0, 0);
+        for (int w = 0; w < NWP; ++w)
+            for (int lane = 0; lane < 64; ++lane)
+                if (off_of(x, lane, w * WT) - off_of(y, lane, w * WT) != d) return false;
+        return true;
+    }
+    __host__ __device__ static constexpr Plan make()
+    {
+        Plan p{};
+        for (int x = 0; x < NCOMBO; ++x) {
+            int b = 0, d = 0;
+            for (; b < p.nbase; ++b)
+                if (same_class(x, p.base_combo[b], d)) break;
+            if (b == p.nbase) {
+                p.base_combo[b] = x;
+                ++p.nbase;
+                d = 0;
+            }
+            p.cls[x] = b;
+            p.delta[x] = d;
+        }
+        for (int b = 0; b < p.nbase; ++b) {
+            int lo = 0;
+            for (int x = 0; x < NCOMBO; ++x)
+                if (p.cls[x] == b && p.delta[x] < lo) lo = p.delta[x];
+            p.base_shift[b] = lo;
+            for (int x = 0; x < NCOMBO; ++x)
+                if (p.cls[x] == b) p.delta[x] -= lo;
+        }
+        return p;
+    }
+    static constexpr Plan PLAN = make();
+    static constexpr int NBASE = PLAN.nbase;
 };
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -193,7 +302,8 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t nrec)
 
 // PAIRED: the operand lives in pair buffers (k-contiguous only): a DMA copy
 // covers two K-steps, register-staged copies one step into half `half`.
-template <class Cfg, int R, bool KC, bool ALIGNED, bool PAIRED = false>
+// WT, NWP: the wave tile's extent along mn and the wave positions along mn.
+template <class Cfg, int R, bool KC, bool ALIGNED, bool PAIRED, int WT, int NWP>
 struct DmaOperand {
     static_assert(!PAIRED || KC, "only k-contiguous operands are paired");
     static constexpr int KD = PAIRED ? 2 * Cfg::BK : Cfg::BK;  // k per buffer
@@ -319,58 +429,69 @@ struct DmaOperand {
         }
     }
 
-    // fp32 [k][mn] fragment piece e: one 32-bit read of k-slot e.  Lanes below
-    // 32 take k0+e and lanes from 32 take k0+4+e, matching the k-major
-    // operand's 16-byte read (4 consecutive k per half-wave).
-    __device__ static __forceinline__ uint32_t frag_f32_piece(const char* lds, int mn0, int ks,
-                                                             int lane, int e)
-    {
-        const int mn = mn0 + (lane & 31);
-        const int k = ks * Cfg::KSTEP + 4 * (lane >> 5) + e;
-        return *reinterpret_cast<const uint32_t*>(lds + L::off(k, mn / VEC) + (mn % VEC) * 4);
-    }
+    // ---- fragment reads (FragAddr: per-lane base registers + constants)
+    using FA = FragAddr<Cfg, R, KC, KD, WT, NWP>;
+    static constexpr int NREAD_PER_FRAG = FA::NPC;
+    uint32_t fbase[FA::NBASE];
 
-    // Half h (k-slots 4h..4h+3) of an mn-major fragment via one transposing read.
-    __device__ static __forceinline__ uint64_t frag_tr_half(const char* lds, int mn0, int ks, int lane,
-                                                           int h)
+    __device__ __forceinline__ void init_frags(int lane, int wmn0)
     {
-        constexpr int FM = Cfg::FM;
+        static_for<FA::NBASE>([&](auto b_c) __attribute__((always_inline)) {
+            constexpr int b = decltype(b_c)::value;
+            fbase[b] = (uint32_t)(FA::off_of(FA::PLAN.base_combo[b], lane, wmn0) +
+                                  FA::PLAN.base_shift[b]);
+        });
+    }
+    // Make the bases opaque to the optimizer at the top of each K-step: every
+    // read address is then formed inside the step as base + constant (the
+    // constant goes into the instruction), instead of one register per
+    // (stage, fragment, piece) hoisted out of the loop.
+    __device__ __forceinline__ void refresh()
+    {
+        static_for<FA::NBASE>([&](auto b_c) __attribute__((always_inline)) {
+            asm volatile("" : "+v"(fbase[decltype(b_c)::value]));
+        });
+    }
+    template <int I, int KK, int PC>
+    __device__ __forceinline__ const char* piece_addr(const char* buf) const
+    {
+        constexpr int x = FA::combo(I, KK, PC);
+        return buf + fbase[FA::PLAN.cls[x]] + FA::PLAN.delta[x];
+    }
+    // piece PC of fragment (I, KK): 16 bytes (k-contiguous), 8 bytes (bf16
+    // transposing read) or 4 bytes (fp32)
+    template <int I, int KK, int PC>
+    __device__ __forceinline__ u32x4 piece16(const char* buf) const
+    {
+        return *reinterpret_cast<const u32x4*>(piece_addr<I, KK, PC>(buf));
+    }
+    template <int I, int KK, int PC>
+    __device__ __forceinline__ uint64_t piece8(const char* buf) const
+    {
         typedef short s4 __attribute__((ext_vector_type(4)));
-        const int g = lane >> 4, q = lane & 15, r = q & 3, j = q >> 2;
-        int mn, k;
-        if constexpr (FM == 32) {
-            mn = mn0 + 16 * (g & 1) + 4 * r;
-            k = ks * Cfg::KSTEP + 8 * (g >> 1) + 4 * h + j;
-        } else {
-            mn = mn0 + 4 * r;
-            k = ks * Cfg::KSTEP + 8 * g + 4 * h + j;
-        }
-        const int o = L::off(k, mn >> 3) + (mn & 7) * 2;
         return __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                                (__attribute__((address_space(3))) s4*)(lds + o)));
+                                                (__attribute__((address_space(3))) s4*)(
+                                                    piece_addr<I, KK, PC>(buf))));
     }
-
-    // MFMA operand fragment: rows mn0 .. mn0+FM-1 (by lane), k-slots of step ks.
-    __device__ static __forceinline__ u32x4 frag(const char* lds, int mn0, int ks, int lane)
+    template <int I, int KK, int PC>
+    __device__ __forceinline__ uint32_t piece4(const char* buf) const
     {
-        constexpr int FM = Cfg::FM;
+        return *reinterpret_cast<const uint32_t*>(piece_addr<I, KK, PC>(buf));
+    }
+    // the whole fragment (I, KK)
+    template <int I, int KK>
+    __device__ __forceinline__ u32x4 frag(const char* buf) const
+    {
         if constexpr (KC) {
-            const int row = mn0 + lane % FM;
-            const int chunk = ks * Cfg::KG + lane / FM;
-            return *reinterpret_cast<const u32x4*>(lds + L::off(row, chunk));
+            return piece16<I, KK, 0>(buf);
         } else if constexpr (Cfg::ES == 4) {
-            return u32x4{frag_f32_piece(lds, mn0, ks, lane, 0), frag_f32_piece(lds, mn0, ks, lane, 1),
-                         frag_f32_piece(lds, mn0, ks, lane, 2), frag_f32_piece(lds, mn0, ks, lane, 3)};
+            return u32x4{piece4<I, KK, 0>(buf), piece4<I, KK, 1>(buf), piece4<I, KK, 2>(buf),
+                         piece4<I, KK, 3>(buf)};
         } else {
-            const uint64_t lo = frag_tr_half(lds, mn0, ks, lane, 0);
-            const uint64_t hi = frag_tr_half(lds, mn0, ks, lane, 1);
+            const uint64_t lo = piece8<I, KK, 0>(buf), hi = piece8<I, KK, 1>(buf);
             return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
         }
     }
-
-    // The n-th of the NREAD memory instructions that read one fragment set
-    // piece by piece (KC: one 16-byte read per fragment; MN: two halves).
-    static constexpr int NREAD_PER_FRAG = KC ? 1 : (Cfg::ES == 2 ? 2 : 4);
 };
 
 // s_waitcnt vmcnt(n) only (expcnt and lgkmcnt fields at their maxima).
@@ -417,8 +538,8 @@ void dma_gemm_kernel(GemmArgs p)
     constexpr bool PA = Cfg::pairs(A_KC, B_KC), PB = Cfg::pairs(B_KC, A_KC);
     constexpr bool PAIRED = PA || PB;
     constexpr int NP = Cfg::NP;
-    using OpA = DmaOperand<Cfg, BM, A_KC, ALIGNED, PA>;
-    using OpB = DmaOperand<Cfg, BN, B_KC, ALIGNED, PB>;
+    using OpA = DmaOperand<Cfg, BM, A_KC, ALIGNED, PA, Cfg::WTM, Cfg::WM>;
+    using OpB = DmaOperand<Cfg, BN, B_KC, ALIGNED, PB, Cfg::WTN, Cfg::WN>;
     constexpr int A_ST = PA ? 0 : OpA::BYTES, ST_BYTES = A_ST + (PB ? 0 : OpB::BYTES);
     constexpr int A_PR = PA ? OpA::BYTES : 0, PR_BYTES = A_PR + (PB ? OpB::BYTES : 0);
     constexpr int ST_DECL = ST_BYTES > 0 ? ST_BYTES : 16, PR_DECL = PR_BYTES > 0 ? PR_BYTES : 16;
@@ -473,6 +594,8 @@ void dma_gemm_kernel(GemmArgs p)
     OpB ob;
     oa.init(wave, lane, p.lda);
     ob.init(wave, lane, p.ldb);
+    oa.init_frags(lane, wave_m0);
+    ob.init_frags(lane, wave_n0);
     // end of each stored matrix: A is M x K (k-contiguous) or K x M, B likewise
     const char* end_a = reinterpret_cast<const char*>(
         A + (A_KC ? (int64_t)(p.M - 1) * p.lda + p.K : (int64_t)(p.K - 1) * p.lda + p.M));
@@ -593,14 +716,26 @@ void dma_gemm_kernel(GemmArgs p)
     }
     barrier_only();
 
-    auto read_frags = [&](int cur, int ks, int buf) __attribute__((always_inline)) {
-        const int ka = ks + (PA ? (cur & 1) * NKS : 0), kb = ks + (PB ? (cur & 1) * NKS : 0);
-#pragma unroll
-        for (int i = 0; i < MF; ++i) fa[buf][i] = OpA::frag(a_lds(cur), wave_m0 + i * FM, ka, lane);
-#pragma unroll
-        for (int j = 0; j < NF; ++j) fb[buf][j] = OpB::frag(b_lds(cur), wave_n0 + j * FM, kb, lane);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+
+    // every fragment of fragment step KS of the step in slot CUR into fa/fb[BUF]
+    auto read_frags = [&](auto cur_c, auto ks_c, auto buf_c) __attribute__((always_inline)) {
+        constexpr int CUR = decltype(cur_c)::value, KS = decltype(ks_c)::value;
+        constexpr int BUF = decltype(buf_c)::value;
+        constexpr int KA = KS + (PA ? (CUR & 1) * NKS : 0), KB = KS + (PB ? (CUR & 1) * NKS : 0);
+        static_for<MF>([&](auto i_c) __attribute__((always_inline)) {
+            fa[BUF][decltype(i_c)::value] = oa.template frag<decltype(i_c)::value, KA>(a_lds(CUR));
+        });
+        static_for<NF>([&](auto j_c) __attribute__((always_inline)) {
+            fb[BUF][decltype(j_c)::value] = ob.template frag<decltype(j_c)::value, KB>(b_lds(CUR));
+        });
     };
-    read_frags(0, 0, 0);
+    read_frags(I0{}, I0{}, I0{});
 
     // Fragment step of a K-step at which the barrier sits, and the stage the
     // copy issued after it fills (relative to the current stage).
@@ -615,9 +750,11 @@ void dma_gemm_kernel(GemmArgs p)
         constexpr int NXT = (CUR + 1) % P;
         constexpr int FAR = (CUR + FILL) % S;
         constexpr int WAIT = (CUR & 1) ? WAIT_O : WAIT_E;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            if (ks == BAR_KS) {
+        oa.refresh();
+        ob.refresh();
+        static_for<NKS>([&](auto ks_c) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ks_c)::value;
+            if constexpr (ks == BAR_KS) {
                 // the next step must have landed in every wave's part of LDS
                 // (and, with the late barrier, this wave's reads of the stage
                 // about to be refilled must be complete: lgkmcnt(0))
@@ -628,9 +765,10 @@ void dma_gemm_kernel(GemmArgs p)
                 if constexpr (PAIRED && (CUR & 1) != 0)
                     if (kt + 2 * NP - 1 < nk) load_pair((kt + 2 * NP - 1) / 2, pr((CUR >> 1) % NP));
             }
-            const int cb = ks & 1;
-            if (ks + 1 < NKS) read_frags(CUR, ks + 1, cb ^ 1);
-            else if (kt + 1 < nk) read_frags(NXT, 0, cb ^ 1);
+            constexpr int cb = ks & 1;
+            using NB = std::integral_constant<int, cb ^ 1>;
+            if constexpr (ks + 1 < NKS) read_frags(cur_c, std::integral_constant<int, ks + 1>{}, NB{});
+            else if (kt + 1 < nk) read_frags(std::integral_constant<int, NXT>{}, I0{}, NB{});
 #pragma unroll
             for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -638,7 +776,7 @@ void dma_gemm_kernel(GemmArgs p)
                     if constexpr (OUT_T) mfma_step<Cfg::KIND>(fa[cb][i], fb[cb][j], acc[i][j]);
                     else mfma_step<Cfg::KIND>(fb[cb][j], fa[cb][i], acc[i][j]);
                 }
-        }
+        });
     };
     // Steady-state step with a pinned instruction order: every MFMA of a
     // fragment step is followed by one or two memory instructions (the next
@@ -647,32 +785,36 @@ void dma_gemm_kernel(GemmArgs p)
     constexpr int RA = OpA::NREAD_PER_FRAG, RB = OpB::NREAD_PER_FRAG;
     constexpr int NREAD = MF * RA + NF * RB;
     constexpr int NMFMA = MF * NF;
-    auto read_op = [&](int n, int cur, int ks, int buf) __attribute__((always_inline)) {
-        if (n < MF * RA) {
-            const int i = n / RA;
-            const char* ab = a_lds(cur);
-            const int kk = ks + (PA ? (cur & 1) * NKS : 0);
+    // the N-th of the NREAD memory instructions reading fragment step KS of
+    // the step in slot CUR into fa/fb[BUF]
+    auto read_op = [&](auto n_c, auto cur_c, auto ks_c, auto buf_c) __attribute__((always_inline)) {
+        constexpr int N = decltype(n_c)::value, CUR = decltype(cur_c)::value;
+        constexpr int KS = decltype(ks_c)::value, BUF = decltype(buf_c)::value;
+        if constexpr (N < MF * RA) {
+            constexpr int i = N / RA, pc = N % RA;
+            constexpr int kk = KS + (PA ? (CUR & 1) * NKS : 0);
+            const char* ab = a_lds(CUR);
             if constexpr (RA == 1) {
-                fa[buf][i] = OpA::frag(ab, wave_m0 + i * FM, kk, lane);
+                fa[BUF][i] = oa.template piece16<i, kk, 0>(ab);
             } else if constexpr (RA == 4) {
-                fa[buf][i][n % RA] = OpA::frag_f32_piece(ab, wave_m0 + i * FM, kk, lane, n % RA);
+                fa[BUF][i][pc] = oa.template piece4<i, kk, pc>(ab);
             } else {
-                const uint64_t v = OpA::frag_tr_half(ab, wave_m0 + i * FM, kk, lane, n % RA);
-                fa[buf][i][2 * (n % RA)] = (uint32_t)v;
-                fa[buf][i][2 * (n % RA) + 1] = (uint32_t)(v >> 32);
+                const uint64_t v = oa.template piece8<i, kk, pc>(ab);
+                fa[BUF][i][2 * pc] = (uint32_t)v;
+                fa[BUF][i][2 * pc + 1] = (uint32_t)(v >> 32);
             }
         } else {
-            const int m = n - MF * RA, j = m / RB;
-            const char* bb = b_lds(cur);
-            const int kk = ks + (PB ? (cur & 1) * NKS : 0);
+            constexpr int m = N - MF * RA, j = m / RB, pc = m % RB;
+            constexpr int kk = KS + (PB ? (CUR & 1) * NKS : 0);
+            const char* bb = b_lds(CUR);
             if constexpr (RB == 1) {
-                fb[buf][j] = OpB::frag(bb, wave_n0 + j * FM, kk, lane);
+                fb[BUF][j] = ob.template piece16<j, kk, 0>(bb);
             } else if constexpr (RB == 4) {
-                fb[buf][j][m % RB] = OpB::frag_f32_piece(bb, wave_n0 + j * FM, kk, lane, m % RB);
+                fb[BUF][j][pc] = ob.template piece4<j, kk, pc>(bb);
             } else {
-                const uint64_t v = OpB::frag_tr_half(bb, wave_n0 + j * FM, kk, lane, m % RB);
-                fb[buf][j][2 * (m % RB)] = (uint32_t)v;
-                fb[buf][j][2 * (m % RB) + 1] = (uint32_t)(v >> 32);
+                const uint64_t v = ob.template piece8<j, kk, pc>(bb);
+                fb[BUF][j][2 * pc] = (uint32_t)v;
+                fb[BUF][j][2 * pc + 1] = (uint32_t)(v >> 32);
             }
         }
     };
@@ -690,6 +832,8 @@ void dma_gemm_kernel(GemmArgs p)
         const int kst = (k_lo + kt + AHEAD) * BK, kpr = (k_lo + kt + 2 * NP - 1) * BK;
         const uint32_t ka = OpA::step_bytes(PA ? kpr : kst, p.lda);
         const uint32_t kb = OpB::step_bytes(PB ? kpr : kst, p.ldb);
+        oa.refresh();
+        ob.refresh();
         static_for<NKS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
             constexpr int cb = ks & 1;
@@ -720,7 +864,10 @@ void dma_gemm_kernel(GemmArgs p)
                 static_for<hi - lo>([&](auto oo_c) __attribute__((always_inline)) {
                     constexpr int o = lo + decltype(oo_c)::value;
                     constexpr int d = o - NREAD;
-                    if constexpr (o < NREAD) read_op(o, rcur, rks, cb ^ 1);
+                    if constexpr (o < NREAD)
+                        read_op(std::integral_constant<int, o>{}, std::integral_constant<int, rcur>{},
+                                std::integral_constant<int, rks>{},
+                                std::integral_constant<int, cb ^ 1>{});
                     else if constexpr (d < NA_ST)
                         oa.dma_one(d, rsrc_a, ka, stage(FAR), wave);
                     else if constexpr (d < NA_ST + NB_ST)
@@ -735,13 +882,6 @@ void dma_gemm_kernel(GemmArgs p)
             });
         });
     };
-
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    using I4 = std::integral_constant<int, 4>;
-    using I5 = std::integral_constant<int, 5>;
 
     int kt = 0;
     // steady state: every step of the round issues its copies as DMA (the

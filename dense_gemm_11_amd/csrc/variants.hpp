@@ -9,7 +9,7 @@ namespace dg {
 typedef hipError_t (*LaunchFn)(const GemmArgs&, int grid, hipStream_t);
 typedef int (*OccFn)();  // workgroups of the kernel that fit on one compute unit
 
-enum VariantKind { KIND_VECTOR_FMA = 0, KIND_MFMA = 1, KIND_MFMA_DMA = 2 };
+enum VariantKind { KIND_VECTOR_FMA = 0, KIND_MFMA = 1, KIND_MFMA_DMA = 2, KIND_SMALL = 3 };
 
 struct Variant {
     const char* name;
@@ -94,6 +94,7 @@ const Variant* f32dma_variant_table(int* count);
 const Variant* bf16dma_sweep_variant_table(int* count);
 const Variant* f32dma_sweep_variant_table(int* count);
 const Variant* bf16dma_tile_variant_table(int* count);
+const Variant* small_variant_table(int* count);
 
 }  // namespace dg
 

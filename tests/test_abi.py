@@ -265,7 +265,7 @@ def test_traffic_record_names_the_step_kernels():
     with open(os.path.join(os.path.dirname(bench.__file__), "profiles", "hbm_traffic.json")) as f:
         rec = json.load(f)
     for name, tile in (("f32_dma32x32x2_256x256x32_w2x2_s2_late", (256, 256, 32)),
-                       ("bf16_dma32x32x16_256x256x32_w2x2_s3_late", (256, 256, 32))):
+                       ("bf16_dma32x32x16_256x256x32_w2x4_s3_late", (256, 256, 32))):
         key = bench.kernel_name_key(name, tile)
         hits = [k for k in rec["kernels"] if key + ">" in k or key + ", " in k]
         assert len(hits) == 1, (name, key, list(rec["kernels"]))

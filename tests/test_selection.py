@@ -15,20 +15,31 @@ P = "bf16_dma32x32x16_"
 CASES = [
     # dtype, transA, transB, M, N, K, beta, bf16 output, expected variant, stream-K?
     ("f32", "N", "N", 4096, 4096, 4096, 0.0, False, "f32_dma32x32x2_256x256x32_w2x2_s2_late", False),
-    ("bf16", "N", "N", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x2_s3_late", False),
-    ("bf16", "N", "T", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x2_s3_late", False),
-    # 544 tiles of 128x128: one round at 3 workgroups per CU (2-stage ring)
-    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, False, P + "128x128x32_w2x2_s2_late", False),
+    ("bf16", "N", "N", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "T", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    # half a wave of 256x256 tiles and rows that are not 16-byte aligned: the
+    # 8-wave 256x256 kernel
+    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, False, P + "256x256x32_w2x4_s3_late", False),
+    # ... and with a long K
+    ("bf16", "N", "N", 3072, 3072, 3072, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    # 576 tiles of 128x128, aligned, short K: one round at 3 workgroups per CU
     ("bf16", "N", "N", 3000, 3000, 512, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
+    ("bf16", "T", "N", 4096, 2176, 1536, 1.5, False, P + "128x128x32_w2x2_s2_late", False),
     # ... but not with bf16 output, which only the 4-stage variant carries
     ("bf16", "T", "N", 4093, 2051, 1537, 1.5, True, P + "128x128x32_w2x2_s4_late", False),
     # at most one tile per CU: the 4-stage ring
     ("bf16", "N", "N", 2048, 2048, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
-    # more tiles than CUs, at most 2 per CU, a k-contiguous operand: paired copies
-    ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    # more 128x128 tiles than CUs, at most 2 per CU, a k-contiguous operand:
+    # paired copies
     ("bf16", "N", "T", 2304, 2304, 2304, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
-    # ... but not without one
-    ("bf16", "T", "N", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    # long K, 128x256 tiles filling 3/4 to 1 of a wave: 128x256
+    ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "N", 4096, 2048, 4096, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    # short K over a full wave of 256x256 tiles: 128x256
+    ("bf16", "N", "N", 8192, 4096, 512, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "T", 8192, 8192, 1024, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    # ... but not below a full wave
+    ("bf16", "N", "N", 8192, 1536, 1024, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]

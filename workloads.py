@@ -94,6 +94,9 @@ WORKLOADS = {
         # few output tiles, long K: the shape split-K / stream-K is for
         Workload("bf16_small_mn_long_k", 12, "bf16", "N", "N", 1024, 1024, 32768, 1.0, 0.0, "n1",
                  "n1", description="few output tiles, long K: 1024x1024x32768"),
+        # the same GEMM for two MFMA instructions (32x32x16 and 16x16x32)
+        Workload("bf16_4096_tn", 13, "bf16", "T", "N", 4096, 4096, 4096, 1.0, 0.0, "n1", "n1",
+                 description="BF16 D=A^T*B, 4096^3, A stored KxM"),
     ]
 }
 
