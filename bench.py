@@ -315,37 +315,42 @@ def amd_smi_sample():
             "mem_clock_mhz": mem[0] if mem else None}
 
 
-def telemetry_under_load(part, stream_handle, lead: float = 0.3):
+def telemetry_under_load(part, stream_handle, seconds: float = 2.5, every: float = 0.25):
     """Clocks and power while part's kernel runs back to back (the bf16 matrix
     cores are power limited, so the clock under load belongs with the
-    timing): one amd-smi sample taken idle, then one started `lead` seconds
-    into a run of launches that goes on until that sample has been read
-    (amd-smi takes a second or more), so the GPU is busy throughout it."""
+    timing).  amd-smi's metrics refresh about once a second, so one sample
+    taken right after the load starts still shows the idle state: a thread
+    polls every `every` seconds through `seconds` of launches, and the
+    samples from the last second of load are reported (the last one as
+    under_load), beside one taken idle before."""
     import threading
     before = amd_smi_sample()
     if before is None:
         return None
-    result = {}
-
-    def sample():
-        time.sleep(lead)
-        t = time.perf_counter()
-        result["sample"] = amd_smi_sample()
-        result["sample_s"] = round(time.perf_counter() - t, 2)
-
-    th = threading.Thread(target=sample)
+    samples = []
+    stop = threading.Event()
     t0 = time.perf_counter()
+
+    def poll():
+        while not stop.is_set():
+            s = amd_smi_sample()
+            samples.append((round(time.perf_counter() - t0, 2), s))
+            time.sleep(every)
+
+    th = threading.Thread(target=poll)
     th.start()
     launches = 0
-    while th.is_alive():
+    while time.perf_counter() - t0 < seconds:
         for _ in range(4):
             part.launch(stream_handle)
         launches += 4
         torch.cuda.synchronize()
+    stop.set()
     th.join()
-    return {"workload": part.name, "before": before, "under_load": result.get("sample"),
-            "sample_seconds": result.get("sample_s"), "launches_during_sample": launches,
-            "load_seconds": round(time.perf_counter() - t0, 2)}
+    late = [s for t, s in samples if t >= seconds - 1.0 and s]
+    return {"workload": part.name, "before": before, "under_load": late[-1] if late else None,
+            "samples_last_second_of_load": late, "load_seconds": seconds,
+            "launches": launches}
 
 
 def oracle_sample_rate(part: Part, cores: int, budget_s: float):
