@@ -216,9 +216,13 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int,
         vid = [i for i, n, _, _ in g.variants() if n == variant_name][0]
     g.gemm_set_variant(h, vid)
     try:
-        run = lambda: g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
-                                    alpha=w.alpha, beta=w.beta, bias=bias,
-                                    activation=activation)
+        # the C call with its arguments marshalled once, so the loop times the
+        # library and the kernel rather than Python's argument checks
+        run = g.bind_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
+                             alpha=w.alpha, beta=w.beta, bias=bias, activation=activation)
+        s0 = run()
+        if s0 != g.GEMM_OK:
+            raise g.GemmError(s0)
         # at least `warmup` calls and ~50 ms of them: clocks that dropped
         # while the GPU idled take tens of milliseconds to come back
         t0 = time.perf_counter()

@@ -273,17 +273,9 @@ def variants():
             for i in range(gemm_variant_count())]
 
 
-def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
-                stream=None, check=True, bias=None, activation=GEMM_ACT_NONE,
-                clamp=None, no_alloc=False) -> int:
-    """gemm_run on torch tensors (row-major 2-D views with unit column stride).
-
-    A: op(A) is M x K (A stored M x K for "N", K x M for "T"); B likewise;
-    C, D: M x N.  A and B are float32 (fp32 GEMM) or bfloat16; with bfloat16
-    operands, C and D are float32 (GEMM_DTYPE_BF16_F32) or both bfloat16
-    (GEMM_DTYPE_BF16_BF16).  bias (a length-N tensor of D's dtype),
-    activation (GEMM_ACT_*) and clamp ((lo, hi)) select gemm_run_epilogue.
-    """
+def _marshal(h, A, B, D, C, transA, transB, alpha, beta, stream, bias, activation, clamp,
+             no_alloc):
+    """Check torch tensors and turn them into (C function, argument tuple)."""
     import torch
 
     def ld(t):
@@ -318,14 +310,41 @@ def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
     if no_alloc:
         if not plain:
             raise ValueError("gemm_run_no_alloc has no fused epilogue")
-        s = gemm_run_no_alloc(*args, stream)
-    elif plain:
-        s = gemm_run(*args, stream)
-    else:
-        lo, hi = (0.0, 0.0) if clamp is None else clamp
-        ep = GemmEpilogue(None if bias is None else bias.data_ptr(), int(activation),
-                          int(clamp is not None), float(lo), float(hi))
-        s = gemm_run_epilogue(*args, ep, stream)
+        return lib.gemm_run_no_alloc, args + (stream,)
+    if plain:
+        return lib.gemm_run, args + (stream,)
+    lo, hi = (0.0, 0.0) if clamp is None else clamp
+    ep = GemmEpilogue(None if bias is None else bias.data_ptr(), int(activation),
+                      int(clamp is not None), float(lo), float(hi))
+    return lib.gemm_run_epilogue, args + (ctypes.byref(ep), stream)
+
+
+def run_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
+                stream=None, check=True, bias=None, activation=GEMM_ACT_NONE,
+                clamp=None, no_alloc=False) -> int:
+    """gemm_run on torch tensors (row-major 2-D views with unit column stride).
+
+    A: op(A) is M x K (A stored M x K for "N", K x M for "T"); B likewise;
+    C, D: M x N.  A and B are float32 (fp32 GEMM) or bfloat16; with bfloat16
+    operands, C and D are float32 (GEMM_DTYPE_BF16_F32) or both bfloat16
+    (GEMM_DTYPE_BF16_BF16).  bias (a length-N tensor of D's dtype),
+    activation (GEMM_ACT_*) and clamp ((lo, hi)) select gemm_run_epilogue;
+    no_alloc selects gemm_run_no_alloc.
+    """
+    fn, args = _marshal(h, A, B, D, C, transA, transB, alpha, beta, stream, bias, activation,
+                        clamp, no_alloc)
+    s = fn(*args)
     if check and s != GEMM_OK:
         raise GemmError(s)
     return s
+
+
+def bind_tensors(h, A, B, D, C=None, transA="N", transB="N", alpha=1.0, beta=0.0,
+                 stream=None, bias=None, activation=GEMM_ACT_NONE, clamp=None,
+                 no_alloc=False):
+    """run_tensors' C call with its arguments marshalled once: returns a
+    function that makes the same call again and returns its status (for
+    timing loops; the tensors must stay alive while it is used)."""
+    fn, args = _marshal(h, A, B, D, C, transA, transB, alpha, beta, stream, bias, activation,
+                        clamp, no_alloc)
+    return lambda: fn(*args)

@@ -4,8 +4,9 @@
 //    unit, so one workgroup's prologue, barrier waits and epilogue overlap
 //    the other's matrix work ("High-Performance FP16 GEMM on NVIDIA Ada
 //    Lovelace", key results: a 256x128 tile with 3 stages);
-//  * 256x256 tiles with 8 waves in a 4x2 grid (64x128 per wave), beside the
-//    selected 2x4 grid;
+//  * 256x256 tiles with 8 waves: a 4x2 grid (64x128 per wave) beside the
+//    selected 2x4 grid, and the 2x4 grid with 4 stages or with 2 stages of
+//    64-deep steps (128 KiB of LDS either way);
 //  * the 16x16x32 bf16 instruction on 128x128 tiles with 64-deep steps (a
 //    step then holds two fragment steps), against the 32x32x16 sweep variant
 //    of the same tile, depth and stage count.
@@ -18,6 +19,8 @@ namespace dg {
 using Dma256x128s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 128, 32, 2, 2, 3, true, PAIR_NONE, 2>;
 using Dma128x256s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 256, 32, 2, 2, 3, true, PAIR_NONE, 2>;
 using Dma256w4x2s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 4, 2, 3, true, PAIR_BOTH_KC>;
+using Dma256w2x4s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 4, 4, true, PAIR_BOTH_KC>;
+using Dma256w2x4k64s2L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 4, 2, true>;
 using Dma16x128k64s2L = DmaConfig<MFMA_BF16_16x16x32, 128, 128, 64, 2, 2, 2, true>;
 
 #define BF16_DMA_VARIANT(NAME, CFG) \
@@ -30,6 +33,8 @@ const Variant* bf16dma_tile_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x128x32_w2x2_s3_late", Dma256x128s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x256x32_w2x2_s3_late", Dma128x256s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w4x2_s3_late", Dma256w4x2s3L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x4_s4_late", Dma256w2x4s4L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x4_s2_late", Dma256w2x4k64s2L),
         BF16_DMA_VARIANT("bf16_dma16x16x32_128x128x64_w2x2_s2_late", Dma16x128k64s2L),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
