@@ -543,8 +543,12 @@ def pipeline_sweep(g, h, reps: int = 10) -> dict:
         occ = g.gemm_variant_occupancy(i)
         r = time_extra(g, h, wname, name, reps=reps, warmup=3)
         mech = "paired" if "_pair" in name else "capped registers" if "_o3" in name else "ring"
+        # a family: one instruction, tile and wave grid; the depth is what varies
+        instr = re.search(r"_dma(\d+x\d+x\d+)_", name).group(1)
+        waves = re.search(r"_w(\d+x\d+)_", name).group(1)
         rows.append({"variant": name, "dtype": "bf16" if dt == g.GEMM_DTYPE_BF16_F32 else "f32",
-                     "family": f"{'bf16' if dt else 'f32'}_{tile[0]}x{tile[1]}x{tile[2]}",
+                     "family": f"{'bf16' if dt else 'f32'}_{instr}_{tile[0]}x{tile[1]}x{tile[2]}"
+                               f"_w{waves}",
                      "stages": stages, "d": ahead, "occ": occ, "kernel_ms": r["kernel_ms"],
                      "tflops": r["tflops"], "workload": wname, "mechanism": mech})
         print(f"[sweep] {name} S={stages} ahead={ahead} occ={occ} {r['kernel_ms']} ms "

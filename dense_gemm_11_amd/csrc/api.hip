@@ -181,13 +181,15 @@ int select_variant(int dtype, int64_t M, int64_t N, int64_t /*K*/, bool dma)
 // variant's lookahead d relative to the measured one ("High-Performance FP16
 // GEMM on NVIDIA Ada Lovelace", methodology: efficiency S/(S + kappa)).
 // kappa was fitted to the sweep of every direct-to-LDS variant on MI355X:
-// 1.27 steps for bf16; 0 for fp32, whose long steps hide the copies at any
-// depth.  (The occupancy part of that model is data_parallel_us's share.)
+// 0.85 steps for bf16 (1.23-1.27 before the fragment-address rework raised
+// the occupancy of several 128x128 variants); 0 for fp32, whose long steps
+// hide the copies at any depth.  (The occupancy part of that model is
+// data_parallel_us's share.)
 double step_us(const Variant& v)
 {
     const bool bf16 = v.dtype == GEMM_DTYPE_BF16_F32;
     const double base = bf16 ? 0.85 : 7.3;
-    const double kappa = bf16 ? 1.27 : 0.0, d_ref = bf16 ? 3.0 : 2.0;
+    const double kappa = bf16 ? 0.85 : 0.0, d_ref = bf16 ? 3.0 : 2.0;
     const double d = std::max(1, v.ahead);
     const double eff = (d / (d + kappa)) / (d_ref / (d_ref + kappa));
     return base * ((double)v.bm * v.bn * v.bk) / (256.0 * 256.0 * 32.0) / eff;
