@@ -1,5 +1,8 @@
-// bf16 matrix-core GEMM for gfx950 with direct-to-LDS loads and an S-stage
-// LDS ring: D = alpha * op(A) * op(B) + beta * C, bf16 operands, fp32 out.
+// Matrix-core GEMM for gfx950 with direct-to-LDS loads and an S-stage LDS
+// ring: D = alpha * op(A) * op(B) + beta * C, bf16 or fp32 operands, fp32
+// accumulate, fp32 or bf16 out.  A workgroup of WM x WN waves computes one
+// BM x BN output tile (the selected bf16 256x256 tile uses 8 waves, two per
+// SIMD, so one wave's waits are covered by the other's matrix work).
 //
 // Same hierarchical tiling as mfma_gemm.hpp ("GEMM on NVIDIA GPUs: from a
 // naive kernel to a tiled pipeline", section 4), with the load/compute
@@ -13,8 +16,9 @@
 //    swizzled layout below.  One buffer resource per operand starts at the
 //    workgroup's panel and ends where the stored matrix ends: a lane's offset
 //    is its fixed in-step offset plus the step's, and reads past the matrix
-//    return zero.  Addresses need only element alignment (16-byte loads at 2-
-//    or 4-byte aligned addresses are served whole by the memory system).
+//    return zero (buffer range checking).  Addresses need only element
+//    alignment: gfx9+ runs in the unaligned access mode, where a 16-byte load
+//    at a 2- or 4-byte aligned address is served whole.
 //  * Operands keep their memory orientation in LDS.  A k-contiguous operand
 //    (A with transA == N, B with transB == T) is stored [mn][k] in 16-byte
 //    chunks with the chunk index XOR-swizzled by row, and its MFMA fragments
@@ -25,6 +29,8 @@
 //    group, lane r+4j supplies the address of (k0+j, mn0+4r..4r+3) and lane
 //    4r+e receives element e of lanes r, r+4, r+8, r+12, i.e. four
 //    consecutive k of column mn0+4r+e — exactly an MFMA operand slice.
+//    Read addresses come from a few per-lane base registers plus
+//    compile-time constants (FragAddr).
 //  * S stages in separate __shared__ arrays (static indices keep the
 //    compiler's LDS-DMA dependency tracking exact).  One barrier per stage:
 //    before it each wave waits until the next stage's DMA has landed; after

@@ -205,10 +205,14 @@ gemm_status_t gemm_set_variant(gemm_handle_t h, int id);
  * call launched no GEMM kernel). */
 int gemm_last_variant(gemm_handle_t h);
 
-/* The variant automatic selection would use for this problem when A and B
- * are 16-byte aligned with 16-byte-multiple row pitches (host logic; it only
- * queries the current device's compute-unit count, assuming 256 when no
- * device answers); -1 for an invalid dtype/transpose. */
+/* The variant gemm_run's automatic selection takes for this problem on a
+ * handle without a workspace and without a forced variant, for A and B at
+ * 16-byte-aligned addresses with tightly packed rows (lda, ldb = the stored
+ * row length) and no fused epilogue: the same host logic gemm_run uses, so a
+ * call of that kind reports this variant through gemm_last_variant.  It
+ * queries the current device's compute-unit count and the variants'
+ * occupancy (assuming 256 compute units and one workgroup when no device
+ * answers); -1 for an invalid dtype, transpose or negative size. */
 int gemm_select_variant(gemm_dtype_t dtype, gemm_op_t transA, gemm_op_t transB,
                         int64_t M, int64_t N, int64_t K);
 
