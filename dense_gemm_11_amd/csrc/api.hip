@@ -78,7 +78,8 @@ const std::vector<Variant>& table()
         for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
                          bf16dma_variant_table, f32dma_variant_table,
                          bf16dma_sweep_variant_table, f32dma_sweep_variant_table,
-                         bf16dma_tile_variant_table, small_variant_table}) {
+                         bf16dma_tile_variant_table, bf16dma_192_variant_table,
+                         small_variant_table}) {
             int n = 0;
             const Variant* t = get(&n);
             v.insert(v.end(), t, t + n);
@@ -482,6 +483,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     //    straddles two units, and two waves per SIMD hide that latency): the
     //    8-wave 256x256 kernel (3072^3 76.5 -> 58.6; 4093x2051x1537 A^T B
     //    58.5 -> 50.1).
+    bool untransposed = false;  // an NN call that keeps its orientation
     if (sk == 0 && c.forced < 0 && aligned && !c.epi && !out_bf16 &&
         op_dtype == GEMM_DTYPE_BF16_F32) {
         static const int wide_tile = find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late");
@@ -499,6 +501,34 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) &&
                      dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
                 id = big_id;
+        }
+        // 192x256 tiles where they fill whole waves of compute units that
+        // 256x256 tiles leave partly empty: a wave of them takes about 3/4 of
+        // a 256x256 wave, so they win when ceil(tiles192 / CUs) * 3/4 is
+        // clearly below ceil(tiles256 / CUs).  The 192 side lies along M, or
+        // along N when an NN problem runs as D^T; NN takes the orientation
+        // with fewer waves, and on a tie D^T unless rows are not 16-byte
+        // aligned.  Measured on MI355X (ms, 256x256 -> 192x256): NN
+        // 8192x1536x4096 0.0982 -> 0.0910 (256 tiles instead of 192, one
+        // wave), 8192x4608x4096 0.2766 -> 0.2538, 3072^3 NN 0.0576 ->
+        // 0.0551 and TN 0.0565 -> 0.0532, 4093x2051x1537 A^T B 0.0497 ->
+        // 0.0489; NN 4093x2051x1537 0.0549 -> 0.0442 untransposed, 0.0590 as
+        // D^T.
+        static const int t192_id = find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late");
+        if (t192_id >= 0 && id == big_id && K >= 1024) {
+            const Variant& v192 = table()[t192_id];
+            constexpr int64_t NONE = INT64_MAX / 64;
+            const bool fit_n = dma_offsets_fit(v192, c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+            const bool can_t = c.a_kc && !c.b_kc && v192.nn_t_fn &&
+                               dma_offsets_fit(v192, false, true, K, c.ldb, c.lda, es);
+            const int64_t w_n = fit_n ? ceil_div(ceil_div(M, 192) * ceil_div(N, 256), cus) : NONE;
+            const int64_t w_t = can_t ? ceil_div(ceil_div(N, 192) * ceil_div(M, 256), cus) : NONE;
+            const bool use_t = can_t && (w_t < w_n || (w_t == w_n && c.rows16));
+            const int64_t w = use_t ? w_t : w_n;
+            if (w < NONE && 15 * w < 19 * ceil_div(t256, cus)) {  // 3/4 w < 0.95 w256
+                id = t192_id;
+                untransposed = can_t && !use_t;
+            }
         }
     }
     // bf16 128x128 whole tiles: the 2-stage ring fits 3 workgroups on a
@@ -527,8 +557,8 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     // bf16 NN with whole tiles: run as D^T = B^T A^T, which puts the
     // mn-contiguous operand first (measured on 8192^3, same box: TT layout
     // 1282 vs NN 1235 TFLOP/s); the transposed-output epilogue writes D.
-    const bool nn_t = sk == 0 && c.forced < 0 && vr.nn_t_fn && aligned && c.a_kc && !c.b_kc &&
-                      dma_offsets_fit(vr, false, true, K, c.ldb, c.lda, es);
+    const bool nn_t = sk == 0 && c.forced < 0 && !untransposed && vr.nn_t_fn && aligned &&
+                      c.a_kc && !c.b_kc && dma_offsets_fit(vr, false, true, K, c.ldb, c.lda, es);
     if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
     // fused epilogue: only the selected direct-to-LDS variants, whole tiles
     // and wide access, carry it
@@ -846,7 +876,9 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     // 4 tile-rows per group measured best on 8192^3 bf16 (groups of 1, 2, 3, 4, 6,
     // 8, 16 and 32 tried, with and without the XCD renumbering)
     a.group_m = std::min(a.tiles_m, 4);
-    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+    // whole tiles: the transposed-output launch tiles N by BM and M by BN
+    const int64_t grid = nn_t ? ceil_div(N, vr.bm) * ceil_div(M, vr.bn)
+                              : (int64_t)a.tiles_m * a.tiles_n;
     if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
     hipError_t e;
     const EpiFns* ef = pl.ef;

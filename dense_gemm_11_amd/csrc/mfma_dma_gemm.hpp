@@ -101,7 +101,18 @@ struct DmaConfig {
     static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MF = WTM / FM, NF = WTN / FM;
-    static constexpr int A_BYTES = BM * BK * ES, B_BYTES = BN * BK * ES;
+    // An operand tile's extent along mn as laid out in LDS: the next power of
+    // two (a 192-wide tile occupies 256), so the XOR swizzles, which permute
+    // chunk indices within a power-of-two row, and the 1 KiB-per-wave DMA
+    // split hold for every tile width.  The padding is copied as zeros (or
+    // as whatever the buffer range admits) and never read.
+    static constexpr int pad_extent(int r)
+    {
+        int e = 1;
+        while (e < r) e *= 2;
+        return e;
+    }
+    static constexpr int A_BYTES = pad_extent(BM) * BK * ES, B_BYTES = pad_extent(BN) * BK * ES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     // whether an operand that is (kc) k-contiguous is paired when the other
     // one is (other_kc)
@@ -148,8 +159,9 @@ __host__ __device__ constexpr int mn_swz(int k) { return (0x0E0A0400 >> (8 * (k 
 template <class Cfg, int R, bool KC, int KD = Cfg::BK>
 struct Layout {
     static constexpr int BK = KD;
+    static constexpr int RP = Cfg::pad_extent(R);  // rows (KC) or row width in LDS
     static constexpr int CPR_K = BK / Cfg::VEC;   // chunks per [mn][k] row
-    static constexpr int CPR_M = R / Cfg::VEC;    // chunks per [k][mn] row
+    static constexpr int CPR_M = RP / Cfg::VEC;   // chunks per [k][mn] row
     static_assert(!KC || CPR_K == 4 || CPR_K == 8, "k-major swizzle");
     static_assert(KC || CPR_M >= 16, "mn-major swizzle needs >= 16 chunks per row");
     // XOR for row k of an [k][mn] tile: bf16 rows are read 4 at a time by the
@@ -180,7 +192,7 @@ struct Layout {
         else
             return row * (CPR_M * 16) + ((chunk ^ mswz(row)) << 4);
     }
-    static constexpr int ROWS = KC ? R : BK;        // LDS rows
+    static constexpr int ROWS = KC ? RP : BK;       // LDS rows
     static constexpr int CPR = KC ? CPR_K : CPR_M;  // chunks per LDS row
 };
 
@@ -316,8 +328,8 @@ struct DmaOperand {
     using L = Layout<Cfg, R, KC, KD>;
     using T = typename Cfg::T;
     static constexpr int VEC = Cfg::VEC;
-    static constexpr int ND = (R * KD * Cfg::ES) / (1024 * Cfg::WAVES);  // DMA instructions per wave
-    static constexpr int BYTES = R * KD * Cfg::ES;                     // one buffer
+    static constexpr int ND = (L::RP * KD * Cfg::ES) / (1024 * Cfg::WAVES);  // DMA instructions per wave
+    static constexpr int BYTES = L::RP * KD * Cfg::ES;                     // one buffer
     static constexpr int SCPR = KC ? Cfg::BK / VEC : R / VEC;          // chunks per row of one step
     static constexpr int CHUNKS = (KC ? R : Cfg::BK) * SCPR;           // chunks of one step
     static constexpr int GL = (CHUNKS + Cfg::THREADS - 1) / Cfg::THREADS;  // guarded loads per thread
@@ -325,6 +337,10 @@ struct DmaOperand {
     // Per-lane byte offsets of this lane's DMA chunks from the start of a step
     // (row = mn and chunks along k for KC, row = k and chunks along mn
     // otherwise).  The host keeps every offset within the panel below 2^32.
+    // Chunks of the padding beyond R get an offset of 2^31: past the end of
+    // any panel the buffer range reaches below 2 GiB they read as zero without
+    // touching memory, and otherwise they fetch bytes of the matrix itself;
+    // either way nothing reads them back.
     uint32_t voff[ND];
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t ld)
@@ -338,7 +354,8 @@ struct DmaOperand {
             int c;
             if constexpr (KC) c = pc ^ L::kswz(row);
             else c = pc ^ L::mswz(row);
-            voff[d] = (uint32_t)(((int64_t)row * ld + c * VEC) * Cfg::ES);
+            const bool pad = KC ? row >= R : c * VEC >= R;
+            voff[d] = pad ? 0x80000000u : (uint32_t)(((int64_t)row * ld + c * VEC) * Cfg::ES);
         }
     }
 
@@ -987,13 +1004,16 @@ void dma_gemm_kernel(GemmArgs p)
     constexpr int ARR = USE_PR ? PR_BYTES : ST_BYTES;
     constexpr int MAXA = USE_PR ? 2 : (S < 3 ? S : 3);
     // fragment columns staged per pass: all NQA of a fragment row when every
-    // wave's block fits in MAXA arrays, else half of them in two passes
+    // wave's block fits in MAXA arrays and a staged row divides a 64-lane
+    // read, else half of them in two passes, else one per pass (three
+    // fragment columns: 24 chunks per row would not divide the read)
     constexpr auto fits = [](int qb) constexpr {
+        const int ch = qb * FM / 4;
         const int wps = ARR / (FM * qb * FM * 4);
-        return qb * FM / 4 >= 16 && qb * FM / 4 <= 64 && wps >= 1 &&
+        return ch >= 8 && ch <= 64 && 64 % ch == 0 && wps >= 1 &&
                (Cfg::WAVES + wps - 1) / wps <= MAXA;
     };
-    constexpr int NQ = fits(NQA) ? NQA : NQA / 2;
+    constexpr int NQ = fits(NQA) ? NQA : (NQA % 2 == 0 && fits(NQA / 2)) ? NQA / 2 : 1;
     static_assert(NQ >= 1 && NQA % NQ == 0 && fits(NQ), "staging space");
     constexpr int QH = NQA / NQ;       // passes per fragment row
     constexpr int DC = NQ * FM;        // D columns of the wave's block in one pass
@@ -1003,6 +1023,8 @@ void dma_gemm_kernel(GemmArgs p)
     constexpr int REGION = FM * DC * 4;
     constexpr int WPS = ARR / REGION;  // wave blocks per array
     static_assert(64 % CH == 0, "staging shape");
+    // row r's chunks are XORed with r mod 16 (mod CH for narrower rows)
+    constexpr int SWZ = CH >= 16 ? 15 : CH - 1;
     constexpr int NSA = (Cfg::WAVES + WPS - 1) / WPS;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     char* base = USE_PR ? pr0 : st0;
@@ -1010,7 +1032,7 @@ void dma_gemm_kernel(GemmArgs p)
     if constexpr (NSA > 2) base = wv / WPS == 2 ? st2 : base;
     char* const region = base + (wv % WPS) * REGION;
     auto slot = [&](int r, int chunk) __attribute__((always_inline)) -> f32x4* {
-        return reinterpret_cast<f32x4*>(region + r * (DC * 4) + ((chunk ^ (r & 15)) * 16));
+        return reinterpret_cast<f32x4*>(region + r * (DC * 4) + ((chunk ^ (r & SWZ)) * 16));
     };
     // first D row and column of the wave's block; the lane's 4 D columns in
     // pass qh start at col0 + qh * DC

@@ -17,11 +17,15 @@ CASES = [
     ("f32", "N", "N", 4096, 4096, 4096, 0.0, False, "f32_dma32x32x2_256x256x32_w2x2_s2_late", False),
     ("bf16", "N", "N", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     ("bf16", "N", "T", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
-    # half a wave of 256x256 tiles and rows that are not 16-byte aligned: the
-    # 8-wave 256x256 kernel
-    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, False, P + "256x256x32_w2x4_s3_late", False),
-    # ... and with a long K
-    ("bf16", "N", "N", 3072, 3072, 3072, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    # half a wave of 256x256 tiles and rows that are not 16-byte aligned, or a
+    # long K: 8-wave tiles, 192x256 where those fill as many waves (198 and
+    # 192 tiles here, 144 of 256x256)
+    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, False, P + "192x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "N", 4093, 2051, 1537, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "N", 3072, 3072, 3072, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
+    # 192x256 tiles would need two waves where 256x256 need one
+    ("bf16", "N", "N", 4096, 4096, 4096, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "T", "T", 8192, 1536, 4096, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     # 576 tiles of 128x128, aligned, short K: one round at 3 workgroups per CU
     ("bf16", "N", "N", 3000, 3000, 512, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
     ("bf16", "T", "N", 4096, 2176, 1536, 1.5, False, P + "128x128x32_w2x2_s2_late", False),
@@ -38,8 +42,10 @@ CASES = [
     # short K over a full wave of 256x256 tiles: 128x256
     ("bf16", "N", "N", 8192, 4096, 512, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
     ("bf16", "T", "T", 8192, 8192, 1024, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
-    # ... but not below a full wave
-    ("bf16", "N", "N", 8192, 1536, 1024, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    # ... but not below a full wave: there 192x256 tiles (as D^T, 192 along
+    # N) fill the wave that 256x256 tiles fill three quarters of
+    ("bf16", "N", "N", 8192, 1536, 1024, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "N", 8192, 1536, 4096, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]
