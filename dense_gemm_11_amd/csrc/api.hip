@@ -502,32 +502,48 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                      dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
                 id = big_id;
         }
-        // 192x256 tiles where they fill whole waves of compute units that
-        // 256x256 tiles leave partly empty: a wave of them takes about 3/4 of
-        // a 256x256 wave, so they win when ceil(tiles192 / CUs) * 3/4 is
-        // clearly below ceil(tiles256 / CUs).  The 192 side lies along M, or
-        // along N when an NN problem runs as D^T; NN takes the orientation
-        // with fewer waves, and on a tie D^T unless rows are not 16-byte
-        // aligned.  Measured on MI355X (ms, 256x256 -> 192x256): NN
-        // 8192x1536x4096 0.0982 -> 0.0910 (256 tiles instead of 192, one
-        // wave), 8192x4608x4096 0.2766 -> 0.2538, 3072^3 NN 0.0576 ->
-        // 0.0551 and TN 0.0565 -> 0.0532, 4093x2051x1537 A^T B 0.0497 ->
-        // 0.0489; NN 4093x2051x1537 0.0549 -> 0.0442 untransposed, 0.0590 as
-        // D^T.
-        static const int t192_id = find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late");
-        if (t192_id >= 0 && id == big_id && K >= 1024) {
-            const Variant& v192 = table()[t192_id];
+        // Tiles with a 192-wide side (192x256, 256x192) where they fill whole
+        // waves of compute units that 256x256 tiles leave partly empty: a
+        // wave of them takes about 3/4 of a 256x256 wave, so they win when
+        // 3/4 of their waves stays below 0.95 of the 256x256 waves.  Each
+        // runs as stored or, for NN, as D^T (which swaps the sides the tile
+        // dimensions lie on); the fewest waves win, and on a tie D^T for NN
+        // unless rows are not 16-byte aligned.  Measured on MI355X (ms,
+        // 256x256 -> 192-wide, one box per group): NN 8192x1536x4096 0.0982
+        // -> 0.0910 (256 tiles instead of 192, one wave), 8192x4608x4096
+        // 0.2766 -> 0.2538, 3072^3 NN 0.0576 -> 0.0551 and TN 0.0565 ->
+        // 0.0532, NN 4093x2051x1537 0.0549 -> 0.0442 as stored (0.0590 as
+        // D^T); NT 8192x1536x4096 0.0974 -> 0.0888 and 8192x3072x4096 0.1868
+        // -> 0.1723 (256x192), NN 1536x8192x4096 0.0917 -> 0.0867.
+        static const int w192[2] = {find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late"),
+                                    find_variant("bf16_dma32x32x16_256x192x32_w4x2_s3_late")};
+        if (id == big_id && K >= 1024) {
             constexpr int64_t NONE = INT64_MAX / 64;
-            const bool fit_n = dma_offsets_fit(v192, c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
-            const bool can_t = c.a_kc && !c.b_kc && v192.nn_t_fn &&
-                               dma_offsets_fit(v192, false, true, K, c.ldb, c.lda, es);
-            const int64_t w_n = fit_n ? ceil_div(ceil_div(M, 192) * ceil_div(N, 256), cus) : NONE;
-            const int64_t w_t = can_t ? ceil_div(ceil_div(N, 192) * ceil_div(M, 256), cus) : NONE;
-            const bool use_t = can_t && (w_t < w_n || (w_t == w_n && c.rows16));
-            const int64_t w = use_t ? w_t : w_n;
-            if (w < NONE && 15 * w < 19 * ceil_div(t256, cus)) {  // 3/4 w < 0.95 w256
-                id = t192_id;
-                untransposed = can_t && !use_t;
+            int64_t best_w = NONE;
+            bool best_pref = false;
+            for (int vi = 0; vi < 2; ++vi) {
+                if (w192[vi] < 0) continue;
+                const Variant& vv = table()[w192[vi]];
+                for (int tr = 0; tr < 2; ++tr) {
+                    const bool ok = tr ? (c.a_kc && !c.b_kc && vv.nn_t_fn &&
+                                          dma_offsets_fit(vv, false, true, K, c.ldb, c.lda, es))
+                                       : dma_offsets_fit(vv, c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+                    if (!ok) continue;
+                    const int64_t tiles = tr ? ceil_div(N, vv.bm) * ceil_div(M, vv.bn)
+                                             : ceil_div(M, vv.bm) * ceil_div(N, vv.bn);
+                    const int64_t w = ceil_div(tiles, cus);
+                    // D^T first for aligned NN rows, as stored otherwise; then
+                    // 192x256 before 256x192
+                    const bool pref = (tr == 1) == c.rows16;
+                    if (w < best_w || (w == best_w && pref && !best_pref)) {
+                        best_w = w;
+                        best_pref = pref;
+                        if (15 * w < 19 * ceil_div(t256, cus)) {  // 3/4 w < 0.95 w256
+                            id = w192[vi];
+                            untransposed = c.a_kc && !c.b_kc && tr == 0;
+                        }
+                    }
+                }
             }
         }
     }

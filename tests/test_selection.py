@@ -23,9 +23,11 @@ CASES = [
     ("bf16", "T", "N", 4093, 2051, 1537, 1.5, False, P + "192x256x32_w2x4_s3_late", False),
     ("bf16", "N", "N", 4093, 2051, 1537, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
     ("bf16", "N", "N", 3072, 3072, 3072, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
-    # 192x256 tiles would need two waves where 256x256 need one
+    # 192-wide tiles would need two waves where 256x256 need one
     ("bf16", "N", "N", 4096, 4096, 4096, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
-    ("bf16", "T", "T", 8192, 1536, 4096, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    # 1536 columns as stored: 256x192 tiles (one wave of 256 instead of 192)
+    ("bf16", "T", "T", 8192, 1536, 4096, 0.0, False, P + "256x192x32_w4x2_s3_late", False),
+    ("bf16", "N", "T", 8192, 1536, 4096, 0.0, False, P + "256x192x32_w4x2_s3_late", False),
     # 576 tiles of 128x128, aligned, short K: one round at 3 workgroups per CU
     ("bf16", "N", "N", 3000, 3000, 512, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
     ("bf16", "T", "N", 4096, 2176, 1536, 1.5, False, P + "128x128x32_w2x2_s2_late", False),
