@@ -556,6 +556,88 @@ def pipeline_sweep(g, h, reps: int = 10) -> dict:
     return {"rows": rows, "model": fit_pipeline_model([r for r in rows if r["mechanism"] == "ring"])}
 
 
+POWER_SWEEP = [("auto", "NN"),
+               ("bf16_dma32x32x16_256x256x32_w2x4_s3_late", "TT"),
+               ("bf16_dma32x32x16_256x256x32_w4x2_s3_late", "TT"),
+               ("bf16_dma32x32x16_256x256x32_w2x4_s4_late", "TT"),
+               ("bf16_dma32x32x16_256x256x32_w2x2_s3_late", "TT"),
+               ("bf16_dma32x32x16_256x256x64_w2x4_s2_late", "TT"),
+               ("bf16_dma32x32x16_256x256x32_w2x4_s3_late", "TN"),
+               ("bf16_dma32x32x16_256x256x32_w2x2_s3_late", "TN"),
+               ("bf16_dma32x32x16_128x256x32_w2x2_s3_late", "TT"),
+               ("bf16_dma32x32x16_128x128x32_w2x2_s4_late", "TT")]
+
+
+def power_sweep(g, h, seconds: float = 3.0) -> dict:
+    """Clock, power and rate of bf16 8192^3 kernels run back to back.
+
+    The bf16 matrix cores run at the board's power limit, so a kernel's rate
+    is set by its energy per FLOP as much as by its efficiency per clock.
+    Each (variant, layout) runs for `seconds` on N(0,1) operands (one buffer
+    set); amd-smi is polled every 0.25 s and the samples of the last second
+    are averaged.  A forced variant runs in the layout given (TT is the
+    operand orientation of the NN-as-D^T launch the selector uses); "auto"
+    is the selected path for NN."""
+    import threading
+    n = 8192
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8192)
+    X = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
+    Y = torch.randn(n, n, device="cuda", generator=gen).to(torch.bfloat16)
+    D = torch.empty(n, n, device="cuda")
+    names = {name: i for i, name, _, _ in g.variants()}
+    rows = []
+    for vname, lay in POWER_SWEEP:
+        if vname != "auto" and vname not in names:
+            continue
+        g.gemm_set_variant(h, -1 if vname == "auto" else names[vname])
+
+        def run():
+            st = g.run_tensors(h, X, Y, D, transA=lay[0], transB=lay[1], check=False)
+            if st != g.GEMM_OK:
+                raise RuntimeError(g.gemm_status_string(st))
+
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
+        used = g.gemm_variant_name(g.gemm_last_variant(h))
+        samples = []
+        stop = threading.Event()
+        t0 = time.perf_counter()
+
+        def poll():
+            while not stop.is_set():
+                samples.append((time.perf_counter() - t0, amd_smi_sample()))
+                time.sleep(0.25)
+
+        th = threading.Thread(target=poll)
+        th.start()
+        launches = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                run()
+            launches += 4
+            torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        stop.set()
+        th.join()
+        late = [x for t, x in samples if t >= seconds - 1.0 and x]
+        pw = sum(x["socket_power_w"] for x in late) / len(late) if late else None
+        clk = sum(x["gfx_clock_mhz_mean"] for x in late) / len(late) if late else None
+        tf = launches * 2.0 * n ** 3 / dt / 1e12
+        row = {"variant": used, "layout": lay, "ms": round(dt * 1e3 / launches, 4),
+               "tflops": round(tf, 1), "power_w": None if pw is None else round(pw),
+               "clock_mhz": None if clk is None else round(clk),
+               "tflops_per_ghz": None if clk is None else round(tf / clk * 1e3),
+               "w_per_tflops": None if pw is None else round(pw / tf, 3)}
+        rows.append(row)
+        print(f"[power] {row}", file=sys.stderr, flush=True)
+        time.sleep(1.0)
+    g.gemm_set_variant(h, -1)
+    return {"workload": "bf16 8192^3, N(0,1) operands, back to back", "seconds": seconds,
+            "rows": rows}
+
+
 def trace_summary(trace_csv: str, stats_csv: str, warmup: int, steps: int) -> int:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of this
     benchmark: rocprofv3's own per-kernel statistics, and for each step kernel
@@ -622,6 +704,9 @@ def main(argv=None):
     ap.add_argument("--pipeline-sweep", action="store_true",
                     help="time every direct-to-LDS variant on the NN step shapes, fit the "
                          "pipeline-depth model, print one JSON object, then exit")
+    ap.add_argument("--power-sweep", action="store_true",
+                    help="run bf16 8192^3 kernels back to back and record clock, power and "
+                         "rate for each, print one JSON object, then exit")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
                     help="summarize a rocprofv3 --kernel-trace --stats run of this benchmark "
                          "(its kernel_trace.csv and kernel_stats.csv; pass that run's --steps "
@@ -644,6 +729,10 @@ def main(argv=None):
     h = g.gemm_create()
     if args.pipeline_sweep:
         print(json.dumps(pipeline_sweep(g, h)), flush=True)
+        g.gemm_destroy(h)
+        return 0
+    if args.power_sweep:
+        print(json.dumps(power_sweep(g, h)), flush=True)
         g.gemm_destroy(h)
         return 0
     if args.vector_fma_only:
