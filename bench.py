@@ -560,6 +560,7 @@ POWER_SWEEP = [("auto", "NN"),
                ("bf16_dma32x32x16_256x256x32_w2x4_s3_late", "TT"),
                ("bf16_dma32x32x16_256x256x32_w4x2_s3_late", "TT"),
                ("bf16_dma32x32x16_256x256x32_w2x4_s4_late", "TT"),
+               ("bf16_dma32x32x16_256x256x32_w2x4_s4_late_pair1", "TT"),
                ("bf16_dma32x32x16_256x256x32_w2x2_s3_late", "TT"),
                ("bf16_dma32x32x16_256x256x64_w2x4_s2_late", "TT"),
                ("bf16_dma32x32x16_256x256x32_w2x4_s3_late", "TN"),

@@ -6,7 +6,8 @@
 //    Lovelace", key results: a 256x128 tile with 3 stages);
 //  * 256x256 tiles with 8 waves: a 4x2 grid (64x128 per wave) beside the
 //    selected 2x4 grid, and the 2x4 grid with 4 stages or with 2 stages of
-//    64-deep steps (128 KiB of LDS either way);
+//    64-deep steps (128 KiB of LDS either way), and the 2x4 grid pairing the
+//    k-contiguous operand's copies when the other operand is mn-contiguous;
 //  * the 16x16x32 bf16 instruction on 128x128 tiles with 64-deep steps (a
 //    step then holds two fragment steps), against the 32x32x16 sweep variant
 //    of the same tile, depth and stage count.
@@ -22,6 +23,7 @@ using Dma256w4x2s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 4, 2, 3, true,
 using Dma256w2x4s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 4, 4, true, PAIR_BOTH_KC>;
 using Dma256w2x4k64s2L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 4, 2, true>;
 using Dma16x128k64s2L = DmaConfig<MFMA_BF16_16x16x32, 128, 128, 64, 2, 2, 2, true>;
+using Dma256w2x4s4LP1 = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 4, 4, true, PAIR_ONE_KC>;
 
 #define BF16_DMA_VARIANT(NAME, CFG) \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, CFG::S, CFG::AHEAD, \
@@ -36,6 +38,7 @@ const Variant* bf16dma_tile_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x4_s4_late", Dma256w2x4s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x4_s2_late", Dma256w2x4k64s2L),
         BF16_DMA_VARIANT("bf16_dma16x16x32_128x128x64_w2x2_s2_late", Dma16x128k64s2L),
+        BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x4_s4_late_pair1", Dma256w2x4s4LP1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
