@@ -63,3 +63,22 @@ def test_tile192_parity(handle, case):
     err, tol = oracle_check("bf16", ta, tb, M, N, K, alpha, beta, A, B, C, D, rows=rows, cols=cols)
     print(f"[result] tile192 {ta}{tb} {M}x{N}x{K} max_rel_err={err:.3e} tol={tol:g}", flush=True)
     assert err <= tol
+
+
+def test_tile192_panel_beyond_2gib(handle):
+    """A 192-wide mn-contiguous operand whose panel spans more than 2 GiB: the
+    padding's copies (offset 2^31 past the step) then land inside the buffer
+    range and fetch bytes of the matrix, which nothing reads back."""
+    import dense_gemm_11_amd as g
+    M, N, K = 3072, 3072, 2048
+    ld_a = 600_000                       # K x M panel: 2048 * 600000 * 2 bytes = 2.46 GB
+    announce("tile192 panel > 2 GiB", M, N, K, ld_a)
+    A, B, _ = make_case("bf16", "T", "N", M, N, K, seed=4200, dist="n1", with_c=False)
+    D, _, _ = gpu_gemm(handle, "bf16", "T", "N", M, N, K, 1.0, 0.0, A, B, None,
+                       ld_pad=(ld_a - M, 0, 0, 0))
+    assert g.gemm_variant_name(g.gemm_last_variant(handle)) in V192
+    rows, cols = workloads.sample_indices(M, N, 4242)
+    err, tol = oracle_check("bf16", "T", "N", M, N, K, 1.0, 0.0, A, B, None, D, rows=rows, cols=cols)
+    print(f"[result] tile192 panel>2GiB max_rel_err={err:.3e} tol={tol:g}", flush=True)
+    assert err <= tol
+    torch.cuda.empty_cache()
