@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -22,6 +23,8 @@ struct gemm_handle_s {
     void* ws;            // caller-owned device workspace for stream-K, or null
     size_t ws_bytes;
     int sk_spin;         // polls a stream-K finisher spends on each contributor
+    int log;             // GEMM_LOG: one line per call on stderr
+    int fail_launch;     // GEMM_DEBUG_FAIL_LAUNCH: report GEMM_ERR_HIP instead of launching
 };
 
 namespace dg {
@@ -603,7 +606,14 @@ extern "C" {
 gemm_status_t gemm_create(gemm_handle_t* out)
 {
     if (!out) return GEMM_ERR_INVALID_VALUE;
-    gemm_handle_t h = new (std::nothrow) gemm_handle_s{-1, -1, -1, 0, nullptr, 0, dg::SK_SPIN_DEFAULT};
+    // a variable that is set, non-empty and not "0" turns its switch on
+    auto env_on = [](const char* name) {
+        const char* v = std::getenv(name);
+        return v && v[0] != '\0' && std::strcmp(v, "0") != 0 ? 1 : 0;
+    };
+    gemm_handle_t h = new (std::nothrow) gemm_handle_s{
+        -1, -1, -1, 0, nullptr, 0, dg::SK_SPIN_DEFAULT, env_on("GEMM_LOG"),
+        env_on("GEMM_DEBUG_FAIL_LAUNCH")};
     if (!h) return GEMM_ERR_ALLOC;
     *out = h;
     return GEMM_OK;
@@ -855,6 +865,7 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     a.clamp_hi = a.clamp ? ep->clamp_hi : 0.0f;
 
     if (!reads_ab) {
+        if (h->fail_launch) return GEMM_ERR_HIP;
         const int64_t blocks = std::min<int64_t>(ceil_div(M * N, 256), 65536);
         void* args[] = {&a};
         const void* k = out_bf16 ? reinterpret_cast<const void*>(&scale_c_kernel<bf16_t>)
@@ -896,6 +907,7 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     const int64_t grid = nn_t ? ceil_div(N, vr.bm) * ceil_div(M, vr.bn)
                               : (int64_t)a.tiles_m * a.tiles_n;
     if (grid > INT_MAX) return GEMM_ERR_NOT_SUPPORTED;
+    if (h->fail_launch) return GEMM_ERR_HIP;
     hipError_t e;
     const EpiFns* ef = pl.ef;
     if (sk > 0) {
@@ -926,6 +938,15 @@ static gemm_status_t run_gemm(gemm_handle_t h, gemm_op_t transA, gemm_op_t trans
     if (e != hipSuccess) return GEMM_ERR_HIP;
     h->last_variant = id;
     h->last_stream_k = sk;
+    if (h->log) {
+        static const char* const dt_name[3] = {"f32", "bf16_f32", "bf16_bf16"};
+        std::fprintf(stderr,
+                     "gemm: %s %c%c M=%lld N=%lld K=%lld dtype=%s grid=%lld stream_k=%d "
+                     "as_transpose=%d epilogue=%d\n",
+                     vr.name, transA == GEMM_OP_N ? 'N' : 'T', transB == GEMM_OP_N ? 'N' : 'T',
+                     (long long)M, (long long)N, (long long)K, dt_name[dtype],
+                     (long long)(sk > 0 ? sk : grid), sk, nn_t ? 1 : 0, epi ? 1 : 0);
+    }
     return GEMM_OK;
 }
 

@@ -95,7 +95,16 @@ typedef enum {
     GEMM_ERR_STREAM_K = 5
 } gemm_status_t;
 
-/* Create a handle (*out receives it).  Makes no HIP call. */
+/* Create a handle (*out receives it).  Makes no HIP call.  Two environment
+ * variables, read here (set, non-empty and not "0" turns them on), apply to
+ * every call made through the handle:
+ *   GEMM_LOG               : after each launch, one line on stderr naming the
+ *                            variant, layout, shape, dtype, grid, stream-K
+ *                            workgroups and whether NN ran as D^T;
+ *   GEMM_DEBUG_FAIL_LAUNCH : calls that pass their checks return GEMM_ERR_HIP
+ *                            instead of launching (D is left untouched), so
+ *                            callers can exercise their launch-failure path
+ *                            without a real fault. */
 gemm_status_t gemm_create(gemm_handle_t* out);
 
 /* Release a handle.  NULL is accepted and ignored.  Pending work on streams
