@@ -1097,17 +1097,33 @@ void dma_gemm_kernel(GemmArgs p)
         const int row0 = wr0 + o * FM + lane / CH;
         // interior tiles: the activation and the clamp are compile-time
         // choices of the loop, so its body has no branches
+        // The C rows of a group of CG read instructions are loaded before any
+        // of the group's D rows is stored, so CG loads are in flight per lane
+        // (the compiler cannot move a C load above an earlier D store itself:
+        // C and D may be the same matrix).  Every element is still read
+        // before it is written, so C == D stays correct.
+        constexpr int CG = NT < 4 ? NT : 4;
         auto interior_rows = [&](auto act_c, auto clamp_c) __attribute__((always_inline)) {
-#pragma unroll 4
-            for (int t = 0; t < NT; ++t) {
-                const int64_t row = row0 + t * RPI;
-                f32x4 out = alpha * *slot(t * RPI + lane / CH, lane % CH);
-                if (beta != 0.0f)
-                    out += beta * load4(reinterpret_cast<const OutT*>(p.C) + row * p.ldc + col);
-                if constexpr (EPI)
-                    out = epilogue_fixed4<decltype(act_c)::value, decltype(clamp_c)::value>(p, out,
-                                                                                          bias4[qh]);
-                store4(reinterpret_cast<OutT*>(p.D) + row * p.ldd + col, out);
+#pragma unroll 1
+            for (int t0 = 0; t0 < NT; t0 += CG) {
+                f32x4 cv[CG];
+                if (beta != 0.0f) {
+#pragma unroll
+                    for (int u = 0; u < CG; ++u)
+                        cv[u] = load4(reinterpret_cast<const OutT*>(p.C) +
+                                      (int64_t)(row0 + (t0 + u) * RPI) * p.ldc + col);
+                }
+#pragma unroll
+                for (int u = 0; u < CG; ++u) {
+                    const int t = t0 + u;
+                    const int64_t row = row0 + t * RPI;
+                    f32x4 out = alpha * *slot(t * RPI + lane / CH, lane % CH);
+                    if (beta != 0.0f) out += beta * cv[u];
+                    if constexpr (EPI)
+                        out = epilogue_fixed4<decltype(act_c)::value, decltype(clamp_c)::value>(
+                            p, out, bias4[qh]);
+                    store4(reinterpret_cast<OutT*>(p.D) + row * p.ldd + col, out);
+                }
             }
         };
         using A0 = std::integral_constant<int, EPI_ACT_NONE>;
@@ -1128,30 +1144,43 @@ void dma_gemm_kernel(GemmArgs p)
                 interior_rows(A0{}, C0{});
             }
         } else {
+            // edge tiles: rows past D skipped, columns masked; C rows of a
+            // group loaded ahead of its stores as on interior tiles
 #pragma unroll 1
-            for (int t = 0; t < NT; ++t) {
-                const int row = row0 + t * RPI;
-                if (row >= d_rows) continue;
-                f32x4 out = alpha * *slot(t * RPI + lane / CH, lane % CH);
+            for (int t0 = 0; t0 < NT; t0 += CG) {
+                f32x4 cv[CG];
                 if (beta != 0.0f) {
-                    const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)row * p.ldc;
-                    f32x4 cv;
-                    if (p.c_vec && col + 4 <= d_cols) {
-                        cv = load4(crow + col);
+#pragma unroll
+                    for (int u = 0; u < CG; ++u) {
+                        const int row = row0 + (t0 + u) * RPI;
+                        cv[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        if (row >= d_rows) continue;
+                        const OutT* crow = reinterpret_cast<const OutT*>(p.C) + (int64_t)row * p.ldc;
+                        if (p.c_vec && col + 4 <= d_cols) {
+                            cv[u] = load4(crow + col);
+                        } else {
+#pragma unroll
+                            for (int s = 0; s < 4; ++s)
+                                if (col + s < d_cols) cv[u][s] = to_f32(crow[col + s]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < CG; ++u) {
+                    const int t = t0 + u;
+                    const int row = row0 + t * RPI;
+                    if (row >= d_rows) continue;
+                    f32x4 out = alpha * *slot(t * RPI + lane / CH, lane % CH);
+                    if (beta != 0.0f) out += beta * cv[u];
+                    if constexpr (EPI) out = epilogue_op4(p, out, bias4[qh]);
+                    OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
+                    if (col_vec) {
+                        store4(drow + col, out);
                     } else {
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) cv[s] = col + s < d_cols ? to_f32(crow[col + s]) : 0.0f;
+                        for (int s = 0; s < 4; ++s)
+                            if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
                     }
-                    out += beta * cv;
-                }
-                if constexpr (EPI) out = epilogue_op4(p, out, bias4[qh]);
-                OutT* drow = reinterpret_cast<OutT*>(p.D) + (int64_t)row * p.ldd;
-                if (col_vec) {
-                    store4(drow + col, out);
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        if (col + s < d_cols) drow[col + s] = from_f32<OutT>(out[s]);
                 }
             }
         }
