@@ -290,11 +290,23 @@ def graph_replay_ms(g, h, name: str, launches: int = 50, replays: int = 5) -> fl
     return round(e0.elapsed_time(e1) / (replays * launches), 4)
 
 
+def under_profiler() -> bool:
+    """Whether a profiler's library is preloaded into this process (rocprofv3
+    runs the program that way).  A child process started from here would
+    inherit it and initialise the GPU before its own program starts, so
+    under a profiler the benchmark starts no helper programs."""
+    pre = os.environ.get("LD_PRELOAD", "")
+    return "rocprof" in pre or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def amd_smi_sample():
     """Socket power (W), mean graphics clock and memory clock (MHz) from
-    `amd-smi metric -p -c --json`, or None where the tool is not there."""
+    `amd-smi metric -p -c --json`, or None where the tool is not there (or
+    under a profiler, see under_profiler)."""
     import shutil
     import subprocess
+    if under_profiler():
+        return None
     exe = shutil.which("amd-smi")
     if not exe:
         return None

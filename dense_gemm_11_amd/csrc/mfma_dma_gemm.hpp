@@ -167,10 +167,14 @@ struct Layout {
     // XOR for row k of an [k][mn] tile: bf16 rows are read 4 at a time by the
     // transposing reads (table above); fp32 rows are read by 32-bit reads in
     // which the two half-waves take rows 4 apart, so rows with bit 2 of k set
-    // move to the other 128-byte half of each 256-byte window.
+    // move to the other 128-byte half of each 256-byte window.  With 16-wide
+    // fragments the two 16-lane groups of a half-wave read the same chunks of
+    // rows 8 apart (32-wide ones read chunks 2 apart of the same rows), so
+    // rows with bit 3 of k set also swap chunk pairs (XOR 2), which puts the
+    // two groups in one 256-byte window as with 32-wide fragments.
     __host__ __device__ static constexpr int mswz(int k)
     {
-        if constexpr (Cfg::ES == 2) return mn_swz(k);
+        if constexpr (Cfg::ES == 2) return mn_swz(k) ^ (Cfg::FM == 16 ? ((k >> 3) & 1) << 1 : 0);
         else return ((k >> 2) & 1) << 3;
     }
     // XOR for row mn of an [mn][k] tile.  A fragment read covers 32 (or 16)

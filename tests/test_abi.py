@@ -300,3 +300,17 @@ def test_selection_queries_from_many_threads_agree():
     for t in threads:
         t.join()
     assert not errors, errors[:5]
+
+
+def test_bench_starts_no_helper_under_a_profiler(monkeypatch):
+    """Under rocprofv3 (its library preloaded) bench.py must not start amd-smi:
+    the child would inherit the preload and initialise the GPU before its own
+    interpreter starts."""
+    import bench
+    monkeypatch.delenv("LD_PRELOAD", raising=False)
+    for k in [k for k in os.environ if k.startswith("ROCPROF")]:
+        monkeypatch.delenv(k)
+    assert not bench.under_profiler()
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
+    assert bench.under_profiler()
+    assert bench.amd_smi_sample() is None
