@@ -470,8 +470,9 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             }
         }
     }
-    // bf16 operands, fp32 output, whole tiles: tile shapes beyond the two
-    // square ones, from measurements on MI355X (us, one box, automatic
+    // bf16 operands, whole tiles, fp32 output (bf16 output too where the
+    // variant carries it): tile shapes beyond the two square ones, from
+    // measurements on MI355X with fp32 output (us, one box, automatic
     // choice before -> after):
     //  * K <= 1024 with at least a full wave of 256x256 tiles: 128x256 tiles,
     //    two workgroups per compute unit, so one's prologue and epilogue hide
@@ -487,19 +488,23 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     //    8-wave 256x256 kernel (3072^3 76.5 -> 58.6; 4093x2051x1537 A^T B
     //    58.5 -> 50.1).
     bool untransposed = false;  // an NN call that keeps its orientation
-    if (sk == 0 && c.forced < 0 && aligned && !c.epi && !out_bf16 &&
-        op_dtype == GEMM_DTYPE_BF16_F32) {
+    // a variant serves the call's output type (bf16 output: its own launches)
+    auto serves = [&](const Variant& x) { return !out_bf16 || x.bo_nn_t_fn != nullptr; };
+    if (sk == 0 && c.forced < 0 && aligned && !c.epi && op_dtype == GEMM_DTYPE_BF16_F32) {
         static const int wide_tile = find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late");
         const int64_t cus = device_cus();
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
         const int64_t t12 = ceil_div(M, 128) * ceil_div(N, 256);
         const int big_id = dma_variant(GEMM_DTYPE_BF16_F32, true);
-        if (wide_tile >= 0 && K <= 1024 && t256 >= cus &&
-            dma_offsets_fit(table()[wide_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
+        const bool wide_ok = wide_tile >= 0 && serves(table()[wide_tile]) &&
+                             dma_offsets_fit(table()[wide_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        // (with bf16 output, whose stores weigh half as much, only from four
+        // waves of 256x256 tiles: 8192x4096x512 0.0433 -> 0.0446 ms on
+        // 128x256 tiles, 16384x4096x512 0.0795 -> 0.0761)
+        if (wide_ok && K <= 1024 && t256 >= (out_bf16 ? 4 : 1) * cus) {
             id = wide_tile;
         } else if (4 * t256 < 3 * cus) {
-            if (wide_tile >= 0 && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus &&
-                dma_offsets_fit(table()[wide_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
+            if (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus)
                 id = wide_tile;
             else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) &&
                      dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
@@ -525,7 +530,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             int64_t best_w = NONE;
             bool best_pref = false;
             for (int vi = 0; vi < 2; ++vi) {
-                if (w192[vi] < 0) continue;
+                if (w192[vi] < 0 || !serves(table()[w192[vi]])) continue;
                 const Variant& vv = table()[w192[vi]];
                 for (int tr = 0; tr < 2; ++tr) {
                     const bool ok = tr ? (c.a_kc && !c.b_kc && vv.nn_t_fn &&

@@ -7,24 +7,28 @@
 // LDS as 256 wide (the padding is never read).  Both have a transposed-output
 // instantiation, so an NN problem (run as D^T = B^T A^T) can put the 192 side
 // on either dimension.
-#include "mfma_dma_gemm.hpp"
+#include "tile_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
-using Dma192x256s3L = DmaConfig<MFMA_BF16_32x32x16, 192, 256, 32, 2, 4, 3, true, PAIR_BOTH_KC>;
-using Dma256x192s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 192, 32, 4, 2, 3, true, PAIR_BOTH_KC>;
-
-#define BF16_DMA_T_VARIANT(NAME, CFG)                                                        \
+// plain and transposed-output launches here, bf16-output ones (table W of
+// bf16_out_fns_tile) in inst_bf16_dma_out_tiles.hip
+#define BF16_DMA_T_VARIANT(NAME, CFG, W)                                                     \
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, CFG::S, \
      CFG::AHEAD, DG_FN_TABLE(dma_gemm_kernel, CFG), {{nullptr, nullptr}, {nullptr, nullptr}},  \
-     nullptr, DG_NN_T_FN(dma_gemm_kernel, CFG)}
+     nullptr, DG_NN_T_FN(dma_gemm_kernel, CFG),                                               \
+     {{{bf16_out_fns_tile(W).fn[0][0][0], bf16_out_fns_tile(W).fn[0][0][1]},                  \
+       {bf16_out_fns_tile(W).fn[0][1][0], bf16_out_fns_tile(W).fn[0][1][1]}},                 \
+      {{bf16_out_fns_tile(W).fn[1][0][0], bf16_out_fns_tile(W).fn[1][0][1]},                  \
+       {bf16_out_fns_tile(W).fn[1][1][0], bf16_out_fns_tile(W).fn[1][1][1]}}},                \
+     bf16_out_fns_tile(W).nn_t}
 
 const Variant* bf16dma_192_variant_table(int* count)
 {
     static const Variant table[] = {
-        BF16_DMA_T_VARIANT("bf16_dma32x32x16_192x256x32_w2x4_s3_late", Dma192x256s3L),
-        BF16_DMA_T_VARIANT("bf16_dma32x32x16_256x192x32_w4x2_s3_late", Dma256x192s3L),
+        BF16_DMA_T_VARIANT("bf16_dma32x32x16_192x256x32_w2x4_s3_late", Dma192x256s3L, 1),
+        BF16_DMA_T_VARIANT("bf16_dma32x32x16_256x192x32_w4x2_s3_late", Dma256x192s3L, 2),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -11,14 +11,12 @@
 //  * the 16x16x32 bf16 instruction on 128x128 tiles with 64-deep steps (a
 //    step then holds two fragment steps), against the 32x32x16 sweep variant
 //    of the same tile, depth and stage count.
-#include "mfma_dma_gemm.hpp"
+#include "tile_configs.hpp"
 #include "variants.hpp"
 
 namespace dg {
 
 // two waves per SIMD: the register budget capped at 256 per lane
-using Dma256x128s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 128, 32, 2, 2, 3, true, PAIR_NONE, 2>;
-using Dma128x256s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 256, 32, 2, 2, 3, true, PAIR_NONE, 2>;
 using Dma256w4x2s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 4, 2, 3, true, PAIR_BOTH_KC>;
 using Dma256w2x4s4L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 32, 2, 4, 4, true, PAIR_BOTH_KC>;
 using Dma256w2x4k64s2L = DmaConfig<MFMA_BF16_32x32x16, 256, 256, 64, 2, 4, 2, true>;
@@ -33,7 +31,17 @@ const Variant* bf16dma_tile_variant_table(int* count)
 {
     static const Variant table[] = {
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x128x32_w2x2_s3_late", Dma256x128s3L),
-        BF16_DMA_VARIANT("bf16_dma32x32x16_128x256x32_w2x2_s3_late", Dma128x256s3L),
+        // with bf16-output instantiations (no transposed-output one: NN keeps
+        // its orientation on this tile)
+        {"bf16_dma32x32x16_128x256x32_w2x2_s3_late", 1, KIND_MFMA_DMA, Dma128x256s3L::BM,
+         Dma128x256s3L::BN, Dma128x256s3L::BK, Dma128x256s3L::THREADS, Dma128x256s3L::LDS_BYTES,
+         Dma128x256s3L::S, Dma128x256s3L::AHEAD, DG_FN_TABLE(dma_gemm_kernel, Dma128x256s3L),
+         {{nullptr, nullptr}, {nullptr, nullptr}}, nullptr, nullptr,
+         {{{bf16_out_fns_tile(0).fn[0][0][0], bf16_out_fns_tile(0).fn[0][0][1]},
+           {bf16_out_fns_tile(0).fn[0][1][0], bf16_out_fns_tile(0).fn[0][1][1]}},
+          {{bf16_out_fns_tile(0).fn[1][0][0], bf16_out_fns_tile(0).fn[1][0][1]},
+           {bf16_out_fns_tile(0).fn[1][1][0], bf16_out_fns_tile(0).fn[1][1][1]}}},
+         bf16_out_fns_tile(0).nn_t},
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w4x2_s3_late", Dma256w4x2s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x4_s4_late", Dma256w2x4s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x4_s2_late", Dma256w2x4k64s2L),

@@ -83,6 +83,8 @@ struct Bf16OutFns {
     LaunchFn nn_t;
 };
 const Bf16OutFns& bf16_out_fns(int bm);
+// ... and of the non-square tiles: 0 = 128x256, 1 = 192x256, 2 = 256x192.
+const Bf16OutFns& bf16_out_fns_tile(int which);
 
 // Table fragments, one per instantiation file (host functions returning a
 // static array, so the device compile never sees host function pointers).

@@ -189,3 +189,29 @@ def test_bf16_output_as_stream_k(sk_handle):
     assert g.gemm_last_stream_k(h) > 1
     rows, cols = workloads.sample_indices(M, N, 5311)
     assert check("N", "N", M, N, K, 1.0, 0.0, A, B, None, D, rows=rows, cols=cols) <= 1.0
+
+
+TILE_CASES = [
+    # transA, transB, M, N, K, alpha, beta, expected tile
+    ("N", "N", 16384, 4096, 512, 1.0, 0.0, "128x256x32"),    # short K: two per CU
+    ("N", "N", 8192, 1536, 2048, 1.0, 0.0, "192x256x32"),    # NN as D^T, 192 along N
+    ("N", "T", 8192, 1536, 2048, 1.0, 0.5, "256x192x32"),    # 192 along N as stored
+    ("T", "N", 4093, 2051, 1537, 0.5, 1.5, "192x256x32"),    # misaligned rows, ragged
+]
+
+
+@pytest.mark.parametrize("c", TILE_CASES, ids=lambda c: f"{c[0]}{c[1]}_{c[2]}x{c[3]}x{c[4]}")
+def test_bf16_output_on_shape_selected_tiles(sk_handle, c):
+    """bf16 output on the non-square tiles the selector takes by shape
+    (128x256, 192x256 as stored and as D^T, 256x192), sampled on 64 x 64
+    outputs including the first and last rows and columns."""
+    import dense_gemm_11_amd as g
+    ta, tb, M, N, K, alpha, beta, tile = c
+    announce("bf16-out tile", c)
+    A, B, C = case(ta, tb, M, N, K, 7000 + K, with_c=beta != 0)
+    D, _ = run_bf16_out(sk_handle, ta, tb, M, N, K, alpha, beta, A, B, C)
+    assert tile in g.gemm_variant_name(g.gemm_last_variant(sk_handle))
+    rows, cols = workloads.sample_indices(M, N, 17 + K)
+    err = check(ta, tb, M, N, K, alpha, beta, A, B, C, D, rows=rows, cols=cols)
+    print(f"[result] bf16-out {ta}{tb} {M}x{N}x{K} max_err={err:.3e}", flush=True)
+    assert err <= 1.0

@@ -31,8 +31,13 @@ CASES = [
     # 576 tiles of 128x128, aligned, short K: one round at 3 workgroups per CU
     ("bf16", "N", "N", 3000, 3000, 512, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
     ("bf16", "T", "N", 4096, 2176, 1536, 1.5, False, P + "128x128x32_w2x2_s2_late", False),
-    # ... but not with bf16 output, which only the 4-stage variant carries
-    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, True, P + "128x128x32_w2x2_s4_late", False),
+    # the misaligned 4093x2051x1537 with bf16 output: a 192-wide tile, which
+    # carries bf16 output (the 2-stage 128x128 variant does not)
+    ("bf16", "T", "N", 4093, 2051, 1537, 1.5, True, P + "192x256x32_w2x4_s3_late", False),
+    # bf16 output on the other shape-selected tiles
+    ("bf16", "N", "N", 16384, 4096, 512, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "N", "N", 8192, 4096, 512, 0.0, True, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "N", 8192, 1536, 4096, 0.0, True, P + "192x256x32_w2x4_s3_late", False),
     # at most one tile per CU: the 4-stage ring
     ("bf16", "N", "N", 2048, 2048, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     # more 128x128 tiles than CUs, at most 2 per CU, a k-contiguous operand:
