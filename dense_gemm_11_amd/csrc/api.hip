@@ -500,15 +500,27 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                              dma_offsets_fit(table()[wide_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
         // (with bf16 output, whose stores weigh half as much, only from four
         // waves of 256x256 tiles: 8192x4096x512 0.0433 -> 0.0446 ms on
-        // 128x256 tiles, 16384x4096x512 0.0795 -> 0.0761)
-        if (wide_ok && K <= 1024 && t256 >= (out_bf16 ? 4 : 1) * cus) {
+        // 128x256 tiles, 16384x4096x512 0.0795 -> 0.0761).  Both operands
+        // k-contiguous (NT): 128x256 copies them half a line per step while
+        // the square tiles pair the copies, so 128x256 only for K <= 512
+        // (NT 8192x4096x1024 0.0766 vs 0.0742 ms on 256x256, 8192x2048x1024
+        // 0.0409 vs 0.0375), none of the long-K rule (the paired 128x128
+        // ring wins: NT 4096x2048x4096 0.0710 vs 0.0660, 8192x1024x4096
+        // 0.0699 vs 0.0647), and 256x256 (or, below, a 192-wide tile) from
+        // more than half a wave of 256x256 tiles and K >= 1024 (NT 3072^2 x
+        // 1024 0.0305 on 128x128 vs 0.0261 on 256x192).
+        const bool both_kc = c.a_kc && c.b_kc;
+        const bool big_fits = dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus) {
             id = wide_tile;
         } else if (4 * t256 < 3 * cus) {
-            if (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus)
+            if (both_kc) {
+                if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
+            } else if (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus) {
                 id = wide_tile;
-            else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) &&
-                     dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
+            } else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) && big_fits) {
                 id = big_id;
+            }
         }
         // Tiles with a 192-wide side (192x256, 256x192) where they fill whole
         // waves of compute units that 256x256 tiles leave partly empty: a

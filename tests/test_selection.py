@@ -43,6 +43,13 @@ CASES = [
     # more 128x128 tiles than CUs, at most 2 per CU, a k-contiguous operand:
     # paired copies
     ("bf16", "N", "T", 2304, 2304, 2304, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    # both operands k-contiguous: the paired 128x128 ring where 128x256 tiles
+    # would fill a wave with a long K, 256x256 at K = 1024 over a full wave,
+    # 128x256 only for K <= 512, a 192-wide tile over half a wave
+    ("bf16", "N", "T", 4096, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    ("bf16", "N", "T", 8192, 2048, 1024, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "T", 8192, 4096, 512, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "N", "T", 3072, 3072, 1024, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
     # long K, 128x256 tiles filling 3/4 to 1 of a wave: 128x256
     ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
     ("bf16", "T", "N", 4096, 2048, 4096, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
