@@ -651,6 +651,88 @@ def power_sweep(g, h, seconds: float = 3.0) -> dict:
             "rows": rows}
 
 
+SELECTOR_CANDIDATES = ["bf16_dma32x32x16_256x256x32_w2x4_s3_late",
+                       "bf16_dma32x32x16_128x128x32_w2x2_s4_late",
+                       "bf16_dma32x32x16_128x128x32_w2x2_s2_late",
+                       "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair",
+                       "bf16_dma32x32x16_128x256x32_w2x2_s3_late",
+                       "bf16_dma32x32x16_256x128x32_w2x2_s3_late",
+                       "bf16_dma32x32x16_192x256x32_w2x4_s3_late",
+                       "bf16_dma32x32x16_256x192x32_w4x2_s3_late"]
+
+
+def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 4096),
+                   layouts=("TN", "NT")) -> dict:
+    """The automatic choice against every whole-tile bf16 candidate, forced,
+    on a grid of shapes (fp32 output, N(0,1) operands).  TN and NT only: a
+    forced variant runs as stored, while NN calls may run as D^T, so an NN
+    comparison with forced variants would not be like for like.  Each
+    candidate is timed, then the automatic choice, then the fastest candidate
+    and the automatic choice again (best of the two each), so neither side
+    pays the clock's warm-up."""
+    names = {name: i for i, name, _, _ in g.variants()}
+
+    def best_ms(run, reps=10):
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / reps)
+        return best
+
+    rows = []
+    for lay in layouts:
+        ta, tb = lay[0], lay[1]
+        for M in dims:
+            for N in dims:
+                for K in ks:
+                    A = torch.randn((M, K) if ta == "N" else (K, M), device="cuda").to(torch.bfloat16)
+                    B = torch.randn((K, N) if tb == "N" else (N, K), device="cuda").to(torch.bfloat16)
+                    D = torch.empty(M, N, device="cuda")
+
+                    def run():
+                        st = g.run_tensors(h, A, B, D, transA=ta, transB=tb, check=False)
+                        if st != g.GEMM_OK:
+                            raise RuntimeError(g.gemm_status_string(st))
+
+                    times = {}
+                    for c in SELECTOR_CANDIDATES:
+                        g.gemm_set_variant(h, names[c])
+                        g.gemm_set_stream_k(h, 0)
+                        times[c] = best_ms(run)
+                    g.gemm_set_variant(h, -1)
+                    g.gemm_set_stream_k(h, -1)
+                    auto = best_ms(run)
+                    chosen = g.gemm_variant_name(g.gemm_last_variant(h))
+                    sk = g.gemm_last_stream_k(h)
+                    b0 = min(times, key=times.get)
+                    g.gemm_set_variant(h, names[b0])
+                    g.gemm_set_stream_k(h, 0)
+                    times[b0] = min(times[b0], best_ms(run))
+                    g.gemm_set_variant(h, -1)
+                    g.gemm_set_stream_k(h, -1)
+                    auto = min(auto, best_ms(run))
+                    best = min(times, key=times.get)
+                    rows.append({"layout": lay, "M": M, "N": N, "K": K, "auto_ms": round(auto, 4),
+                                 "auto_variant": chosen, "stream_k": sk,
+                                 "best_ms": round(times[best], 4), "best_variant": best,
+                                 "ratio": round(auto / times[best], 3)})
+                    print(f"[select] {rows[-1]}", file=sys.stderr, flush=True)
+                    del A, B, D
+    torch.cuda.empty_cache()
+    r = [x["ratio"] for x in rows]
+    return {"rows": rows, "shapes": len(rows), "within_5pct": sum(1 for x in r if x <= 1.05),
+            "worst_ratio": max(r) if r else None}
+
+
 def trace_summary(trace_csv: str, stats_csv: str, warmup: int, steps: int) -> int:
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of this
     benchmark: rocprofv3's own per-kernel statistics, and for each step kernel
@@ -717,6 +799,9 @@ def main(argv=None):
     ap.add_argument("--pipeline-sweep", action="store_true",
                     help="time every direct-to-LDS variant on the NN step shapes, fit the "
                          "pipeline-depth model, print one JSON object, then exit")
+    ap.add_argument("--selector-check", action="store_true",
+                    help="time the automatic choice against every whole-tile bf16 candidate "
+                         "on a grid of TN and NT shapes, print one JSON object, then exit")
     ap.add_argument("--power-sweep", action="store_true",
                     help="run bf16 8192^3 kernels back to back and record clock, power and "
                          "rate for each, print one JSON object, then exit")
@@ -746,6 +831,13 @@ def main(argv=None):
         return 0
     if args.power_sweep:
         print(json.dumps(power_sweep(g, h)), flush=True)
+        g.gemm_destroy(h)
+        return 0
+    if args.selector_check:
+        workspace = g.attach_workspace(h)
+        print(json.dumps(selector_check(g, h)), flush=True)
+        g.gemm_set_workspace(h, None, 0, None)
+        del workspace
         g.gemm_destroy(h)
         return 0
     if args.vector_fma_only:
