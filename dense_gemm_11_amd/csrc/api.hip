@@ -411,6 +411,26 @@ const LaunchFn (*sk_launchers(const Variant& x, int op_dtype, bool out_bf16, boo
     return f ? f->fn : nullptr;
 }
 
+// Fused-epilogue launches of variant `id` for the call's operand and output
+// types, or null where the variant carries none (the selected square
+// direct-to-LDS variants and the non-square bf16 tiles do).
+const EpiFns* epi_fns_for(int id, int op_dtype, bool out_bf16)
+{
+    if (id < 0) return nullptr;
+    const Variant& v = table()[id];
+    if (id == dma_variant(op_dtype, v.bm == 256))
+        return op_dtype == GEMM_DTYPE_F32 ? epi_fns_f32(v.bm)
+               : out_bf16                 ? epi_fns_bf16_out(v.bm)
+                                          : epi_fns_bf16(v.bm);
+    if (op_dtype != GEMM_DTYPE_BF16_F32) return nullptr;
+    static const int tiles[3] = {find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late"),
+                                 find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late"),
+                                 find_variant("bf16_dma32x32x16_256x192x32_w4x2_s3_late")};
+    for (int w = 0; w < 3; ++w)
+        if (id == tiles[w]) return out_bf16 ? epi_fns_tile_bf16out(w) : epi_fns_tile_f32out(w);
+    return nullptr;
+}
+
 // The whole host choice for a call, shared by gemm_run and
 // gemm_select_variant.  Returns GEMM_OK or why the call cannot run.
 gemm_status_t plan_call(const CallDesc& c, Plan& pl)
@@ -488,9 +508,13 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     //    8-wave 256x256 kernel (3072^3 76.5 -> 58.6; 4093x2051x1537 A^T B
     //    58.5 -> 50.1).
     bool untransposed = false;  // an NN call that keeps its orientation
-    // a variant serves the call's output type (bf16 output: its own launches)
-    auto serves = [&](const Variant& x) { return !out_bf16 || x.bo_nn_t_fn != nullptr; };
-    if (sk == 0 && c.forced < 0 && aligned && !c.epi && op_dtype == GEMM_DTYPE_BF16_F32) {
+    // a variant serves the call's output type and epilogue (bf16 output and
+    // the fused epilogue: launches of its own)
+    auto serves = [&](const Variant& x) {
+        return (!out_bf16 || x.bo_nn_t_fn != nullptr) &&
+               (!c.epi || epi_fns_for((int)(&x - table().data()), op_dtype, out_bf16) != nullptr);
+    };
+    if (sk == 0 && c.forced < 0 && aligned && op_dtype == GEMM_DTYPE_BF16_F32) {
         static const int wide_tile = find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late");
         const int64_t cus = device_cus();
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
@@ -596,14 +620,12 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     const bool nn_t = sk == 0 && c.forced < 0 && !untransposed && vr.nn_t_fn && aligned &&
                       c.a_kc && !c.b_kc && dma_offsets_fit(vr, false, true, K, c.ldb, c.lda, es);
     if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
-    // fused epilogue: only the selected direct-to-LDS variants, whole tiles
-    // and wide access, carry it
+    // fused epilogue: only the selected direct-to-LDS variants and the
+    // non-square bf16 tiles, whole tiles and wide access, carry it
     const EpiFns* ef = nullptr;
     if (c.epi) {
-        if (!aligned || id != dma_variant(op_dtype, vr.bm == 256)) return GEMM_ERR_NOT_SUPPORTED;
-        ef = op_dtype == GEMM_DTYPE_F32 ? epi_fns_f32(vr.bm)
-             : out_bf16                 ? epi_fns_bf16_out(vr.bm)
-                                        : epi_fns_bf16(vr.bm);
+        if (!aligned) return GEMM_ERR_NOT_SUPPORTED;
+        ef = epi_fns_for(id, op_dtype, out_bf16);
         if (!ef) return GEMM_ERR_NOT_SUPPORTED;
     }
     pl.id = id;

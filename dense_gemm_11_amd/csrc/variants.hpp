@@ -42,6 +42,10 @@ struct EpiFns {
 const EpiFns* epi_fns_f32(int bm);
 const EpiFns* epi_fns_bf16(int bm);
 const EpiFns* epi_fns_bf16_out(int bm);
+// ... and of the non-square tiles (0 = 128x256, 1 = 192x256, 2 = 256x192),
+// with fp32 or bf16 C and D.
+const EpiFns* epi_fns_tile_f32out(int which);
+const EpiFns* epi_fns_tile_bf16out(int which);
 
 // Stream-K instantiations with bf16 output or the fused epilogue (the
 // partial sums stay fp32): [A k-contiguous][B k-contiguous].

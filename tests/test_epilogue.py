@@ -234,3 +234,29 @@ def test_epilogue_as_stream_k(g, sk_handle, dtype):
     err, tol = check(dtype, "N", "N", M, N, K, 1.0, 0.0, A, B, None, bias, ACTS["gelu"], None, D,
                      rows=rows, cols=cols)
     assert err <= tol
+
+
+TILE_CASES = [
+    # transA, transB, M, N, K, alpha, beta, expected tile
+    ("N", "N", 16384, 4096, 512, 1.0, 0.0, "128x256x32"),
+    ("N", "N", 8192, 1536, 2048, 1.0, 0.5, "192x256x32"),   # NN as D^T
+    ("N", "T", 8192, 1536, 2048, 0.5, 0.0, "256x192x32"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16_f32", "bf16_bf16"])
+@pytest.mark.parametrize("c", TILE_CASES, ids=lambda c: f"{c[0]}{c[1]}_{c[2]}x{c[3]}x{c[4]}")
+def test_epilogue_on_shape_selected_tiles(g, handle, dtype, c):
+    """bias + GELU + clamp fused into the non-square tiles the selector takes
+    by shape (128x256, 192x256 as D^T, 256x192), sampled outputs including
+    the first and last rows and columns."""
+    ta, tb, M, N, K, alpha, beta, tile = c
+    A, B, C, bias, out = make(dtype, ta, tb, M, N, K, 7400 + K, beta != 0.0)
+    announce("epilogue tile", dtype, c)
+    D = run(g, handle, ta, tb, alpha, beta, A, B, C, bias, ACTS["gelu"], (-0.5, 3.0), out, M, N)
+    assert tile in g.gemm_variant_name(g.gemm_last_variant(handle))
+    rows, cols = workloads.sample_indices(M, N, 7400 + M % 101)
+    err, tol = check(dtype, ta, tb, M, N, K, alpha, beta, A, B, C, bias, ACTS["gelu"],
+                     (-0.5, 3.0), D, rows=rows, cols=cols)
+    print(f"[result] epilogue tile {dtype} {ta}{tb} {M}x{N}x{K} err={err:.3e}", flush=True)
+    assert err <= tol
