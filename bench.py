@@ -724,7 +724,8 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                     rows.append({"layout": lay, "M": M, "N": N, "K": K, "auto_ms": round(auto, 4),
                                  "auto_variant": chosen, "stream_k": sk,
                                  "best_ms": round(times[best], 4), "best_variant": best,
-                                 "ratio": round(auto / times[best], 3)})
+                                 "ratio": round(auto / times[best], 3),
+                                 "times": {c[17:]: round(t, 4) for c, t in times.items()}})
                     print(f"[select] {rows[-1]}", file=sys.stderr, flush=True)
                     del A, B, D
     torch.cuda.empty_cache()
@@ -802,6 +803,8 @@ def main(argv=None):
     ap.add_argument("--selector-check", action="store_true",
                     help="time the automatic choice against every whole-tile bf16 candidate "
                          "on a grid of TN and NT shapes, print one JSON object, then exit")
+    ap.add_argument("--selector-ks", default="1024,4096",
+                    help="comma-separated K values of the --selector-check grid")
     ap.add_argument("--power-sweep", action="store_true",
                     help="run bf16 8192^3 kernels back to back and record clock, power and "
                          "rate for each, print one JSON object, then exit")
@@ -835,7 +838,8 @@ def main(argv=None):
         return 0
     if args.selector_check:
         workspace = g.attach_workspace(h)
-        print(json.dumps(selector_check(g, h)), flush=True)
+        ks = tuple(int(k) for k in args.selector_ks.split(","))
+        print(json.dumps(selector_check(g, h, ks=ks)), flush=True)
         g.gemm_set_workspace(h, None, 0, None)
         del workspace
         g.gemm_destroy(h)

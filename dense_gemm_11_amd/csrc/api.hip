@@ -535,8 +535,41 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // 1024 0.0305 on 128x128 vs 0.0261 on 256x192).
         const bool both_kc = c.a_kc && c.b_kc;
         const bool big_fits = dma_offsets_fit(table()[big_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
-        if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus) {
+        // Short K, fp32 output (the D write is most of the traffic): 128x256
+        // tiles only where their rounds at two per compute unit come out
+        // nearly whole (at least 9/10 full for K <= 256, 3/4 for K <= 512),
+        // the 128x128 rings elsewhere from three quarters of a wave of
+        // 256x256 tiles; and with both operands k-contiguous and K below
+        // 1024, the 128x128 rings (paired) over more than a wave of 256x256
+        // tiles whose last wave is less than 9/10 full.  From every whole-tile
+        // candidate timed on 36 shapes (M, N in 1024 .. 8192) per K and layout
+        // (TN, NT; ms, one box, automatic choice before -> 128x128 rings):
+        // TN 6144x3072x256 0.0261 (128x256; 288 tiles of 256x256, so its
+        // rounds are 9/16 full) -> 0.0206-0.0222, TN 3072x4096x256 0.0169
+        // (256x256, 192 tiles) -> 0.0145-0.0152, NT 6144x2048x512 0.0217 ->
+        // 0.0193 (paired), NT 6144x3072x768 0.0520 (256x256) -> 0.0413
+        // (paired); mean ratio to the fastest candidate 1.066 -> 1.038 at
+        // K = 256, 1.034 -> 1.026 at 512, 1.040 -> 1.027 at 768.
+        const auto rounds_at_least = [&](int64_t tiles, int64_t per_cu, int num, int den) {
+            const int64_t slots = per_cu * cus;
+            return den * tiles >= num * ceil_div(tiles, slots) * slots;
+        };
+        const int mid_id = dma_variant(GEMM_DTYPE_BF16_F32, false);
+        const bool mid_ok = serves(table()[mid_id]) &&
+                            dma_offsets_fit(table()[mid_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        // (measured with fp32 output and 16-byte aligned rows; other calls
+        // keep the rules below)
+        const bool measured = !out_bf16 && c.rows16;
+        const bool wide_rounds = K > 512 || !measured ||
+                                 rounds_at_least(t12, 2, K <= 256 ? 9 : 3, K <= 256 ? 10 : 4);
+        if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus &&
+            wide_rounds) {
             id = wide_tile;
+        } else if (measured && K <= 512 && 4 * t256 >= 3 * cus && mid_ok) {
+            id = mid_id;
+        } else if (measured && both_kc && K < 1024 && t256 > cus &&
+                   !rounds_at_least(t256, 1, 9, 10) && mid_ok) {
+            id = mid_id;
         } else if (4 * t256 < 3 * cus) {
             if (both_kc) {
                 if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
@@ -601,7 +634,8 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     if (sk == 0 && c.forced < 0 && aligned && !c.epi && !out_bf16 &&
         id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
         static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
-        if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < dp_us) id = s2;
+        if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < data_parallel_us(table()[id], M, N, K))
+            id = s2;
         // Otherwise, with a k-contiguous operand and more tiles than compute
         // units (two workgroups on a unit hide the latency of the larger
         // copies), the 4-stage ring copying that operand two K-steps at a

@@ -60,6 +60,21 @@ CASES = [
     # N) fill the wave that 256x256 tiles fill three quarters of
     ("bf16", "N", "N", 8192, 1536, 1024, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
     ("bf16", "N", "N", 8192, 1536, 4096, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
+    # short K (fp32 output, aligned rows): 128x256 only where its rounds at
+    # two per CU come out nearly whole (4096x8192: 1024 tiles, two whole
+    # rounds; 6144^2 x 512: 1152, 3/4 of the last round), the 128x128 rings
+    # elsewhere from 3/4 of a wave of 256x256 tiles (6144x3072: 576 tiles of
+    # 128x256, the second round 1/8 full; 3072x4096: 192 tiles of 256x256)
+    ("bf16", "T", "N", 4096, 8192, 256, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "N", 6144, 6144, 512, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "N", 6144, 3072, 256, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "T", "N", 3072, 4096, 256, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
+    ("bf16", "N", "T", 3072, 6144, 256, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    # both operands k-contiguous, K below 1024: the paired 128x128 ring over
+    # more than a wave of 256x256 tiles whose last wave is partly empty
+    # (288 tiles), 256x256 where its waves are whole (512 tiles)
+    ("bf16", "N", "T", 6144, 3072, 768, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    ("bf16", "N", "T", 8192, 4096, 768, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]
