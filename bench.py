@@ -662,14 +662,16 @@ SELECTOR_CANDIDATES = ["bf16_dma32x32x16_256x256x32_w2x4_s3_late",
 
 
 def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 4096),
-                   layouts=("TN", "NT")) -> dict:
+                   layouts=("TN", "NT"), out_bf16: bool = False) -> dict:
     """The automatic choice against every whole-tile bf16 candidate, forced,
     on a grid of shapes (fp32 output, N(0,1) operands).  TN and NT only: a
     forced variant runs as stored, while NN calls may run as D^T, so an NN
     comparison with forced variants would not be like for like.  Each
     candidate is timed, then the automatic choice, then the fastest candidate
     and the automatic choice again (best of the two each), so neither side
-    pays the clock's warm-up."""
+    pays the clock's warm-up.  With out_bf16, D is bf16 and the candidates
+    are those that carry a bf16-output epilogue (a forced variant without
+    one is refused as not supported and left out)."""
     names = {name: i for i, name, _, _ in g.variants()}
 
     def best_ms(run, reps=10):
@@ -696,7 +698,8 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                 for K in ks:
                     A = torch.randn((M, K) if ta == "N" else (K, M), device="cuda").to(torch.bfloat16)
                     B = torch.randn((K, N) if tb == "N" else (N, K), device="cuda").to(torch.bfloat16)
-                    D = torch.empty(M, N, device="cuda")
+                    D = torch.empty(M, N, device="cuda",
+                                    dtype=torch.bfloat16 if out_bf16 else torch.float32)
 
                     def run():
                         st = g.run_tensors(h, A, B, D, transA=ta, transB=tb, check=False)
@@ -707,6 +710,9 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                     for c in SELECTOR_CANDIDATES:
                         g.gemm_set_variant(h, names[c])
                         g.gemm_set_stream_k(h, 0)
+                        st = g.run_tensors(h, A, B, D, transA=ta, transB=tb, check=False)
+                        if st == g.GEMM_ERR_NOT_SUPPORTED:
+                            continue
                         times[c] = best_ms(run)
                     g.gemm_set_variant(h, -1)
                     g.gemm_set_stream_k(h, -1)
@@ -805,6 +811,8 @@ def main(argv=None):
                          "on a grid of TN and NT shapes, print one JSON object, then exit")
     ap.add_argument("--selector-ks", default="1024,4096",
                     help="comma-separated K values of the --selector-check grid")
+    ap.add_argument("--selector-out", choices=("f32", "bf16"), default="f32",
+                    help="output type of the --selector-check calls")
     ap.add_argument("--power-sweep", action="store_true",
                     help="run bf16 8192^3 kernels back to back and record clock, power and "
                          "rate for each, print one JSON object, then exit")
@@ -839,7 +847,8 @@ def main(argv=None):
     if args.selector_check:
         workspace = g.attach_workspace(h)
         ks = tuple(int(k) for k in args.selector_ks.split(","))
-        print(json.dumps(selector_check(g, h, ks=ks)), flush=True)
+        print(json.dumps(selector_check(g, h, ks=ks, out_bf16=args.selector_out == "bf16")),
+              flush=True)
         g.gemm_set_workspace(h, None, 0, None)
         del workspace
         g.gemm_destroy(h)

@@ -560,6 +560,17 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // (measured with fp32 output and 16-byte aligned rows; other calls
         // keep the rules below)
         const bool measured = !out_bf16 && c.rows16;
+        // bf16 output, K <= 512, aligned rows, from 3/4 to 4 waves of 256x256
+        // tiles (half the D bytes, so the matrix work weighs more): 256x256
+        // where its waves are whole, below one wave the 192-wide search that
+        // follows; otherwise 128x256 where its rounds at two per compute unit
+        // are at least 3/4 full, else the 128x128 ring.  Same grid with bf16
+        // D (ms, one box, 256x256 -> the rule's choice): TN 6144x3072x256
+        // 0.0259 -> 0.0209 (128x128), TN 3072x4096x256 0.0142 -> 0.0124
+        // (192x256), TN 8192x3072x512 0.0366 -> 0.0320 (128x256); mean ratio
+        // to the fastest candidate 1.061 -> 1.015 at K = 256, 1.045 -> 1.013
+        // at 512 (fitted to that run).
+        const bool short_bo = out_bf16 && c.rows16 && K <= 512;
         const bool wide_rounds = K > 512 || !measured ||
                                  rounds_at_least(t12, 2, K <= 256 ? 9 : 3, K <= 256 ? 10 : 4);
         if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus &&
@@ -570,6 +581,14 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         } else if (measured && both_kc && K < 1024 && t256 > cus &&
                    !rounds_at_least(t256, 1, 9, 10) && mid_ok) {
             id = mid_id;
+        } else if (short_bo && 4 * t256 >= 3 * cus && t256 < 4 * cus) {
+            if (t256 < cus || rounds_at_least(t256, 1, 9, 10)) {
+                if (big_fits && serves(table()[big_id])) id = big_id;
+            } else if (wide_ok && rounds_at_least(t12, 2, 3, 4)) {
+                id = wide_tile;
+            } else if (mid_ok) {
+                id = mid_id;
+            }
         } else if (4 * t256 < 3 * cus) {
             if (both_kc) {
                 if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
@@ -594,7 +613,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // -> 0.1723 (256x192), NN 1536x8192x4096 0.0917 -> 0.0867.
         static const int w192[2] = {find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late"),
                                     find_variant("bf16_dma32x32x16_256x192x32_w4x2_s3_late")};
-        if (id == big_id && K >= 1024) {
+        if (id == big_id && (K >= 1024 || (short_bo && t256 < cus))) {
             constexpr int64_t NONE = INT64_MAX / 64;
             int64_t best_w = NONE;
             bool best_pref = false;
