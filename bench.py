@@ -659,10 +659,14 @@ SELECTOR_CANDIDATES = ["bf16_dma32x32x16_256x256x32_w2x4_s3_late",
                        "bf16_dma32x32x16_256x128x32_w2x2_s3_late",
                        "bf16_dma32x32x16_192x256x32_w2x4_s3_late",
                        "bf16_dma32x32x16_256x192x32_w4x2_s3_late"]
+SELECTOR_CANDIDATES_F32 = ["f32_dma32x32x2_256x256x32_w2x2_s2_late",
+                           "f32_dma32x32x2_256x256x16_w2x2_s3_late",
+                           "f32_dma32x32x2_256x256x16_w2x2_s4_late",
+                           "f32_dma32x32x2_128x128x16_w2x2_s3_late"]
 
 
 def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 4096),
-                   layouts=("TN", "NT"), out_bf16: bool = False) -> dict:
+                   layouts=("TN", "NT"), out_bf16: bool = False, f32: bool = False) -> dict:
     """The automatic choice against every whole-tile bf16 candidate, forced,
     on a grid of shapes (fp32 output, N(0,1) operands).  TN and NT only: a
     forced variant runs as stored, while NN calls may run as D^T, so an NN
@@ -671,7 +675,10 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
     and the automatic choice again (best of the two each), so neither side
     pays the clock's warm-up.  With out_bf16, D is bf16 and the candidates
     are those that carry a bf16-output epilogue (a forced variant without
-    one is refused as not supported and left out)."""
+    one is refused as not supported and left out).  With f32, operands and D
+    are fp32 and the candidates are the fp32 whole-tile variants."""
+    candidates = SELECTOR_CANDIDATES_F32 if f32 else SELECTOR_CANDIDATES
+    op_dtype = torch.float32 if f32 else torch.bfloat16
     names = {name: i for i, name, _, _ in g.variants()}
 
     def best_ms(run, reps=10):
@@ -696,8 +703,8 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
         for M in dims:
             for N in dims:
                 for K in ks:
-                    A = torch.randn((M, K) if ta == "N" else (K, M), device="cuda").to(torch.bfloat16)
-                    B = torch.randn((K, N) if tb == "N" else (N, K), device="cuda").to(torch.bfloat16)
+                    A = torch.randn((M, K) if ta == "N" else (K, M), device="cuda").to(op_dtype)
+                    B = torch.randn((K, N) if tb == "N" else (N, K), device="cuda").to(op_dtype)
                     D = torch.empty(M, N, device="cuda",
                                     dtype=torch.bfloat16 if out_bf16 else torch.float32)
 
@@ -707,7 +714,7 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                             raise RuntimeError(g.gemm_status_string(st))
 
                     times = {}
-                    for c in SELECTOR_CANDIDATES:
+                    for c in candidates:
                         g.gemm_set_variant(h, names[c])
                         g.gemm_set_stream_k(h, 0)
                         st = g.run_tensors(h, A, B, D, transA=ta, transB=tb, check=False)
@@ -731,7 +738,7 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                                  "auto_variant": chosen, "stream_k": sk,
                                  "best_ms": round(times[best], 4), "best_variant": best,
                                  "ratio": round(auto / times[best], 3),
-                                 "times": {c[17:]: round(t, 4) for c, t in times.items()}})
+                                 "times": {c.split("_", 2)[2]: round(t, 4) for c, t in times.items()}})
                     print(f"[select] {rows[-1]}", file=sys.stderr, flush=True)
                     del A, B, D
     torch.cuda.empty_cache()
@@ -813,6 +820,8 @@ def main(argv=None):
                     help="comma-separated K values of the --selector-check grid")
     ap.add_argument("--selector-out", choices=("f32", "bf16"), default="f32",
                     help="output type of the --selector-check calls")
+    ap.add_argument("--selector-f32", action="store_true",
+                    help="fp32 operands and the fp32 candidates in --selector-check")
     ap.add_argument("--power-sweep", action="store_true",
                     help="run bf16 8192^3 kernels back to back and record clock, power and "
                          "rate for each, print one JSON object, then exit")
@@ -847,8 +856,8 @@ def main(argv=None):
     if args.selector_check:
         workspace = g.attach_workspace(h)
         ks = tuple(int(k) for k in args.selector_ks.split(","))
-        print(json.dumps(selector_check(g, h, ks=ks, out_bf16=args.selector_out == "bf16")),
-              flush=True)
+        print(json.dumps(selector_check(g, h, ks=ks, out_bf16=args.selector_out == "bf16",
+                                        f32=args.selector_f32)), flush=True)
         g.gemm_set_workspace(h, None, 0, None)
         del workspace
         g.gemm_destroy(h)

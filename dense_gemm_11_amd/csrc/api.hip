@@ -461,6 +461,28 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         id = select_variant(op_dtype, M, N, K,
                             c.wide && dma_offsets_fit(big, c.a_kc, c.b_kc, K, c.lda, c.ldb, es));
     }
+    // fp32 from 3/4 of a wave of 256x256 tiles: 128x128 tiles (three
+    // workgroups per compute unit) for K <= 1024, where they were the fastest
+    // candidate on every shape timed (the D write weighs more and three
+    // resident workgroups spread it), and for longer K where the
+    // data-parallel model gives them less time, i.e. where the 256x256
+    // tiles' last wave would be partly empty while the 128x128 rounds come
+    // out fuller.  Every fp32 whole-tile candidate timed on 36 shapes (M, N
+    // in 1024 .. 8192) per K and layout (TN, NT; ms, one box, 256x256 ->
+    // 128x128): TN 6144^2 x 4096 2.79 -> 2.09 (576 tiles, the third wave
+    // 1/4 full), TN 3072x6144x256 0.137 -> 0.084, TN 8192x3072x1024 0.480
+    // -> 0.366; at long K the model keeps 256x256 on whole waves (4096^3:
+    // 0.933 against 0.932 on 128x128; 8192^2 x 4096).  Mean ratio to the
+    // fastest candidate 1.140 -> 1.000 at K = 256 and 1.052 -> 1.000 at 1024
+    // (128x128 fastest on all 144 shapes), 1.011 -> 1.001 at 4096 (the
+    // model's choices), judged on one run.
+    if (c.forced < 0 && op_dtype == GEMM_DTYPE_F32 && id == dma_variant(GEMM_DTYPE_F32, true)) {
+        const int mid = dma_variant(GEMM_DTYPE_F32, false);
+        if (mid >= 0 && dma_offsets_fit(table()[mid], c.a_kc, c.b_kc, K, c.lda, c.ldb, es) &&
+            (K <= 1024 ||
+             data_parallel_us(table()[mid], M, N, K) < data_parallel_us(table()[id], M, N, K)))
+            id = mid;
+    }
     const Variant& v = table()[id];
     if (v.dtype != op_dtype) return GEMM_ERR_NOT_SUPPORTED;
     // bf16 C/D: only the selected direct-to-LDS variants carry that epilogue,

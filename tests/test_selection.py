@@ -15,6 +15,13 @@ P = "bf16_dma32x32x16_"
 CASES = [
     # dtype, transA, transB, M, N, K, beta, bf16 output, expected variant, stream-K?
     ("f32", "N", "N", 4096, 4096, 4096, 0.0, False, "f32_dma32x32x2_256x256x32_w2x2_s2_late", False),
+    # fp32: 128x128 tiles for K <= 1024 and, at longer K, where 256x256
+    # would leave the last wave partly empty (576 tiles of 256x256); 256x256
+    # on whole waves with a long K
+    ("f32", "N", "N", 6144, 6144, 4096, 0.0, False, "f32_dma32x32x2_128x128x16_w2x2_s3_late", False),
+    ("f32", "T", "N", 3072, 6144, 256, 0.0, False, "f32_dma32x32x2_128x128x16_w2x2_s3_late", False),
+    ("f32", "N", "T", 8192, 8192, 1024, 0.0, False, "f32_dma32x32x2_128x128x16_w2x2_s3_late", False),
+    ("f32", "N", "T", 8192, 8192, 4096, 0.0, False, "f32_dma32x32x2_256x256x32_w2x2_s2_late", False),
     ("bf16", "N", "N", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     ("bf16", "N", "T", 8192, 8192, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     # half a wave of 256x256 tiles and rows that are not 16-byte aligned, or a
