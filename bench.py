@@ -822,6 +822,9 @@ def main(argv=None):
                     help="output type of the --selector-check calls")
     ap.add_argument("--selector-f32", action="store_true",
                     help="fp32 operands and the fp32 candidates in --selector-check")
+    ap.add_argument("--selector-layouts", default="TN,NT",
+                    help="comma-separated layouts of the --selector-check grid (an automatic "
+                         "NN call may run as D^T while a forced candidate runs as stored)")
     ap.add_argument("--power-sweep", action="store_true",
                     help="run bf16 8192^3 kernels back to back and record clock, power and "
                          "rate for each, print one JSON object, then exit")
@@ -857,7 +860,9 @@ def main(argv=None):
         workspace = g.attach_workspace(h)
         ks = tuple(int(k) for k in args.selector_ks.split(","))
         print(json.dumps(selector_check(g, h, ks=ks, out_bf16=args.selector_out == "bf16",
-                                        f32=args.selector_f32)), flush=True)
+                                        f32=args.selector_f32,
+                                        layouts=tuple(args.selector_layouts.split(",")))),
+              flush=True)
         g.gemm_set_workspace(h, None, 0, None)
         del workspace
         g.gemm_destroy(h)

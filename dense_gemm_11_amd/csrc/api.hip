@@ -499,13 +499,18 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                  : 0;
     if (c.forced < 0 && aligned && v.kind == KIND_MFMA_DMA && c.sk_mode != 0) {
         // With a workspace, stream-K on the other tile size competes too; the
-        // lowest estimate wins.
+        // lowest estimate wins.  It has to beat that tile size's own
+        // data-parallel estimate as well as the chosen one's: stream-K over
+        // whole waves of tiles only adds its fix-up (fp32 4096^2 x 256 took
+        // stream-K on 256 tiles of 256x256, one workgroup per tile, at 0.0737
+        // ms against 0.0688 for the chosen 128x128 tiles).
         const int other = dma_variant(op_dtype, v.bm < 256);
         if (other != id && sk_launchers(table()[other], op_dtype, out_bf16, c.epi) &&
             dma_offsets_fit(table()[other], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
             double o_us = 0.0;
+            const double ref_us = std::min(dp_us, data_parallel_us(table()[other], M, N, K));
             const int sk_o =
-                stream_k_grid(table()[other], M, N, K, c.sk_mode, c.ws_bytes, dp_us, &o_us);
+                stream_k_grid(table()[other], M, N, K, c.sk_mode, c.ws_bytes, ref_us, &o_us);
             if (sk_o > 0 && (sk == 0 || o_us < sk_us)) {
                 id = other;
                 sk = sk_o;
