@@ -600,8 +600,25 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         const bool short_bo = out_bf16 && c.rows16 && K <= 512;
         const bool wide_rounds = K > 512 || !measured ||
                                  rounds_at_least(t12, 2, K <= 256 ? 9 : 3, K <= 256 ? 10 : 4);
-        if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus &&
-            wide_rounds) {
+        // Only B k-contiguous (A^T B^T): the 128x256 tile puts its 256-wide
+        // side on that operand, copying 256 rows half a line per step; the
+        // 256x128 tile puts 128 there.  From the same grid (TT, fp32 output):
+        // at 512 < K <= 1024 over a wave of 256x256 tiles the 256x128 tile
+        // (3072x8192x1024 0.0572 ms against 0.0540), and 256x128 instead of
+        // 128x256 in the long-K rule below (4096x2048x4096 0.0676 against
+        // 0.0587); mean ratio to the fastest candidate 1.039 -> 1.009 at K =
+        // 1024, 1.029 -> 1.004 at 4096 (on a second run).  At K <= 512 the
+        // layout follows the rules above (the 128x128 rings won some shapes
+        // on one run and lost them on the next).
+        static const int tall_tile = find_variant("bf16_dma32x32x16_256x128x32_w2x2_s3_late");
+        const bool b_only_kc = c.b_kc && !c.a_kc;
+        const bool tall_ok = measured && b_only_kc && tall_tile >= 0 &&
+                             serves(table()[tall_tile]) &&
+                             dma_offsets_fit(table()[tall_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        if (tall_ok && K > 512 && K <= 1024 && t256 >= cus) {
+            id = tall_tile;
+        } else if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus &&
+                   wide_rounds) {
             id = wide_tile;
         } else if (measured && K <= 512 && 4 * t256 >= 3 * cus && mid_ok) {
             id = mid_id;
@@ -620,7 +637,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             if (both_kc) {
                 if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
             } else if (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus) {
-                id = wide_tile;
+                id = tall_ok ? tall_tile : wide_tile;
             } else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) && big_fits) {
                 id = big_id;
             }

@@ -60,9 +60,13 @@ CASES = [
     # long K, 128x256 tiles filling 3/4 to 1 of a wave: 128x256
     ("bf16", "N", "N", 4096, 2048, 4096, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
     ("bf16", "T", "N", 4096, 2048, 4096, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
-    # short K over a full wave of 256x256 tiles: 128x256
+    # short K over a full wave of 256x256 tiles: 128x256; with only B
+    # k-contiguous (A^T B^T) and 512 < K <= 1024, 256x128 (128 rows of the
+    # k-contiguous operand per tile instead of 256), also in the long-K rule
     ("bf16", "N", "N", 8192, 4096, 512, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
-    ("bf16", "T", "T", 8192, 8192, 1024, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "T", 8192, 8192, 1024, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
+    ("bf16", "T", "T", 8192, 8192, 512, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "T", 4096, 2048, 4096, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
     # ... but not below a full wave: there 192x256 tiles (as D^T, 192 along
     # N) fill the wave that 256x256 tiles fill three quarters of
     ("bf16", "N", "N", 8192, 1536, 1024, 0.0, False, P + "192x256x32_w2x4_s3_late", False),
