@@ -634,9 +634,18 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                 id = mid_id;
             }
         } else if (4 * t256 < 3 * cus) {
+            // bf16 output, aligned rows: 128x256 tiles filling 3/4 to 1 of a
+            // wave from K = 1024, both operands k-contiguous included (no
+            // paired ring carries bf16 output; with bf16 D, ms, one box:
+            // NT 2048x4096x4096 0.0747 on 128x128 -> 0.0688, TN 3072x2048x1024
+            // 0.0214 -> 0.0188; within 5 % of the fastest candidate 65 -> 72
+            // of 72 grid shapes at K = 4096, 66 -> 68 at 1024, on that run)
+            const bool bo_wide = out_bf16 && c.rows16 && wide_ok && K >= 1024 && t12 <= cus &&
+                                 4 * t12 >= 3 * cus;
             if (both_kc) {
                 if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
-            } else if (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus) {
+                else if (bo_wide) id = wide_tile;
+            } else if (bo_wide || (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus)) {
                 id = tall_ok ? tall_tile : wide_tile;
             } else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) && big_fits) {
                 id = big_id;

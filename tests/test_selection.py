@@ -94,6 +94,10 @@ CASES = [
     ("bf16", "T", "N", 3072, 4096, 256, 0.0, True, P + "192x256x32_w2x4_s3_late", False),
     ("bf16", "T", "N", 8192, 3072, 512, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
     ("bf16", "T", "N", 6144, 3072, 256, 0.0, True, P + "128x128x32_w2x2_s4_late", False),
+    # bf16 output, 128x256 tiles filling 3/4 to 1 of a wave from K = 1024,
+    # both operands k-contiguous included (no paired ring carries bf16 D)
+    ("bf16", "N", "T", 2048, 4096, 4096, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "N", 3072, 2048, 1024, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]
