@@ -5,7 +5,8 @@ transpose, the three precisions, random alpha/beta, fused epilogues,
 leading-dimension padding and element offsets.  Outputs are checked on 64 x
 64 samples that always include the first and last row and column; each case
 prints its draw and the variant it ran before the check, so a failure names
-both."""
+both.  A second set of fixed calls takes the tiles that the shape rules pick
+for particular layouts, output types and K, and checks the variant as well."""
 from __future__ import annotations
 
 import numpy as np
@@ -104,3 +105,50 @@ def test_random_large_call_matches_oracle(g, handle, case):
         err, tol = oracle.max_relative_error(got, val, den), oracle.TOLERANCE[ab]
     assert np.isfinite(D.cpu().float().numpy()).all()
     assert err <= tol, (d, err)
+
+
+P = "bf16_dma32x32x16_"
+# Calls that take the tiles the shape rules pick for particular layouts,
+# output types and K (a ragged side included), checked on samples like the
+# random calls: dtype, transA, transB, M, N, K, alpha, beta, expected variant
+SELECTED = [
+    ("bf16_f32", "T", "T", 4000, 2048, 4096, 0.5, 1.0, P + "256x128x32_w2x2_s3_late"),
+    ("bf16_f32", "T", "T", 8192, 8192, 1024, 1.0, 0.0, P + "256x128x32_w2x2_s3_late"),
+    ("bf16_f32", "T", "N", 6144, 3072, 256, -1.5, 0.0, P + "128x128x32_w2x2_s4_late"),
+    ("bf16_f32", "N", "T", 6144, 3072, 768, 1.0, -0.75, P + "128x128x32_w2x2_s4_late_pair"),
+    ("bf16_bf16", "N", "T", 2048, 4096, 4096, 1.0, 1.0, P + "128x256x32_w2x2_s3_late"),
+    ("bf16_bf16", "T", "N", 3072, 4096, 256, 0.5, 0.0, P + "192x256x32_w2x4_s3_late"),
+    ("f32", "N", "N", 6144, 6144, 1024, 1.0, 1.0, "f32_dma32x32x2_128x128x16_w2x2_s3_late"),
+    ("f32", "T", "N", 3000, 6144, 256, -1.5, 0.0, "f32_dma32x32x2_128x128x16_w2x2_s3_late"),
+]
+
+
+@pytest.mark.parametrize("case", SELECTED, ids=lambda c: f"{c[0]}_{c[1]}{c[2]}_{c[3]}x{c[4]}x{c[5]}")
+def test_selected_tile_matches_oracle(g, handle, case):
+    dtype, ta, tb, M, N, K, alpha, beta, expected = case
+    announce("selected-tile", case)
+    ab = "f32" if dtype == "f32" else "bf16"
+    out = torch.bfloat16 if dtype == "bf16_bf16" else torch.float32
+    seed = 19600 + SELECTED.index(case) * 10
+    A = workloads.draw_matrix((M, K) if ta == "N" else (K, M), "n1", seed, ab)
+    B = workloads.draw_matrix((K, N) if tb == "N" else (N, K), "n1", seed + 1, ab)
+    C = workloads.draw_matrix((M, N), "u11", seed + 2, "f32").to(out) if beta else None
+    D = torch.full((M, N), float("nan"), dtype=out, device="cuda")
+    s = g.run_tensors(handle, A.cuda(), B.cuda(), D, C=None if C is None else C.cuda(),
+                      transA=ta, transB=tb, alpha=alpha, beta=beta, check=False)
+    torch.cuda.synchronize()
+    assert s == g.GEMM_OK, g.gemm_status_string(s)
+    assert g.gemm_variant_name(g.gemm_last_variant(handle)) == expected
+    rows, cols = workloads.sample_indices(M, N, seed + 3)
+    ii, jj = np.meshgrid(rows, cols, indexing="ij")
+    ii, jj = ii.ravel(), jj.ravel()
+    val, den = oracle.gemm_points(ta, tb, M, N, K, alpha, host_operand(A), A.shape[1],
+                                  host_operand(B), B.shape[1], beta,
+                                  None if C is None else C.float().numpy(), N, ii, jj)
+    got = D.cpu().double().numpy()[ii, jj]
+    if dtype == "bf16_bf16":
+        err, tol = oracle.max_bf16_output_error(got, val, den), 1.0
+    else:
+        err, tol = oracle.max_relative_error(got, val, den), oracle.TOLERANCE[ab]
+    assert np.isfinite(D.float().cpu().numpy()).all()
+    assert err <= tol, (case, err)
