@@ -822,6 +822,8 @@ def main(argv=None):
                     help="output type of the --selector-check calls")
     ap.add_argument("--selector-f32", action="store_true",
                     help="fp32 operands and the fp32 candidates in --selector-check")
+    ap.add_argument("--selector-dims", default="1024,2048,3072,4096,6144,8192",
+                    help="comma-separated M and N values of the --selector-check grid")
     ap.add_argument("--selector-layouts", default="TN,NT",
                     help="comma-separated layouts of the --selector-check grid (an automatic "
                          "NN call may run as D^T while a forced candidate runs as stored)")
@@ -859,7 +861,9 @@ def main(argv=None):
     if args.selector_check:
         workspace = g.attach_workspace(h)
         ks = tuple(int(k) for k in args.selector_ks.split(","))
-        print(json.dumps(selector_check(g, h, ks=ks, out_bf16=args.selector_out == "bf16",
+        dims = tuple(int(d) for d in args.selector_dims.split(","))
+        print(json.dumps(selector_check(g, h, dims=dims, ks=ks,
+                                        out_bf16=args.selector_out == "bf16",
                                         f32=args.selector_f32,
                                         layouts=tuple(args.selector_layouts.split(",")))),
               flush=True)

@@ -615,8 +615,21 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         const bool tall_ok = measured && b_only_kc && tall_tile >= 0 &&
                              serves(table()[tall_tile]) &&
                              dma_offsets_fit(table()[tall_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        // Rows not 16-byte aligned (every 16-byte copy straddles two units),
+        // fp32 output, K <= 512: no 128x256 tiles, which lost 16-33 % there;
+        // NN over 3/4 of a wave of 256x256 tiles keeps 256x256 (run as
+        // stored, below), everything else takes the 128x128 rings.  From
+        // every whole-tile candidate on 36 shapes with odd sides (1021 ..
+        // 8189) per layout, K = 511 (ms, one box): TN 4093x4093 0.0513 on
+        // 128x256 -> 0.0393 on the 4-stage 128x128 ring, NN 4093x4093 0.0536
+        // -> 0.0412 on 256x256 as stored; mean ratio to the fastest candidate
+        // 1.126 -> 1.020 (TN), 1.140 -> 1.026 (NN), fitted to that run.
+        const bool mis_short = !out_bf16 && !c.rows16 && K <= 512;
         if (tall_ok && K > 512 && K <= 1024 && t256 >= cus) {
             id = tall_tile;
+        } else if (mis_short) {
+            if (c.a_kc && !c.b_kc && 4 * t256 >= 3 * cus && big_fits) id = big_id;
+            else if (mid_ok) id = mid_id;
         } else if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus &&
                    wide_rounds) {
             id = wide_tile;
@@ -672,9 +685,14 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             bool best_pref = false;
             for (int vi = 0; vi < 2; ++vi) {
                 if (w192[vi] < 0 || !serves(table()[w192[vi]])) continue;
+                // 256x192 on rows that are not 16-byte aligned ran 13-46 %
+                // behind the fastest candidate (odd-sided grid, K = 1537 and
+                // 4093: TN 4093x6141x1537 0.1437 against 0.1076 on 256x256),
+                // 192x256 where it was chosen within a few %
+                if (vi == 1 && !c.rows16) continue;
                 const Variant& vv = table()[w192[vi]];
                 for (int tr = 0; tr < 2; ++tr) {
-                    const bool ok = tr ? (c.a_kc && !c.b_kc && vv.nn_t_fn &&
+                    const bool ok = tr ? (c.rows16 && c.a_kc && !c.b_kc && vv.nn_t_fn &&
                                           dma_offsets_fit(vv, false, true, K, c.ldb, c.lda, es))
                                        : dma_offsets_fit(vv, c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
                     if (!ok) continue;
@@ -723,8 +741,13 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     // bf16 NN with whole tiles: run as D^T = B^T A^T, which puts the
     // mn-contiguous operand first (measured on 8192^3, same box: TT layout
     // 1282 vs NN 1235 TFLOP/s); the transposed-output epilogue writes D.
+    // (not for rows that are not 16-byte aligned: as D^T the transposed
+    // epilogue writes D in short row pieces, each straddling two lines of the
+    // misaligned rows; NN 8189x2045x1537 0.0683 as D^T on 256x256 against
+    // 0.0605 as stored, 4093x4093x511 0.0535 against 0.0412)
     const bool nn_t = sk == 0 && c.forced < 0 && !untransposed && vr.nn_t_fn && aligned &&
-                      c.a_kc && !c.b_kc && dma_offsets_fit(vr, false, true, K, c.ldb, c.lda, es);
+                      c.rows16 && c.a_kc && !c.b_kc &&
+                      dma_offsets_fit(vr, false, true, K, c.ldb, c.lda, es);
     if (out_bf16 && !aligned) return GEMM_ERR_NOT_SUPPORTED;
     // fused epilogue: only the selected direct-to-LDS variants and the
     // non-square bf16 tiles, whole tiles and wide access, carry it

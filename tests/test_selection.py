@@ -98,6 +98,15 @@ CASES = [
     # both operands k-contiguous included (no paired ring carries bf16 D)
     ("bf16", "N", "T", 2048, 4096, 4096, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
     ("bf16", "T", "N", 3072, 2048, 1024, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
+    # rows that are not 16-byte aligned (odd sides): at K <= 512 no 128x256,
+    # NN from 3/4 of a wave of 256x256 tiles on 256x256 (as stored), else the
+    # 128x128 rings; no 256x192 and no D^T, so NN 2045x6141 keeps 256x256
+    # where 192x256 would take two waves as stored
+    ("bf16", "T", "N", 4093, 4093, 511, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "N", "N", 4093, 4093, 511, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "N", "N", 2045, 4093, 511, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    ("bf16", "N", "N", 2045, 6141, 1537, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "T", "N", 4093, 6141, 1537, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]
