@@ -617,8 +617,11 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                              dma_offsets_fit(table()[tall_tile], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
         // Rows not 16-byte aligned (every 16-byte copy straddles two units),
         // fp32 output, K <= 512: no 128x256 tiles, which lost 16-33 % there;
-        // NN over 3/4 of a wave of 256x256 tiles keeps 256x256 (run as
-        // stored, below), everything else takes the 128x128 rings.  From
+        // with a k-contiguous operand (NN, NT, TT) 256x256 tiles over waves
+        // at least 3/4 full (NN runs as stored, below), everything else the
+        // 128x128 rings (NT 8189x4093x511 0.0906 on the paired 128x128 ring
+        // -> 0.0798 on 256x256, on a second grid run; at 288 tiles of 256x256
+        // the 2-stage 128x128 ring was fastest in every layout).  From
         // every whole-tile candidate on 36 shapes with odd sides (1021 ..
         // 8189) per layout, K = 511 (ms, one box): TN 4093x4093 0.0513 on
         // 128x256 -> 0.0393 on the 4-stage 128x128 ring, NN 4093x4093 0.0536
@@ -628,8 +631,11 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         if (tall_ok && K > 512 && K <= 1024 && t256 >= cus) {
             id = tall_tile;
         } else if (mis_short) {
-            if (c.a_kc && !c.b_kc && 4 * t256 >= 3 * cus && big_fits) id = big_id;
-            else if (mid_ok) id = mid_id;
+            if ((c.a_kc || c.b_kc) && 4 * t256 >= 3 * cus && rounds_at_least(t256, 1, 3, 4) &&
+                big_fits)
+                id = big_id;
+            else if (mid_ok)
+                id = mid_id;
         } else if (wide_ok && K <= (both_kc ? 512 : 1024) && t256 >= (out_bf16 ? 4 : 1) * cus &&
                    wide_rounds) {
             id = wide_tile;
@@ -655,9 +661,20 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             // of 72 grid shapes at K = 4096, 66 -> 68 at 1024, on that run)
             const bool bo_wide = out_bf16 && c.rows16 && wide_ok && K >= 1024 && t12 <= cus &&
                                  4 * t12 >= 3 * cus;
+            // only B k-contiguous, rows not 16-byte aligned, fp32 output:
+            // 256x128 where 128x256 tiles would fill 3/4 to 1 of a wave, from
+            // K = 1024 (odd-sided grid, TT: fastest candidate on all 16 such
+            // shapes at K = 1537 and 4093; 2045x4093x4093 0.0941 on 128x256 ->
+            // 0.0832)
+            const bool tall_mis = !out_bf16 && !c.rows16 && b_only_kc && tall_tile >= 0 &&
+                                  serves(table()[tall_tile]) &&
+                                  dma_offsets_fit(table()[tall_tile], c.a_kc, c.b_kc, K, c.lda,
+                                                  c.ldb, es);
             if (both_kc) {
                 if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
                 else if (bo_wide) id = wide_tile;
+            } else if (tall_mis && K >= 1024 && t12 <= cus && 4 * t12 >= 3 * cus) {
+                id = tall_tile;
             } else if (bo_wide || (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus)) {
                 id = tall_ok ? tall_tile : wide_tile;
             } else if (2 * t256 >= cus && (K >= 2048 || !c.rows16) && big_fits) {

@@ -107,6 +107,12 @@ CASES = [
     ("bf16", "N", "N", 2045, 4093, 511, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
     ("bf16", "N", "N", 2045, 6141, 1537, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     ("bf16", "T", "N", 4093, 6141, 1537, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    # ... 256x256 at short K in any layout with a k-contiguous operand, over
+    # waves at least 3/4 full; with only B k-contiguous, 256x128 where
+    # 128x256 tiles would fill 3/4 to 1 of a wave from K = 1024
+    ("bf16", "N", "T", 8189, 4093, 511, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
+    ("bf16", "T", "T", 2045, 4093, 4093, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
+    ("bf16", "T", "T", 4093, 2045, 1537, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
     # few tiles, long K: stream-K
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
 ]
