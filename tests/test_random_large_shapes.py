@@ -20,7 +20,7 @@ from .gpu_support import announce, host_operand, place, require_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 48
 
 
 @pytest.fixture(scope="module")
