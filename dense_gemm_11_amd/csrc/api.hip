@@ -653,12 +653,12 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                 id = mid_id;
             }
         } else if (4 * t256 < 3 * cus) {
-            // bf16 output, aligned rows: 128x256 tiles filling 3/4 to 1 of a
-            // wave from K = 1024, both operands k-contiguous included (no
-            // paired ring carries bf16 output; with bf16 D, ms, one box:
-            // NT 2048x4096x4096 0.0747 on 128x128 -> 0.0688, TN 3072x2048x1024
-            // 0.0214 -> 0.0188; within 5 % of the fastest candidate 65 -> 72
-            // of 72 grid shapes at K = 4096, 66 -> 68 at 1024, on that run)
+            // bf16 output, aligned rows, one or no operand k-contiguous:
+            // 128x256 tiles filling 3/4 to 1 of a wave from K = 1024 (with
+            // bf16 D, ms, one box: TN 3072x2048x1024 0.0214 on 128x128 ->
+            // 0.0188).  Both operands k-contiguous take the paired 128x128
+            // ring there, as with fp32 D (NT 2048x4096x4096: 0.0667 on it
+            // against 0.0740 on 128x256).
             const bool bo_wide = out_bf16 && c.rows16 && wide_ok && K >= 1024 && t12 <= cus &&
                                  4 * t12 >= 3 * cus;
             // only B k-contiguous, rows not 16-byte aligned, fp32 output:
@@ -672,7 +672,6 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                                                   c.ldb, es);
             if (both_kc) {
                 if (2 * t256 > cus && K >= 1024 && big_fits) id = big_id;
-                else if (bo_wide) id = wide_tile;
             } else if (tall_mis && K >= 1024 && t12 <= cus && 4 * t12 >= 3 * cus) {
                 id = tall_tile;
             } else if (bo_wide || (wide_ok && K >= 2048 && t12 <= cus && 4 * t12 >= 3 * cus)) {
@@ -736,12 +735,14 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     // when that removes a round of tiles (4093x2051x1537: 544 tiles in one
     // round instead of a full round and a nearly empty one; measured 0.0593
     // vs 0.0624 ms), which the round and pipeline-depth model above decides.
-    // Neither variant has transposed-output, bf16-output or fused-epilogue
-    // instantiations, so only plain fp32-output calls take them.
-    if (sk == 0 && c.forced < 0 && aligned && !c.epi && !out_bf16 &&
+    // Neither variant has transposed-output or fused-epilogue
+    // instantiations (NN keeps its orientation on them); both carry bf16
+    // output.
+    if (sk == 0 && c.forced < 0 && aligned && !c.epi &&
         id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
         static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
-        if (s2 >= 0 && data_parallel_us(table()[s2], M, N, K) < data_parallel_us(table()[id], M, N, K))
+        if (s2 >= 0 && serves(table()[s2]) &&
+            data_parallel_us(table()[s2], M, N, K) < data_parallel_us(table()[id], M, N, K))
             id = s2;
         // Otherwise, with a k-contiguous operand and more tiles than compute
         // units (two workgroups on a unit hide the latency of the larger
@@ -750,7 +751,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // vs 44.0 us, 2560^2 x 4096 62.0 vs 72.8) and 5-22 % slower at 256
         // tiles and fewer.
         static const int pair = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair");
-        if (id != s2 && pair >= 0 && (c.a_kc || c.b_kc) &&
+        if (id != s2 && pair >= 0 && serves(table()[pair]) && (c.a_kc || c.b_kc) &&
             ceil_div(M, 128) * ceil_div(N, 128) > (int64_t)device_cus())
             id = pair;
     }

@@ -37,6 +37,18 @@ using Dma128s2P = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true, PAI
     {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, CFG::S, CFG::AHEAD, \
      DG_FN_TABLE(dma_gemm_kernel, CFG)}
 
+// with bf16-output launches (table W of bf16_out_fns_tile, instantiated in
+// inst_bf16_dma_out_tiles.hip); NN keeps its orientation on these tiles
+#define BF16_DMA_BO_VARIANT(NAME, CFG, W)                                                    \
+    {NAME, 1, KIND_MFMA_DMA, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::LDS_BYTES, CFG::S, \
+     CFG::AHEAD, DG_FN_TABLE(dma_gemm_kernel, CFG), {{nullptr, nullptr}, {nullptr, nullptr}},  \
+     nullptr, nullptr,                                                                        \
+     {{{bf16_out_fns_tile(W).fn[0][0][0], bf16_out_fns_tile(W).fn[0][0][1]},                  \
+       {bf16_out_fns_tile(W).fn[0][1][0], bf16_out_fns_tile(W).fn[0][1][1]}},                 \
+      {{bf16_out_fns_tile(W).fn[1][0][0], bf16_out_fns_tile(W).fn[1][0][1]},                  \
+       {bf16_out_fns_tile(W).fn[1][1][0], bf16_out_fns_tile(W).fn[1][1][1]}}},                \
+     bf16_out_fns_tile(W).nn_t}
+
 const Variant* bf16dma_sweep_variant_table(int* count)
 {
     static const Variant table[] = {
@@ -45,7 +57,7 @@ const Variant* bf16dma_sweep_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s3", Dma256s3),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late", Dma256s4L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x64_w2x2_s2_late", Dma256k64s2L),
-        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s2_late", Dma128s2L),
+        BF16_DMA_BO_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s2_late", Dma128s2L, 3),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late", Dma128s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s5_late", Dma128s5L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s3_late_o3", Dma128s3LO3),
@@ -55,7 +67,7 @@ const Variant* bf16dma_sweep_variant_table(int* count)
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x64_w2x2_s3_late", Dma128k64s3L),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s4_late_pair", Dma256s4P),
         BF16_DMA_VARIANT("bf16_dma32x32x16_256x256x32_w2x2_s2_late_pair", Dma256s2P),
-        BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair", Dma128s4P),
+        BF16_DMA_BO_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair", Dma128s4P, 4),
         BF16_DMA_VARIANT("bf16_dma32x32x16_128x128x32_w2x2_s2_late_pair", Dma128s2P),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));

@@ -6,7 +6,10 @@
 //    per compute unit (register budget capped at 256 per lane);
 //  * 192x256 (8 waves, 2x4 grid, 96x64 per wave) and 256x192 (4x2 grid,
 //    64x96 per wave): 3 stages, late barrier; both operands k-contiguous:
-//    pair buffers, as for the 256x256 tile.
+//    pair buffers, as for the 256x256 tile;
+//  * the two 128x128 rings the selector puts beside the 4-stage one: 2
+//    stages (three workgroups per compute unit), and 4 stages with the
+//    k-contiguous operand copied two steps at a time into pair buffers.
 #pragma once
 
 #include "mfma_dma_gemm.hpp"
@@ -17,5 +20,7 @@ using Dma256x128s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 128, 32, 2, 2, 3, true,
 using Dma128x256s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 256, 32, 2, 2, 3, true, PAIR_NONE, 2>;
 using Dma192x256s3L = DmaConfig<MFMA_BF16_32x32x16, 192, 256, 32, 2, 4, 3, true, PAIR_BOTH_KC>;
 using Dma256x192s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 192, 32, 4, 2, 3, true, PAIR_BOTH_KC>;
+using Dma128x128s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true>;
+using Dma128x128s4LPair = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true, PAIR_KC>;
 
 }  // namespace dg

@@ -215,3 +215,25 @@ def test_bf16_output_on_shape_selected_tiles(sk_handle, c):
     err = check(ta, tb, M, N, K, alpha, beta, A, B, C, D, rows=rows, cols=cols)
     print(f"[result] bf16-out {ta}{tb} {M}x{N}x{K} max_err={err:.3e}", flush=True)
     assert err <= 1.0
+
+
+@pytest.mark.parametrize("variant", ["bf16_dma32x32x16_128x128x32_w2x2_s2_late",
+                                     "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair"])
+@pytest.mark.parametrize("ta,tb", list(itertools.product("NT", "NT")))
+def test_bf16_output_on_the_other_128_rings(handle, variant, ta, tb):
+    """bf16 output on the 2-stage and the paired 4-stage 128x128 rings (each
+    forced), ragged shapes with partial tiles on every side and beta != 0,
+    against the whole oracle result."""
+    import dense_gemm_11_amd as g
+    names = {name: i for i, name, _, _ in g.variants()}
+    g.gemm_set_variant(handle, names[variant])
+    try:
+        for M, N, K in ((300, 520, 200), (513, 260, 70)):
+            announce("bf16-out ring", variant, ta, tb, M, N, K)
+            A, B, C = case(ta, tb, M, N, K, 7300 + M, with_c=True)
+            D, _ = run_bf16_out(handle, ta, tb, M, N, K, 0.5, -1.25, A, B, C)
+            assert g.gemm_variant_name(g.gemm_last_variant(handle)) == variant
+            err = check(ta, tb, M, N, K, 0.5, -1.25, A, B, C, D)
+            assert err <= 1.0, (variant, ta, tb, M, N, K, err)
+    finally:
+        g.gemm_set_variant(handle, -1)

@@ -94,10 +94,12 @@ CASES = [
     ("bf16", "T", "N", 3072, 4096, 256, 0.0, True, P + "192x256x32_w2x4_s3_late", False),
     ("bf16", "T", "N", 8192, 3072, 512, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
     ("bf16", "T", "N", 6144, 3072, 256, 0.0, True, P + "128x128x32_w2x2_s4_late", False),
-    # bf16 output, 128x256 tiles filling 3/4 to 1 of a wave from K = 1024,
-    # both operands k-contiguous included (no paired ring carries bf16 D)
-    ("bf16", "N", "T", 2048, 4096, 4096, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
+    # bf16 output, 128x256 tiles filling 3/4 to 1 of a wave from K = 1024;
+    # both operands k-contiguous: the paired 128x128 ring (which carries bf16
+    # D), as with fp32 D; 3072^2 at short K: the 2-stage ring
+    ("bf16", "N", "T", 2048, 4096, 4096, 0.0, True, P + "128x128x32_w2x2_s4_late_pair", False),
     ("bf16", "T", "N", 3072, 2048, 1024, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
+    ("bf16", "T", "N", 3072, 3072, 512, 0.0, True, P + "128x128x32_w2x2_s2_late", False),
     # rows that are not 16-byte aligned (odd sides): at K <= 512 no 128x256,
     # NN from 3/4 of a wave of 256x256 tiles on 256x256 (as stored), else the
     # 128x128 rings; no 256x192 and no D^T, so NN 2045x6141 keeps 256x256
