@@ -628,7 +628,19 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // -> 0.0412 on 256x256 as stored; mean ratio to the fastest candidate
         // 1.126 -> 1.020 (TN), 1.140 -> 1.026 (NN), fitted to that run.
         const bool mis_short = !out_bf16 && !c.rows16 && K <= 512;
-        if (tall_ok && K > 512 && K <= 1024 && t256 >= cus) {
+        // bf16 output, no k-contiguous operand, K <= 256, from 3/8 of a wave
+        // of 256x256 tiles: the 2-stage 128x128 ring (three workgroups per
+        // compute unit), the fastest candidate on 22 of 28 such grid shapes
+        // and within 6 % on the rest (TN 4096x3072x256 0.0142 ms on 256x192
+        // -> 0.0123, 6144x6144x256 0.0349 on 128x256 -> 0.0309; mean ratio
+        // to the fastest candidate 1.074 -> 1.013 on that run)
+        static const int s2_id = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
+        const bool s2_bo = short_bo && !c.a_kc && !c.b_kc && K <= 256 && 8 * t256 >= 3 * cus &&
+                           s2_id >= 0 && serves(table()[s2_id]) &&
+                           dma_offsets_fit(table()[s2_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        if (s2_bo) {
+            id = s2_id;
+        } else if (tall_ok && K > 512 && K <= 1024 && t256 >= cus) {
             id = tall_tile;
         } else if (mis_short) {
             if ((c.a_kc || c.b_kc) && 4 * t256 >= 3 * cus && rounds_at_least(t256, 1, 3, 4) &&

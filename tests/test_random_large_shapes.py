@@ -118,7 +118,8 @@ SELECTED = [
     ("bf16_f32", "N", "T", 6144, 3072, 768, 1.0, -0.75, P + "128x128x32_w2x2_s4_late_pair"),
     ("bf16_bf16", "N", "T", 2048, 4096, 4096, 1.0, 1.0, P + "128x128x32_w2x2_s4_late_pair"),
     ("bf16_bf16", "T", "N", 3072, 2048, 1024, -1.0, 0.5, P + "128x256x32_w2x2_s3_late"),
-    ("bf16_bf16", "T", "N", 3072, 4096, 256, 0.5, 0.0, P + "192x256x32_w2x4_s3_late"),
+    ("bf16_bf16", "T", "N", 3072, 4096, 512, 0.5, 0.0, P + "192x256x32_w2x4_s3_late"),
+    ("bf16_bf16", "T", "N", 6144, 3072, 256, 1.0, 0.5, P + "128x128x32_w2x2_s2_late"),
     ("f32", "N", "N", 6144, 6144, 1024, 1.0, 1.0, "f32_dma32x32x2_128x128x16_w2x2_s3_late"),
     ("f32", "T", "N", 3000, 6144, 256, -1.5, 0.0, "f32_dma32x32x2_128x128x16_w2x2_s3_late"),
 ]

@@ -86,14 +86,16 @@ CASES = [
     # (288 tiles), 256x256 where its waves are whole (512 tiles)
     ("bf16", "N", "T", 6144, 3072, 768, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
     ("bf16", "N", "T", 8192, 4096, 768, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
-    # bf16 output, short K: 256x256 on whole waves (4096^2: 256 tiles),
-    # below a wave the 192-wide search (3072x4096: 192 tiles of 256x256, 256
-    # of 192x256), 128x256 where its rounds are 3/4 full (8192x3072: 768
-    # tiles), else the 128x128 ring (6144x3072: 576 tiles of 128x256)
+    # bf16 output, short K: with no k-contiguous operand and K <= 256 the
+    # 2-stage 128x128 ring from 3/8 of a wave of 256x256 tiles; otherwise
+    # 256x256 on whole waves (4096^2: 256 tiles), below a wave the 192-wide
+    # search (3072x4096: 192 tiles of 256x256, 256 of 192x256), 128x256
+    # where its rounds are 3/4 full (8192x3072: 768 tiles)
+    ("bf16", "T", "N", 6144, 3072, 256, 0.0, True, P + "128x128x32_w2x2_s2_late", False),
+    ("bf16", "T", "N", 3072, 4096, 256, 0.0, True, P + "128x128x32_w2x2_s2_late", False),
     ("bf16", "T", "N", 4096, 4096, 512, 0.0, True, P + "256x256x32_w2x4_s3_late", False),
-    ("bf16", "T", "N", 3072, 4096, 256, 0.0, True, P + "192x256x32_w2x4_s3_late", False),
+    ("bf16", "T", "N", 3072, 4096, 512, 0.0, True, P + "192x256x32_w2x4_s3_late", False),
     ("bf16", "T", "N", 8192, 3072, 512, 0.0, True, P + "128x256x32_w2x2_s3_late", False),
-    ("bf16", "T", "N", 6144, 3072, 256, 0.0, True, P + "128x128x32_w2x2_s4_late", False),
     # bf16 output, 128x256 tiles filling 3/4 to 1 of a wave from K = 1024;
     # both operands k-contiguous: the paired 128x128 ring (which carries bf16
     # D), as with fp32 D; 3072^2 at short K: the 2-stage ring
