@@ -413,7 +413,8 @@ const LaunchFn (*sk_launchers(const Variant& x, int op_dtype, bool out_bf16, boo
 
 // Fused-epilogue launches of variant `id` for the call's operand and output
 // types, or null where the variant carries none (the selected square
-// direct-to-LDS variants and the non-square bf16 tiles do).
+// direct-to-LDS variants, the non-square bf16 tiles and the 2-stage and
+// paired 128x128 bf16 rings do).
 const EpiFns* epi_fns_for(int id, int op_dtype, bool out_bf16)
 {
     if (id < 0) return nullptr;
@@ -423,10 +424,12 @@ const EpiFns* epi_fns_for(int id, int op_dtype, bool out_bf16)
                : out_bf16                 ? epi_fns_bf16_out(v.bm)
                                           : epi_fns_bf16(v.bm);
     if (op_dtype != GEMM_DTYPE_BF16_F32) return nullptr;
-    static const int tiles[3] = {find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late"),
+    static const int tiles[5] = {find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late"),
                                  find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late"),
-                                 find_variant("bf16_dma32x32x16_256x192x32_w4x2_s3_late")};
-    for (int w = 0; w < 3; ++w)
+                                 find_variant("bf16_dma32x32x16_256x192x32_w4x2_s3_late"),
+                                 find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late"),
+                                 find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair")};
+    for (int w = 0; w < 5; ++w)
         if (id == tiles[w]) return out_bf16 ? epi_fns_tile_bf16out(w) : epi_fns_tile_f32out(w);
     return nullptr;
 }
@@ -747,10 +750,9 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     // when that removes a round of tiles (4093x2051x1537: 544 tiles in one
     // round instead of a full round and a nearly empty one; measured 0.0593
     // vs 0.0624 ms), which the round and pipeline-depth model above decides.
-    // Neither variant has transposed-output or fused-epilogue
-    // instantiations (NN keeps its orientation on them); both carry bf16
-    // output.
-    if (sk == 0 && c.forced < 0 && aligned && !c.epi &&
+    // Neither variant has a transposed-output instantiation (NN keeps its
+    // orientation on them); both carry bf16 output and the fused epilogue.
+    if (sk == 0 && c.forced < 0 && aligned &&
         id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
         static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
         if (s2 >= 0 && serves(table()[s2]) &&

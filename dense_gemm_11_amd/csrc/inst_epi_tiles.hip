@@ -1,6 +1,6 @@
 // Fused-epilogue (bias, activation, clamp) instantiations of the non-square
 // bf16 direct-to-LDS tiles the selector takes by shape (128x256, 192x256,
-// 256x192), fp32 C and D.
+// 256x192) and of the 2-stage and paired 128x128 rings, fp32 C and D.
 #include "tile_configs.hpp"
 #include "variants.hpp"
 
@@ -11,7 +11,9 @@ const EpiFns* epi_fns_tile_f32out(int which)
     static const EpiFns wide = DG_EPI_TABLE(dma_gemm_kernel, Dma128x256s3L, false);
     static const EpiFns t192 = DG_EPI_TABLE(dma_gemm_kernel, Dma192x256s3L, false);
     static const EpiFns w192 = DG_EPI_TABLE(dma_gemm_kernel, Dma256x192s3L, false);
-    return which == 0 ? &wide : which == 1 ? &t192 : which == 2 ? &w192 : nullptr;
+    static const EpiFns s2 = DG_EPI_TABLE(dma_gemm_kernel, Dma128x128s2L, false);
+    static const EpiFns pair = DG_EPI_TABLE(dma_gemm_kernel, Dma128x128s4LPair, false);
+    return which == 0 ? &wide : which == 1 ? &t192 : which == 2 ? &w192 : which == 3 ? &s2 : which == 4 ? &pair : nullptr;
 }
 
 }  // namespace dg

@@ -260,3 +260,29 @@ def test_epilogue_on_shape_selected_tiles(g, handle, dtype, c):
                      (-0.5, 3.0), D, rows=rows, cols=cols)
     print(f"[result] epilogue tile {dtype} {ta}{tb} {M}x{N}x{K} err={err:.3e}", flush=True)
     assert err <= tol
+
+
+@pytest.mark.parametrize("variant", ["bf16_dma32x32x16_128x128x32_w2x2_s2_late",
+                                     "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair"])
+@pytest.mark.parametrize("dtype", ["bf16_f32", "bf16_bf16"])
+def test_epilogue_on_the_other_128_rings(g, handle, variant, dtype):
+    """bias / activation / clamp fused into the 2-stage and the paired
+    4-stage 128x128 rings (each forced), every transpose, ragged shapes,
+    against the whole oracle result."""
+    names = {name: i for i, name, _, _ in g.variants()}
+    assert g.gemm_set_variant(handle, names[variant]) == g.GEMM_OK
+    try:
+        for n, ((ta, tb), (M, N, K)) in enumerate(itertools.product(
+                list(itertools.product("NT", "NT")), [(300, 200, 513), (513, 260, 70)])):
+            with_bias, act, clamp = EPIS[n % len(EPIS)]
+            alpha, beta = [(1.0, 0.0), (0.5, 1.5), (-1.0, 1.0)][n % 3]
+            A, B, C, bias, out = make(dtype, ta, tb, M, N, K, 7500 + n, beta != 0.0)
+            bias = bias if with_bias else None
+            announce("epilogue ring", variant, dtype, ta, tb, M, N, K, act, clamp)
+            D = run(g, handle, ta, tb, alpha, beta, A, B, C, bias, ACTS[act], clamp, out, M, N)
+            assert g.gemm_variant_name(g.gemm_last_variant(handle)) == variant
+            err, tol = check(dtype, ta, tb, M, N, K, alpha, beta, A, B, C, bias, ACTS[act],
+                             clamp, D)
+            assert err <= tol, (variant, dtype, ta, tb, M, N, K, act, clamp, err)
+    finally:
+        g.gemm_set_variant(handle, -1)
