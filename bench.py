@@ -666,7 +666,8 @@ SELECTOR_CANDIDATES_F32 = ["f32_dma32x32x2_256x256x32_w2x2_s2_late",
 
 
 def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 4096),
-                   layouts=("TN", "NT"), out_bf16: bool = False, f32: bool = False) -> dict:
+                   layouts=("TN", "NT"), out_bf16: bool = False, f32: bool = False,
+                   beta: float = 0.0) -> dict:
     """The automatic choice against every whole-tile bf16 candidate, forced,
     on a grid of shapes (fp32 output, N(0,1) operands).  TN and NT only: a
     forced variant runs as stored, while NN calls may run as D^T, so an NN
@@ -676,7 +677,8 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
     pays the clock's warm-up.  With out_bf16, D is bf16 and the candidates
     are those that carry a bf16-output epilogue (a forced variant without
     one is refused as not supported and left out).  With f32, operands and D
-    are fp32 and the candidates are the fp32 whole-tile variants."""
+    are fp32 and the candidates are the fp32 whole-tile variants.  A nonzero
+    beta adds beta * C (C drawn U[-1, 1]) to every call."""
     candidates = SELECTOR_CANDIDATES_F32 if f32 else SELECTOR_CANDIDATES
     op_dtype = torch.float32 if f32 else torch.bfloat16
     names = {name: i for i, name, _, _ in g.variants()}
@@ -707,9 +709,11 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                     B = torch.randn((K, N) if tb == "N" else (N, K), device="cuda").to(op_dtype)
                     D = torch.empty(M, N, device="cuda",
                                     dtype=torch.bfloat16 if out_bf16 else torch.float32)
+                    C = (torch.rand(M, N, device="cuda") * 2 - 1).to(D.dtype) if beta else None
 
                     def run():
-                        st = g.run_tensors(h, A, B, D, transA=ta, transB=tb, check=False)
+                        st = g.run_tensors(h, A, B, D, C=C, transA=ta, transB=tb, beta=beta,
+                                           check=False)
                         if st != g.GEMM_OK:
                             raise RuntimeError(g.gemm_status_string(st))
 
@@ -717,7 +721,8 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                     for c in candidates:
                         g.gemm_set_variant(h, names[c])
                         g.gemm_set_stream_k(h, 0)
-                        st = g.run_tensors(h, A, B, D, transA=ta, transB=tb, check=False)
+                        st = g.run_tensors(h, A, B, D, C=C, transA=ta, transB=tb, beta=beta,
+                                           check=False)
                         if st == g.GEMM_ERR_NOT_SUPPORTED:
                             continue
                         times[c] = best_ms(run)
@@ -740,7 +745,7 @@ def selector_check(g, h, dims=(1024, 2048, 3072, 4096, 6144, 8192), ks=(1024, 40
                                  "ratio": round(auto / times[best], 3),
                                  "times": {c.split("_", 2)[2]: round(t, 4) for c, t in times.items()}})
                     print(f"[select] {rows[-1]}", file=sys.stderr, flush=True)
-                    del A, B, D
+                    del A, B, C, D
     torch.cuda.empty_cache()
     r = [x["ratio"] for x in rows]
     return {"rows": rows, "shapes": len(rows), "within_5pct": sum(1 for x in r if x <= 1.05),
@@ -824,6 +829,8 @@ def main(argv=None):
                     help="fp32 operands and the fp32 candidates in --selector-check")
     ap.add_argument("--selector-dims", default="1024,2048,3072,4096,6144,8192",
                     help="comma-separated M and N values of the --selector-check grid")
+    ap.add_argument("--selector-beta", type=float, default=0.0,
+                    help="beta of the --selector-check calls (nonzero: C is read)")
     ap.add_argument("--selector-layouts", default="TN,NT",
                     help="comma-separated layouts of the --selector-check grid (an automatic "
                          "NN call may run as D^T while a forced candidate runs as stored)")
@@ -864,7 +871,7 @@ def main(argv=None):
         dims = tuple(int(d) for d in args.selector_dims.split(","))
         print(json.dumps(selector_check(g, h, dims=dims, ks=ks,
                                         out_bf16=args.selector_out == "bf16",
-                                        f32=args.selector_f32,
+                                        f32=args.selector_f32, beta=args.selector_beta,
                                         layouts=tuple(args.selector_layouts.split(",")))),
               flush=True)
         g.gemm_set_workspace(h, None, 0, None)
