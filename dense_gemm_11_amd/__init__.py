@@ -47,7 +47,7 @@ EXPORTS = ("gemm_create", "gemm_destroy", "gemm_run", "gemm_status_string",
            "gemm_select_variant", "gemm_stream_k_workspace_bytes", "gemm_set_workspace",
            "gemm_set_stream_k", "gemm_last_stream_k", "gemm_run_epilogue",
            "gemm_variant_pipeline", "gemm_variant_occupancy", "gemm_stream_k_status",
-           "gemm_set_stream_k_poll_limit", "gemm_run_no_alloc")
+           "gemm_set_stream_k_poll_limit", "gemm_run_no_alloc", "gemm_set_planning_model")
 
 
 class GemmEpilogue(ctypes.Structure):
@@ -117,6 +117,8 @@ def _load():
     lib.gemm_variant_pipeline.restype = i32
     lib.gemm_variant_occupancy.argtypes = [i32]
     lib.gemm_variant_occupancy.restype = i32
+    lib.gemm_set_planning_model.argtypes = [i32, ctypes.POINTER(i32), i32]
+    lib.gemm_set_planning_model.restype = i32
     lib.gemm_set_variant.argtypes = [vp, i32]
     lib.gemm_set_variant.restype = i32
     lib.gemm_last_variant.argtypes = [vp]
@@ -212,6 +214,16 @@ def gemm_variant_pipeline(i: int):
 
 def gemm_variant_occupancy(i: int) -> int:
     return lib.gemm_variant_occupancy(i)
+
+
+def gemm_set_planning_model(cus: int, occupancy=None) -> int:
+    """gemm_set_planning_model: `occupancy` is a sequence of
+    gemm_variant_count() workgroups-per-unit figures (0: keep the device
+    query), or None (with cus = 0) to clear the model."""
+    if occupancy is None:
+        return lib.gemm_set_planning_model(cus, None, 0)
+    arr = (ctypes.c_int32 * len(occupancy))(*occupancy)
+    return lib.gemm_set_planning_model(cus, arr, len(occupancy))
 
 
 def gemm_set_variant(h, i: int) -> int:

@@ -105,6 +105,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Per-device caches are indexed by device ordinal; devices beyond this many
 // are answered without caching.
 constexpr int MAX_DEVICES = 64;
+constexpr int MAX_VARIANTS = 128;
+
+// Planning model set by gemm_set_planning_model: a compute-unit count and
+// per-variant data-parallel occupancies that replace the device queries in
+// the planner (0: use the query).
+std::atomic<int> g_model_cus{0};
+std::atomic<int> g_model_occ[MAX_VARIANTS];
 
 // Ordinal of the current device, or -1 when it cannot be queried.
 int current_device()
@@ -119,6 +126,8 @@ int current_device()
 // value is only ever replaced by the same value).
 int device_cus()
 {
+    const int model = g_model_cus.load(std::memory_order_relaxed);
+    if (model > 0) return model;
     static std::atomic<int> cached[MAX_DEVICES];
     const int dev = current_device();
     if (dev < 0) return 256;
@@ -204,9 +213,12 @@ double step_us(const Variant& v)
 // variant, atomically as for device_cus).
 int variant_occupancy(const Variant& v, bool sk = true)
 {
-    constexpr int MAX_VARIANTS = 128;
     static std::atomic<int> cache[MAX_DEVICES][2][MAX_VARIANTS];
     const int vid = (int)(&v - table().data());
+    if (!sk && vid >= 0 && vid < MAX_VARIANTS) {
+        const int model = g_model_occ[vid].load(std::memory_order_relaxed);
+        if (model > 0) return model;
+    }
     const OccFn f = sk ? v.sk_occ : v.occ;
     if (!f) return v.bm * v.bn >= 256 * 256 ? 1 : 2;
     const int dev = current_device();
@@ -868,6 +880,21 @@ gemm_status_t gemm_variant_pipeline(int id, int* stages, int* ahead)
     const dg::Variant& v = dg::table()[id];
     if (stages) *stages = v.stages;
     if (ahead) *ahead = v.ahead;
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_set_planning_model(int cus, const int* occupancy, int count)
+{
+    if (cus < 0 || (occupancy && count != gemm_variant_count()) || count > dg::MAX_VARIANTS ||
+        count < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (occupancy)
+        for (int i = 0; i < count; ++i)
+            if (occupancy[i] < 0) return GEMM_ERR_INVALID_VALUE;
+    for (int i = 0; i < dg::MAX_VARIANTS; ++i)
+        dg::g_model_occ[i].store(occupancy && i < count ? occupancy[i] : 0,
+                                 std::memory_order_relaxed);
+    dg::g_model_cus.store(cus, std::memory_order_relaxed);
     return GEMM_OK;
 }
 

@@ -206,6 +206,20 @@ gemm_status_t gemm_variant_pipeline(int id, int* stages, int* ahead);
  * device cannot be queried. */
 int gemm_variant_occupancy(int id);
 
+/* Planning model: what the planner behind gemm_run and gemm_select_variant
+ * assumes about the device in place of querying it -- `cus` compute units
+ * (0: the device attribute) and, per variant, occupancy[id] workgroups per
+ * compute unit for its data-parallel kernel (0: the HIP occupancy query, as
+ * gemm_variant_occupancy reports it).  The choices then follow the same
+ * rules ("GEMM on NVIDIA GPUs", section 5: waves of tiles over the compute
+ * units) for that model: planning on a host without the device, e.g. tests
+ * of the selection rules, or for another device's figures.  `occupancy`
+ * holds `count` == gemm_variant_count() entries, all >= 0, and is copied;
+ * occupancy = NULL with cus = 0 clears the model.  Process-wide (every
+ * handle); not meant to change while another thread plans a call.
+ * GEMM_ERR_INVALID_VALUE for a negative cus or entry, or a wrong count. */
+gemm_status_t gemm_set_planning_model(int cus, const int* occupancy, int count);
+
 /* Force variant `id` for later gemm_run calls on h; -1 restores automatic
  * selection.  GEMM_ERR_INVALID_VALUE for an unknown id or NULL handle. */
 gemm_status_t gemm_set_variant(gemm_handle_t h, int id);
