@@ -550,6 +550,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     //    8-wave 256x256 kernel (3072^3 76.5 -> 58.6; 4093x2051x1537 A^T B
     //    58.5 -> 50.1).
     bool untransposed = false;  // an NN call that keeps its orientation
+    bool keep_depth = false;    // the 128x128 rings keep their 4-stage depth
     // a variant serves the call's output type and epilogue (bf16 output and
     // the fused epilogue: launches of its own)
     auto serves = [&](const Variant& x) {
@@ -622,9 +623,10 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // (3072x8192x1024 0.0572 ms against 0.0540), and 256x128 instead of
         // 128x256 in the long-K rule below (4096x2048x4096 0.0676 against
         // 0.0587); mean ratio to the fastest candidate 1.039 -> 1.009 at K =
-        // 1024, 1.029 -> 1.004 at 4096 (on a second run).  At K <= 512 the
-        // layout follows the rules above (the 128x128 rings won some shapes
-        // on one run and lost them on the next).
+        // 1024, 1.029 -> 1.004 at 4096 (on a second run).  At K <= 512 only
+        // over 3/4 to 1 wave of 256x256 tiles (below); elsewhere the rules
+        // above (a rule sending more of these calls to the 128x128 rings won
+        // some shapes on one run and lost them on the next).
         static const int tall_tile = find_variant("bf16_dma32x32x16_256x128x32_w2x2_s3_late");
         const bool b_only_kc = c.b_kc && !c.a_kc;
         const bool tall_ok = measured && b_only_kc && tall_tile >= 0 &&
@@ -653,9 +655,27 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         const bool s2_bo = short_bo && !c.a_kc && !c.b_kc && K <= 256 && 8 * t256 >= 3 * cus &&
                            s2_id >= 0 && serves(table()[s2_id]) &&
                            dma_offsets_fit(table()[s2_id], c.a_kc, c.b_kc, K, c.lda, c.ldb, es);
+        // Three quarters to one wave of 256x256 tiles at K <= 512, fp32 output,
+        // aligned rows, with B k-contiguous: the 2-stage 128x128 ring, which
+        // the round model takes there (its 3 workgroups per compute unit run
+        // the 128x128 tiles in one round), trailed the deeper rings, its two
+        // stages too shallow for the half-line copies of a k-contiguous
+        // operand.  TT (only B k-contiguous) at 256 < K <= 512 takes 256x128;
+        // NT (both) at K <= 512 keeps the paired 4-stage ring.  Two grid runs
+        // on two boxes (ms, 2-stage ring -> the rule's choice): TT
+        // 4096x3072x512 0.0225 -> 0.0203 and 0.0207 -> 0.0183, NT
+        // 6144x2048x512 0.0226 -> 0.0197 and 0.0210 -> 0.0180; mean ratio to
+        // the fastest candidate over the four such shapes and two runs 1.10
+        // -> 1.01 (TT, K = 512), 1.14 -> 1.02 (NT, K = 512), 1.08 -> 1.03
+        // (NT, K = 256).  TN (no k-contiguous operand) and TT at K = 256 stay
+        // on the 2-stage ring (mean ratio 1.03 there).
+        const bool ring_wave = measured && K <= 512 && 4 * t256 >= 3 * cus && t256 < cus;
+        keep_depth = ring_wave && both_kc;
         if (s2_bo) {
             id = s2_id;
         } else if (tall_ok && K > 512 && K <= 1024 && t256 >= cus) {
+            id = tall_tile;
+        } else if (tall_ok && ring_wave && K > 256) {
             id = tall_tile;
         } else if (mis_short) {
             if ((c.a_kc || c.b_kc) && 4 * t256 >= 3 * cus && rounds_at_least(t256, 1, 3, 4) &&
@@ -767,7 +787,7 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     if (sk == 0 && c.forced < 0 && aligned &&
         id == dma_variant(GEMM_DTYPE_BF16_F32, false)) {
         static const int s2 = find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late");
-        if (s2 >= 0 && serves(table()[s2]) &&
+        if (s2 >= 0 && !keep_depth && serves(table()[s2]) &&
             data_parallel_us(table()[s2], M, N, K) < data_parallel_us(table()[id], M, N, K))
             id = s2;
         // Otherwise, with a k-contiguous operand and more tiles than compute

@@ -81,6 +81,13 @@ CASES = [
     ("bf16", "T", "N", 6144, 3072, 256, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     ("bf16", "T", "N", 3072, 4096, 256, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
     ("bf16", "N", "T", 3072, 6144, 256, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    # ... but over 3/4 to 1 wave (192 tiles of 256x256) with B k-contiguous
+    # not the 2-stage ring: 256x128 for TT at K = 512 (TT at K = 256 keeps
+    # the 2-stage ring), the paired ring for NT
+    ("bf16", "T", "T", 4096, 3072, 512, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
+    ("bf16", "T", "T", 3072, 4096, 256, 0.0, False, P + "128x128x32_w2x2_s2_late", False),
+    ("bf16", "N", "T", 6144, 2048, 512, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
+    ("bf16", "N", "T", 4096, 3072, 256, 0.0, False, P + "128x128x32_w2x2_s4_late_pair", False),
     # both operands k-contiguous, K below 1024: the paired 128x128 ring over
     # more than a wave of 256x256 tiles whose last wave is partly empty
     # (288 tiles), 256x256 where its waves are whole (512 tiles)
