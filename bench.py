@@ -256,17 +256,52 @@ def time_extra(g, h, name: str, variant_name, reps: int, warmup: int,
                          if out_dtype == torch.bfloat16 else w.description)}
 
 
-def graph_replay_ms(g, h, name: str, launches: int = 50, replays: int = 5) -> float:
+def store_only_call_ms(g, h, name: str, reps: int = 50) -> float:
+    """Per-call time of the workload's call with alpha = beta = 0 (arguments
+    marshalled once, as in time_extra): the library's launch path with one
+    kernel writing D = 0, the floor under a small GEMM called one at a time."""
+    w = workloads.WORKLOADS[name]
+    A, B, _ = workloads.make_inputs(w)
+    A, B = A.cuda(), B.cuda()
+    D = torch.empty(w.M, w.N, dtype=torch.float32, device="cuda")
+    run = g.bind_tensors(h, A, B, D, transA=w.transA, transB=w.transB, alpha=0.0, beta=0.0)
+    if run() != g.GEMM_OK:
+        raise RuntimeError("store-only call failed")
+    # warm-up as in time_extra, synchronizing every 8 calls: a long unsynced
+    # queue of these short calls left later calls issuing 2x slower
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < 0.05:
+        run()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / reps, 4)
+
+
+def graph_replay_ms(g, h, name: str, launches: int = 50, replays: int = 5,
+                    store_only: bool = False) -> float:
     """Per-launch time with `launches` back-to-back calls captured in one HIP
     graph (through torch.cuda.graph) and replayed: the kernels without the
-    host's per-call cost, which bounds a small GEMM called one at a time."""
+    host's per-call cost, which bounds a small GEMM called one at a time.
+    store_only: the same call with alpha = beta = 0, which the library serves
+    with one kernel writing D = 0 (no operand read, no matrix work)."""
     w = workloads.WORKLOADS[name]
     A, B, C = workloads.make_inputs(w)
     A, B = A.cuda(), B.cuda()
-    C = None if C is None else C.cuda()
+    C = None if C is None or store_only else C.cuda()
     D = torch.empty(w.M, w.N, dtype=torch.float32, device="cuda")
+    alpha, beta = (0.0, 0.0) if store_only else (w.alpha, w.beta)
     run = lambda: g.run_tensors(h, A, B, D, C=C, transA=w.transA, transB=w.transB,
-                                alpha=w.alpha, beta=w.beta)
+                                alpha=alpha, beta=beta)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -974,6 +1009,10 @@ def main(argv=None):
         extras["fp32_4096_vector_fma"] = vf
         extras["fp32_256"] = time_extra(g, h, "fp32_256", None, reps=50, warmup=10)
         extras["fp32_256"]["graph_replay_kernel_ms"] = graph_replay_ms(g, h, "fp32_256")
+        # the launch floor under it: the same call with alpha = beta = 0
+        extras["fp32_256"]["store_only_call_ms"] = store_only_call_ms(g, h, "fp32_256")
+        extras["fp32_256"]["store_only_graph_replay_ms"] = graph_replay_ms(
+            g, h, "fp32_256", store_only=True)
         extras["bf16_tn_edge_alpha_beta"] = time_extra(g, h, "bf16_tn_edge", None, reps=20,
                                                        warmup=5)
         extras["bf16_8192_bf16_output"] = time_extra(g, h, "bf16_8192", None, reps=10, warmup=3,
