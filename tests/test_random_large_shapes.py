@@ -122,6 +122,9 @@ SELECTED = [
     ("bf16_bf16", "T", "N", 6144, 3072, 256, 1.0, 0.5, P + "128x128x32_w2x2_s2_late"),
     ("f32", "N", "N", 6144, 6144, 1024, 1.0, 1.0, "f32_dma32x32x2_128x128x16_w2x2_s3_late"),
     ("f32", "T", "N", 3000, 6144, 256, -1.5, 0.0, "f32_dma32x32x2_128x128x16_w2x2_s3_late"),
+    # B k-contiguous at K = 512 over 3/4 of a wave of 256x256 tiles
+    ("bf16_f32", "T", "T", 4096, 3072, 512, 1.0, 0.5, P + "256x128x32_w2x2_s3_late"),
+    ("bf16_f32", "N", "T", 6144, 2048, 512, -0.5, 0.0, P + "128x128x32_w2x2_s4_late_pair"),
 ]
 
 
