@@ -512,6 +512,21 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     int sk = (aligned && sk_launchers(v, op_dtype, out_bf16, c.epi))
                  ? stream_k_grid(v, M, N, K, c.sk_mode, c.ws_bytes, dp_us, &sk_us)
                  : 0;
+    // bf16, fp32 output, at most half a wave of 128x128 tiles and K >= 3072:
+    // stream-K wherever a grid fits.  With one tile per busy compute unit the
+    // whole-tile kernel is bound by each K-step's copy latency (more so with a
+    // k-contiguous operand: NN 1024^2 x 4096 0.0320 ms against 0.0255 for
+    // TN), and the model above, which needs a fifth's margin, declined
+    // grids that were faster.  Every such shape timed (M, N in 512 .. 2048,
+    // 48 to 128 tiles, K = 3072, 4096, 6144, TN and NN; one box, ms, whole
+    // tiles -> stream-K): TN 0.68-1.00 (1024^2 x 4096 0.0255 -> 0.0208), NN
+    // 0.61-0.83 (1024^2 x 4096 0.0320 -> 0.0231); at K = 2048 and from 144
+    // tiles it lost or tied (TN 1536^2 x 4096 0.0270 -> 0.0327).
+    if (sk == 0 && c.forced < 0 && c.sk_mode < 0 && aligned && op_dtype == GEMM_DTYPE_BF16_F32 &&
+        !out_bf16 && !c.epi && v.kind == KIND_MFMA_DMA && v.bm == 128 && v.bn == 128 &&
+        K >= 3072 && 2 * ceil_div(M, 128) * ceil_div(N, 128) <= (int64_t)device_cus() &&
+        sk_launchers(v, op_dtype, out_bf16, c.epi))
+        sk = stream_k_grid(v, M, N, K, 1, c.ws_bytes, dp_us, &sk_us);
     if (c.forced < 0 && aligned && v.kind == KIND_MFMA_DMA && c.sk_mode != 0) {
         // With a workspace, stream-K on the other tile size competes too; the
         // lowest estimate wins.  It has to beat that tile size's own

@@ -124,8 +124,13 @@ CASES = [
     ("bf16", "N", "T", 8189, 4093, 511, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     ("bf16", "T", "T", 2045, 4093, 4093, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
     ("bf16", "T", "T", 4093, 2045, 1537, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
-    # few tiles, long K: stream-K
+    # few tiles, long K: stream-K; with bf16 operands from K = 3072 at up to
+    # half a wave of 128x128 tiles, not at K = 2048 nor from 144 tiles
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
+    ("bf16", "T", "N", 1024, 1024, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
+    ("bf16", "N", "N", 1024, 2048, 3072, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
+    ("bf16", "T", "N", 1024, 1024, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "T", "N", 1536, 1536, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
 ]
 
 
