@@ -131,6 +131,12 @@ CASES = [
     ("bf16", "N", "N", 1024, 2048, 3072, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
     ("bf16", "T", "N", 1024, 1024, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     ("bf16", "T", "N", 1536, 1536, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    # ... with no k-contiguous operand at 128 tiles only from K = 6144; bf16
+    # output alike
+    ("bf16", "T", "N", 1024, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "T", "N", 2048, 1024, 6144, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
+    ("bf16", "N", "T", 1024, 2048, 3072, 0.0, True, P + "128x128x32_w2x2_s4_late", True),
+    ("bf16", "T", "N", 1024, 2048, 3072, 0.0, True, P + "128x128x32_w2x2_s4_late", False),
 ]
 
 
