@@ -512,8 +512,9 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     int sk = (aligned && sk_launchers(v, op_dtype, out_bf16, c.epi))
                  ? stream_k_grid(v, M, N, K, c.sk_mode, c.ws_bytes, dp_us, &sk_us)
                  : 0;
-    // bf16 operands (fp32 or bf16 output, no fused epilogue), at most half a
-    // wave of 128x128 tiles, K >= 3072: stream-K wherever a grid fits.  With
+    // bf16 operands (fp32 or bf16 output, with or without the fused
+    // epilogue), at most half a wave of 128x128 tiles, K >= 3072: stream-K
+    // wherever a grid fits.  With
     // one tile per busy compute unit the whole-tile kernel is bound by each
     // K-step's copy latency, more so with a k-contiguous operand (NN 1024^2
     // x 4096 0.0320 ms against 0.0255 for TN), and the model above, which
@@ -524,9 +525,10 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
     // 0.66-0.93 up to 96 tiles (1024^2 x 4096 0.0255 -> 0.0208); TN at 128
     // tiles only from K = 6144 (0.84-0.88; at K = 3072 up to 1.15 with bf16
     // output).  At K = 2048 it was mixed (0.76-1.36), from 144 tiles it lost
-    // or about tied (0.95-1.41; TN 1536^2 x 4096 0.0270 -> 0.0327).
+    // or about tied (0.95-1.41; TN 1536^2 x 4096 0.0270 -> 0.0327).  With
+    // bias + GELU fused, TN and NN: 0.65-1.00 where this takes it.
     if (sk == 0 && c.forced < 0 && c.sk_mode < 0 && aligned && op_dtype == GEMM_DTYPE_BF16_F32 &&
-        !c.epi && v.kind == KIND_MFMA_DMA && v.bm == 128 && v.bn == 128 && K >= 3072 &&
+        v.kind == KIND_MFMA_DMA && v.bm == 128 && v.bn == 128 && K >= 3072 &&
         sk_launchers(v, op_dtype, out_bf16, c.epi)) {
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), cus = device_cus();
         if (2 * t128 <= cus && (c.a_kc || c.b_kc || 8 * t128 <= 3 * cus || K >= 6144))

@@ -236,6 +236,22 @@ def test_epilogue_as_stream_k(g, sk_handle, dtype):
     assert err <= tol
 
 
+@pytest.mark.parametrize("dtype", ["bf16_f32", "bf16_bf16"])
+def test_epilogue_stream_k_on_few_tiles(g, sk_handle, dtype):
+    """bf16 operands, 64 tiles of 128x128, K = 4096: the automatic policy
+    takes stream-K, and the fused epilogue (bias, GELU, with beta * C) holds."""
+    h = sk_handle
+    M, N, K = 1024, 1024, 4096
+    announce("epilogue stream-k few tiles", dtype, M, N, K)
+    A, B, C, bias, out = make(dtype, "T", "N", M, N, K, 7520, True)
+    D = run(g, h, "T", "N", 0.75, -0.5, A, B, C, bias, ACTS["gelu"], None, out, M, N)
+    assert g.gemm_last_stream_k(h) > 1
+    rows, cols = workloads.sample_indices(M, N, 7521)
+    err, tol = check(dtype, "T", "N", M, N, K, 0.75, -0.5, A, B, C, bias, ACTS["gelu"], None, D,
+                     rows=rows, cols=cols)
+    assert err <= tol
+
+
 TILE_CASES = [
     # transA, transB, M, N, K, alpha, beta, expected tile
     ("N", "N", 16384, 4096, 512, 1.0, 0.0, "128x256x32"),
