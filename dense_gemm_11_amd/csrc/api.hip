@@ -822,6 +822,25 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         if (id != s2 && pair >= 0 && serves(table()[pair]) && (c.a_kc || c.b_kc) &&
             ceil_div(M, 128) * ceil_div(N, 128) > (int64_t)device_cus())
             id = pair;
+        // One 128x128 tile per busy compute unit (more than half a wave, at
+        // most one), a k-contiguous operand, K >= 3072, fp32 output, aligned
+        // rows: 64-deep K-steps (three stages), as stored.  A k-contiguous
+        // row of a 32-deep bf16 step is half a 128-byte line; at 64 it is a
+        // whole line, and with no second workgroup on the unit to hide the
+        // copies that halves their requests per FLOP.  Timed on 63 such
+        // shapes (M, N in 1024 .. 4096, 144 to 256 tiles, K = 3072, 4096,
+        // 8192, NN, NT, TT; one box, ms, the 4-stage ring -> 64-deep steps):
+        // 0.75-1.00 of the automatic time, mean 0.90 (NT 1536^2 x 3072 0.0313
+        // -> 0.0236, NN 1536^2 x 4096 0.0344 -> 0.0295); TN, whose rows
+        // along mn already copy whole lines, lost 5-16 %.
+        static const int deep = find_variant("bf16_dma32x32x16_128x128x64_w2x2_s3_late");
+        const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), cus = device_cus();
+        if (id == dma_variant(GEMM_DTYPE_BF16_F32, false) && deep >= 0 && !out_bf16 && !c.epi &&
+            c.rows16 && (c.a_kc || c.b_kc) && K >= 3072 && 2 * t128 > cus && t128 <= cus &&
+            dma_offsets_fit(table()[deep], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
+            id = deep;
+            untransposed = true;
+        }
     }
     const Variant& vr = table()[id];
     // bf16 NN with whole tiles: run as D^T = B^T A^T, which puts the

@@ -125,6 +125,9 @@ SELECTED = [
     # B k-contiguous at K = 512 over 3/4 of a wave of 256x256 tiles
     ("bf16_f32", "T", "T", 4096, 3072, 512, 1.0, 0.5, P + "256x128x32_w2x2_s3_late"),
     ("bf16_f32", "N", "T", 6144, 2048, 512, -0.5, 0.0, P + "128x128x32_w2x2_s4_late_pair"),
+    # one 128x128 tile per compute unit with a k-contiguous operand: 64-deep steps
+    ("bf16_f32", "N", "N", 1536, 1536, 4096, 1.0, 0.5, P + "128x128x64_w2x2_s3_late"),
+    ("bf16_f32", "T", "T", 2048, 1536, 3072, -1.0, 0.0, P + "128x128x64_w2x2_s3_late"),
 ]
 
 

@@ -124,6 +124,13 @@ CASES = [
     ("bf16", "N", "T", 8189, 4093, 511, 0.0, False, P + "256x256x32_w2x4_s3_late", False),
     ("bf16", "T", "T", 2045, 4093, 4093, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
     ("bf16", "T", "T", 4093, 2045, 1537, 0.0, False, P + "256x128x32_w2x2_s3_late", False),
+    # one 128x128 tile per busy compute unit, a k-contiguous operand, K >=
+    # 3072: 64-deep K-steps (TN and K = 2048 keep the 4-stage ring)
+    ("bf16", "N", "N", 1536, 1536, 4096, 0.0, False, P + "128x128x64_w2x2_s3_late", False),
+    ("bf16", "N", "T", 2048, 2048, 3072, 0.0, False, P + "128x128x64_w2x2_s3_late", False),
+    ("bf16", "T", "T", 1024, 3072, 8192, 0.0, False, P + "128x128x64_w2x2_s3_late", False),
+    ("bf16", "T", "N", 2048, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "T", "T", 2048, 2048, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     # few tiles, long K: stream-K; with bf16 operands from K = 3072 at up to
     # half a wave of 128x128 tiles, not at K = 2048 nor from 144 tiles
     ("bf16", "N", "N", 1024, 1024, 32768, 0.0, False, P + "128x128x32_w2x2_s4_late", True),
