@@ -531,8 +531,30 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         v.kind == KIND_MFMA_DMA && v.bm == 128 && v.bn == 128 && K >= 3072 &&
         sk_launchers(v, op_dtype, out_bf16, c.epi)) {
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), cus = device_cus();
-        if (2 * t128 <= cus && (c.a_kc || c.b_kc || 8 * t128 <= 3 * cus || K >= 6144))
-            sk = stream_k_grid(v, M, N, K, 1, c.ws_bytes, dp_us, &sk_us);
+        if (2 * t128 <= cus && (c.a_kc || c.b_kc || 8 * t128 <= 3 * cus || K >= 6144)) {
+            // Both operands k-contiguous (NT), fp32 output, aligned rows: the
+            // stream-K launch of the 64-deep variant, whose copied rows are
+            // whole 128-byte lines for both operands.  Against the 4-stage
+            // ring's stream-K, three runs on three boxes: NT 0.78-1.05, means
+            // 0.91-0.94 (512x2048x3072 0.0245 -> 0.0194 ms); with one
+            // k-contiguous operand (NN, TT) 0.89-1.14, mean 1.00, and TN
+            // 1.04-1.15, so those keep the 4-stage ring.
+            static const int deep = find_variant("bf16_dma32x32x16_128x128x64_w2x2_s3_late");
+            double d_us = 0.0;
+            const int sk_d =
+                (deep >= 0 && c.a_kc && c.b_kc && c.rows16 && !out_bf16 && !c.epi &&
+                 sk_launchers(table()[deep], op_dtype, out_bf16, c.epi) &&
+                 dma_offsets_fit(table()[deep], c.a_kc, c.b_kc, K, c.lda, c.ldb, es))
+                    ? stream_k_grid(table()[deep], M, N, K, 1, c.ws_bytes, dp_us, &d_us)
+                    : 0;
+            if (sk_d > 0) {
+                id = deep;
+                sk = sk_d;
+                sk_us = d_us;
+            } else {
+                sk = stream_k_grid(v, M, N, K, 1, c.ws_bytes, dp_us, &sk_us);
+            }
+        }
     }
     if (c.forced < 0 && aligned && v.kind == KIND_MFMA_DMA && c.sk_mode != 0) {
         // With a workspace, stream-K on the other tile size competes too; the

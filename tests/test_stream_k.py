@@ -127,6 +127,25 @@ def test_automatic_stream_k_on_few_tiles_with_long_k(handle, dtype, M, N, K):
     assert err <= tol
 
 
+@pytest.mark.parametrize("ta,tb,M,N,K", [("N", "T", 1024, 1024, 4096), ("N", "T", 1536, 1024, 3072),
+                                          ("N", "T", 1024, 2048, 4096)])
+def test_automatic_stream_k_on_the_64_deep_variant(handle, ta, tb, M, N, K):
+    """bf16, both operands k-contiguous, at most half a wave of 128x128 tiles and
+    K >= 3072: stream-K on the 64-deep 128x128 variant (its own stream-K
+    launches), against the oracle on 64 rows x 64 columns, with beta * C."""
+    import dense_gemm_11_amd as g
+    announce("stream-k auto 64-deep", ta, tb, M, N, K)
+    A, B, C = make_case("bf16", ta, tb, M, N, K, seed=4350, with_c=True)
+    D, _, _ = gpu_gemm(handle, "bf16", ta, tb, M, N, K, 0.5, -1.25, A, B, C)
+    assert g.gemm_last_stream_k(handle) > 1
+    assert g.gemm_variant_name(g.gemm_last_variant(handle)) == \
+        "bf16_dma32x32x16_128x128x64_w2x2_s3_late"
+    rows, cols = workloads.sample_indices(M, N, 4351)
+    err, tol = oracle_check("bf16", ta, tb, M, N, K, 0.5, -1.25, A, B, C, D, rows=rows, cols=cols)
+    print(f"[result] stream-k auto 64-deep {ta}{tb} {M}x{N}x{K} max_rel_err={err:.3e}", flush=True)
+    assert err <= tol
+
+
 def test_automatic_policy_keeps_whole_tiles_where_they_are_faster(handle):
     """The misaligned 4093x2051x1537 edge workload measured faster on whole
     128x128 tiles (0.069 ms) than split (0.090 ms): no stream-K."""
