@@ -514,11 +514,11 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
                  : 0;
     // bf16 operands (fp32 or bf16 output, with or without the fused
     // epilogue), at most half a wave of 128x128 tiles, K >= 3072: stream-K
-    // wherever a grid fits.  With
-    // one tile per busy compute unit the whole-tile kernel is bound by each
-    // K-step's copy latency, more so with a k-contiguous operand (NN 1024^2
-    // x 4096 0.0320 ms against 0.0255 for TN), and the model above, which
-    // needs a fifth's margin, declined grids that were faster.  Every such
+    // wherever a grid fits.  With one tile per busy compute unit the
+    // whole-tile kernel is bound by each K-step's copy latency, more so with
+    // a k-contiguous operand (NN 1024^2 x 4096 0.0320 ms against 0.0255 for
+    // TN), and the model above, which needs a fifth's margin, declined grids
+    // that were faster.  Every such
     // shape timed (M, N in 512 .. 2048, 48 to 128 tiles, K = 3072, 4096,
     // 6144, all four layouts; one box, ms, whole tiles -> stream-K): with a
     // k-contiguous operand 0.58-0.90 (NN 1024^2 x 4096 0.0320 -> 0.0231), TN
