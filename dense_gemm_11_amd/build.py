@@ -22,8 +22,9 @@ LIB = os.path.join(HERE, "libdense_gemm.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "inst_bf16.hip", "inst_bf16_dma.hip", "inst_bf16_dma_out.hip",
-           "inst_bf16_dma_sweep.hip", "inst_f32_mfma.hip", "inst_f32_dma.hip",
-           "inst_f32_dma_sweep.hip", "inst_f32_fma.hip", "inst_epi_f32.hip", "inst_epi_bf16.hip",
+           "inst_bf16_dma_sweep.hip", "inst_bf16_dma_sweep128.hip", "inst_f32_mfma.hip",
+           "inst_f32_dma.hip", "inst_f32_dma_sweep.hip", "inst_f32_fma.hip", "inst_epi_f32.hip",
+           "inst_epi_bf16.hip",
            "inst_epi_bf16_out.hip", "inst_sk_bf16_256.hip", "inst_sk_bf16_128.hip",
            "inst_sk_f32.hip", "inst_bf16_dma_tiles.hip", "inst_bf16_dma_192.hip",
            "inst_bf16_dma_out_tiles.hip", "inst_epi_tiles.hip",

@@ -80,7 +80,8 @@ const std::vector<Variant>& table()
         std::vector<Variant> v;
         for (auto get : {bf16_variant_table, f32mfma_variant_table, f32fma_variant_table,
                          bf16dma_variant_table, f32dma_variant_table,
-                         bf16dma_sweep_variant_table, f32dma_sweep_variant_table,
+                         bf16dma_sweep_variant_table, bf16dma_sweep128_variant_table,
+                         f32dma_sweep_variant_table,
                          bf16dma_tile_variant_table, bf16dma_192_variant_table,
                          small_variant_table}) {
             int n = 0;

@@ -98,6 +98,7 @@ const Variant* f32fma_variant_table(int* count);
 const Variant* bf16dma_variant_table(int* count);
 const Variant* f32dma_variant_table(int* count);
 const Variant* bf16dma_sweep_variant_table(int* count);
+const Variant* bf16dma_sweep128_variant_table(int* count);
 const Variant* f32dma_sweep_variant_table(int* count);
 const Variant* bf16dma_tile_variant_table(int* count);
 const Variant* bf16dma_192_variant_table(int* count);
