@@ -557,6 +557,37 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             }
         }
     }
+    // bf16, fp32 output, 3/8 to 1/2 of a wave of 256x256 tiles and a very
+    // long K (NT from K = 8192, other layouts from 16384, e.g. weight
+    // gradients over many tokens): stream-K on the 8-wave 256x256 kernel.
+    // The whole-tile rules below take 128x256 or the paired 128x128 ring
+    // there, and the model rejected the 256x256 grid (its step time is
+    // calibrated on 8192^3 at the board's power limit, where the clock sits
+    // near 1.6 GHz; with a third of the units busy it runs faster).  Timed
+    // on 96 and 100 tiles of 256x256 (2048x3072, 3072x2048, 2560^2,
+    // 1536x4096; one box, ms, automatic -> stream-K on 256x256): NT
+    // 0.87-0.95 at K = 8192 (2048x3072 0.1129 -> 0.0981) and 0.88-0.90 at
+    // 16384; NN 0.91-0.96 and TN 0.93-0.96 at 16384, while at 8192 they
+    // varied 0.95-1.03.  On a second box, also over 112 tiles (1792x4096,
+    // 3584x2048) and in TT, against the fastest whole-tile candidate: NT
+    // 0.92-1.03 at 8192 and 0.86-0.91 at 16384; NN, TN, TT 0.90-0.98 at
+    // 16384.
+    if (sk == 0 && c.forced < 0 && c.sk_mode < 0 && aligned && op_dtype == GEMM_DTYPE_BF16_F32 &&
+        !out_bf16 && !c.epi && K >= ((c.a_kc && c.b_kc) ? 8192 : 16384)) {
+        const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256), cus = device_cus();
+        const int big = dma_variant(GEMM_DTYPE_BF16_F32, true);
+        if (3 * cus <= 8 * t256 && 8 * t256 < 4 * cus && big >= 0 &&
+            sk_launchers(table()[big], op_dtype, out_bf16, c.epi) &&
+            dma_offsets_fit(table()[big], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
+            double b_us = 0.0;
+            const int sk_b = stream_k_grid(table()[big], M, N, K, 1, c.ws_bytes, dp_us, &b_us);
+            if (sk_b > 0) {
+                id = big;
+                sk = sk_b;
+                sk_us = b_us;
+            }
+        }
+    }
     if (c.forced < 0 && aligned && v.kind == KIND_MFMA_DMA && c.sk_mode != 0) {
         // With a workspace, stream-K on the other tile size competes too; the
         // lowest estimate wins.  It has to beat that tile size's own

@@ -140,6 +140,11 @@ CASES = [
     ("bf16", "N", "T", 1024, 1024, 4096, 0.0, False, P + "128x128x64_w2x2_s3_late", True),
     ("bf16", "T", "N", 1024, 1024, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     ("bf16", "T", "N", 1536, 1536, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    # 3/8 to 1/2 of a wave of 256x256 tiles with a very long K (NT from
+    # 8192, the others from 16384): stream-K on 256x256
+    ("bf16", "N", "T", 2048, 3072, 8192, 0.0, False, P + "256x256x32_w2x4_s3_late", True),
+    ("bf16", "T", "N", 2560, 2560, 16384, 0.0, False, P + "256x256x32_w2x4_s3_late", True),
+    ("bf16", "T", "N", 2560, 2560, 8192, 0.0, False, P + "128x256x32_w2x2_s3_late", False),
     # ... with no k-contiguous operand at 128 tiles only from K = 6144; bf16
     # output alike
     ("bf16", "T", "N", 1024, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),

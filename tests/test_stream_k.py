@@ -146,6 +146,23 @@ def test_automatic_stream_k_on_the_64_deep_variant(handle, ta, tb, M, N, K):
     assert err <= tol
 
 
+@pytest.mark.parametrize("ta,tb,M,N,K", [("N", "T", 1792, 4096, 8192), ("T", "T", 2560, 2560, 16384)])
+def test_automatic_stream_k_on_256_tiles_with_very_long_k(handle, ta, tb, M, N, K):
+    """bf16, 3/8 to 1/2 of a wave of 256x256 tiles and a very long K: stream-K
+    on the 8-wave 256x256 kernel, against the oracle on 64 rows x 64 columns."""
+    import dense_gemm_11_amd as g
+    announce("stream-k auto 256 long K", ta, tb, M, N, K)
+    A, B, C = make_case("bf16", ta, tb, M, N, K, seed=4370, with_c=True)
+    D, _, _ = gpu_gemm(handle, "bf16", ta, tb, M, N, K, 1.0, 0.5, A, B, C)
+    assert g.gemm_last_stream_k(handle) > 1
+    assert g.gemm_variant_name(g.gemm_last_variant(handle)) == \
+        "bf16_dma32x32x16_256x256x32_w2x4_s3_late"
+    rows, cols = workloads.sample_indices(M, N, 4371)
+    err, tol = oracle_check("bf16", ta, tb, M, N, K, 1.0, 0.5, A, B, C, D, rows=rows, cols=cols)
+    print(f"[result] stream-k auto 256 {ta}{tb} {M}x{N}x{K} max_rel_err={err:.3e}", flush=True)
+    assert err <= tol
+
+
 def test_automatic_policy_keeps_whole_tiles_where_they_are_faster(handle):
     """The misaligned 4093x2051x1537 edge workload measured faster on whole
     128x128 tiles (0.069 ms) than split (0.090 ms): no stream-K."""
