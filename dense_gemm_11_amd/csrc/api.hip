@@ -437,12 +437,13 @@ const EpiFns* epi_fns_for(int id, int op_dtype, bool out_bf16)
                : out_bf16                 ? epi_fns_bf16_out(v.bm)
                                           : epi_fns_bf16(v.bm);
     if (op_dtype != GEMM_DTYPE_BF16_F32) return nullptr;
-    static const int tiles[5] = {find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late"),
+    static const int tiles[6] = {find_variant("bf16_dma32x32x16_128x256x32_w2x2_s3_late"),
                                  find_variant("bf16_dma32x32x16_192x256x32_w2x4_s3_late"),
                                  find_variant("bf16_dma32x32x16_256x192x32_w4x2_s3_late"),
                                  find_variant("bf16_dma32x32x16_128x128x32_w2x2_s2_late"),
-                                 find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair")};
-    for (int w = 0; w < 5; ++w)
+                                 find_variant("bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair"),
+                                 find_variant("bf16_dma32x32x16_128x128x64_w2x2_s3_late")};
+    for (int w = 0; w < 6; ++w)
         if (id == tiles[w]) return out_bf16 ? epi_fns_tile_bf16out(w) : epi_fns_tile_f32out(w);
     return nullptr;
 }
@@ -877,8 +878,9 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
             ceil_div(M, 128) * ceil_div(N, 128) > (int64_t)device_cus())
             id = pair;
         // One 128x128 tile per busy compute unit (more than half a wave, at
-        // most one), a k-contiguous operand, K >= 3072, fp32 output, aligned
-        // rows: 64-deep K-steps (three stages), as stored.  A k-contiguous
+        // most one), a k-contiguous operand, K >= 3072, aligned rows: 64-deep
+        // K-steps (three stages), as stored; with either output type and
+        // with or without the fused epilogue.  A k-contiguous
         // row of a 32-deep bf16 step is half a 128-byte line; at 64 it is a
         // whole line, and with no second workgroup on the unit to hide the
         // copies that halves their requests per FLOP.  Timed on 63 such
@@ -886,10 +888,12 @@ gemm_status_t plan_call(const CallDesc& c, Plan& pl)
         // 8192, NN, NT, TT; one box, ms, the 4-stage ring -> 64-deep steps):
         // 0.75-1.00 of the automatic time, mean 0.90 (NT 1536^2 x 3072 0.0313
         // -> 0.0236, NN 1536^2 x 4096 0.0344 -> 0.0295); TN, whose rows
-        // along mn already copy whole lines, lost 5-16 %.
+        // along mn already copy whole lines, lost 5-16 %.  With bf16 output,
+        // bias + GELU, or both (NN, NT, TT, 24 shapes each): 0.77-0.98 of
+        // the 4-stage ring, means 0.89-0.90.
         static const int deep = find_variant("bf16_dma32x32x16_128x128x64_w2x2_s3_late");
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), cus = device_cus();
-        if (id == dma_variant(GEMM_DTYPE_BF16_F32, false) && deep >= 0 && !out_bf16 && !c.epi &&
+        if (id == dma_variant(GEMM_DTYPE_BF16_F32, false) && deep >= 0 && serves(table()[deep]) &&
             c.rows16 && (c.a_kc || c.b_kc) && K >= 3072 && 2 * t128 > cus && t128 <= cus &&
             dma_offsets_fit(table()[deep], c.a_kc, c.b_kc, K, c.lda, c.ldb, es)) {
             id = deep;

@@ -13,7 +13,9 @@ const EpiFns* epi_fns_tile_f32out(int which)
     static const EpiFns w192 = DG_EPI_TABLE(dma_gemm_kernel, Dma256x192s3L, false);
     static const EpiFns s2 = DG_EPI_TABLE(dma_gemm_kernel, Dma128x128s2L, false);
     static const EpiFns pair = DG_EPI_TABLE(dma_gemm_kernel, Dma128x128s4LPair, false);
-    return which == 0 ? &wide : which == 1 ? &t192 : which == 2 ? &w192 : which == 3 ? &s2 : which == 4 ? &pair : nullptr;
+    static const EpiFns deep = DG_EPI_TABLE(dma_gemm_kernel, Dma128x128k64s3L, false);
+    return which == 0 ? &wide : which == 1 ? &t192 : which == 2 ? &w192 : which == 3 ? &s2
+         : which == 4 ? &pair : which == 5 ? &deep : nullptr;
 }
 
 }  // namespace dg

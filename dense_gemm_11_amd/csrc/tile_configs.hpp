@@ -22,5 +22,6 @@ using Dma192x256s3L = DmaConfig<MFMA_BF16_32x32x16, 192, 256, 32, 2, 4, 3, true,
 using Dma256x192s3L = DmaConfig<MFMA_BF16_32x32x16, 256, 192, 32, 4, 2, 3, true, PAIR_BOTH_KC>;
 using Dma128x128s2L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 2, true>;
 using Dma128x128s4LPair = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 32, 2, 2, 4, true, PAIR_KC>;
+using Dma128x128k64s3L = DmaConfig<MFMA_BF16_32x32x16, 128, 128, 64, 2, 2, 3, true>;
 
 }  // namespace dg

@@ -218,7 +218,8 @@ def test_bf16_output_on_shape_selected_tiles(sk_handle, c):
 
 
 @pytest.mark.parametrize("variant", ["bf16_dma32x32x16_128x128x32_w2x2_s2_late",
-                                     "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair"])
+                                     "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair",
+                                     "bf16_dma32x32x16_128x128x64_w2x2_s3_late"])
 @pytest.mark.parametrize("ta,tb", list(itertools.product("NT", "NT")))
 def test_bf16_output_on_the_other_128_rings(handle, variant, ta, tb):
     """bf16 output on the 2-stage and the paired 4-stage 128x128 rings (each

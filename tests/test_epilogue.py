@@ -279,7 +279,8 @@ def test_epilogue_on_shape_selected_tiles(g, handle, dtype, c):
 
 
 @pytest.mark.parametrize("variant", ["bf16_dma32x32x16_128x128x32_w2x2_s2_late",
-                                     "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair"])
+                                     "bf16_dma32x32x16_128x128x32_w2x2_s4_late_pair",
+                                     "bf16_dma32x32x16_128x128x64_w2x2_s3_late"])
 @pytest.mark.parametrize("dtype", ["bf16_f32", "bf16_bf16"])
 def test_epilogue_on_the_other_128_rings(g, handle, variant, dtype):
     """bias / activation / clamp fused into the 2-stage and the paired

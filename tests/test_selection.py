@@ -131,6 +131,7 @@ CASES = [
     ("bf16", "T", "T", 1024, 3072, 8192, 0.0, False, P + "128x128x64_w2x2_s3_late", False),
     ("bf16", "T", "N", 2048, 2048, 4096, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
     ("bf16", "T", "T", 2048, 2048, 2048, 0.0, False, P + "128x128x32_w2x2_s4_late", False),
+    ("bf16", "N", "N", 2048, 1536, 4096, 0.0, True, P + "128x128x64_w2x2_s3_late", False),
     # few tiles, long K: stream-K; with bf16 operands from K = 3072 at up to
     # half a wave of 128x128 tiles, not at K = 2048 nor from 144 tiles; with
     # both operands k-contiguous (fp32 output) on the 64-deep variant
